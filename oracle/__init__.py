@@ -1,0 +1,35 @@
+"""Plain fp64 CPU oracle for one context-parallel rank's ring attention forward.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or
+executes anything in this package: only the tests, the smoke check and the
+benchmark's ``cpu_baseline`` leg use it. It shares no code with the HIP path
+(no kernels, headers, helpers, constants or pre/post-processing) and imports
+nothing from it. Every input it sees is passed in as an array; the seeded
+generators live in a module of their own.
+
+Sources (the pages this oracle restates; cited by title and section):
+
+* "Context Parallelism and Ring Attention" (hs-black.github.io, posts/
+  scaling-context-parallel) -- §2 basic CP, §3 blockwise attention with
+  online softmax and the log-sum-exp merge, §4 Ring Attention, §5 causal
+  imbalance, §6 zig-zag and striped token reassignment, §8 all-gather CP,
+  §9 DeepSpeed-Ulysses.
+* "Tensor Parallelism" (t6page.pages.dev, LLM parallel communication) -- the
+  GQA head table (tbl-tp-gqa).
+* "DeepSpeed-Ulysses and hybrids" (t6page.pages.dev, context parallelism) --
+  the pre/post all-to-all shapes.
+
+Modules:
+
+* :mod:`oracle.attention` -- the plain definition of softmax attention
+  (primary oracle), the per-block statistics and the two-block merge
+  (secondary, block-then-merge oracle), and the ring schedule.
+* :mod:`oracle.partition` -- contiguous / zig-zag / striped token maps,
+  visible-pair counts, tile classification and ring efficiency.
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+against closed forms, brute force, a library special case or numbers the
+pages print. No function is "parity unpinned".
+"""
+
+from . import attention, partition  # noqa: F401
