@@ -1,0 +1,202 @@
+"""Benchmark of one context-parallel rank's ring attention forward (libringattn).
+
+A step is one ``ra_ring_fwd`` call: all N ring steps of the rank (K/V chunk
+prefetch into the double buffer, block attention, LSE merge) over one batch of
+synthetic inputs already resident in HBM. The default workload is the
+Llama-3-70B attention shape at 128K tokens split zig-zag over 8 ranks
+(rank 0: 16K queries x 64 heads against 128K keys x 8 KV heads, d = 128, bf16,
+causal).
+
+Metric: causal-adjusted TFLOP/s = 4 * b * n_q * d * (visible query/key pairs)
+/ time, and its fraction of the MI355X dense bf16 MFMA peak (2516.6 TFLOP/s =
+256 CU x 4096 flop/clk x 2.4 GHz).
+
+Prints progress on stderr and ONE JSON line on stdout.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "causal-adjusted attention TFLOP/s per rank shard + % of bf16 MFMA peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def visible_pairs_per_step(kind, S, N, rank, causal):
+    """Visible (query, key) pairs of each ring step, from the library's maps."""
+    import numpy as np
+    from ring_attention_context_amd import ra_partition
+    q_pos = ra_partition(kind, S, N, rank).astype(np.int64)
+    out = []
+    for r in range(N):
+        src = (rank - r) % N
+        kv = ra_partition(kind, S, N, src).astype(np.int64)
+        if causal:
+            out.append(int(np.searchsorted(kv, q_pos, side="right").sum()))
+        else:
+            out.append(len(q_pos) * len(kv))
+    return out
+
+
+def cpu_baseline(w, seconds_hint=15.0):
+    """Time the fp64 CPU oracle (as it stands) on a bounded sample of the same
+    workload: a few query rows x all heads against the full sequence."""
+    import numpy as np
+    import synth
+    from oracle import attention as oatt
+    from oracle import partition as opart
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    # size the sample so the oracle runs roughly seconds_hint seconds
+    per_row = w.n_q * w.S * (4 * w.d + 20) / 2.0      # flops-ish per row, causal ~S/2 keys
+    rows_n = int(max(8, min(256, seconds_hint * 2.0e9 / per_row)))
+    rows = synth.sample_rows(w.c, rows_n, w.seed)
+    inp = synth.draw(w, q_rows=rows)
+    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)[rows]
+    k64, v64, q64 = inp.k64, inp.v64, inp.q64
+    t0 = time.perf_counter()
+    oatt.rows_attention(q64, k64, v64, q_pos, w.causal, w.scale)
+    t = time.perf_counter() - t0
+    pairs = opart.visible_pairs(q_pos, np.arange(w.S), w.causal)
+    flops = 4 * w.b * w.n_q * w.d * pairs
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {w.c} query rows x {w.n_q} heads vs all {w.S} keys "
+                      f"(fp64 NumPy naive softmax, {t:.1f} s, {pairs} visible pairs)",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_70b_128k_zigzag")
+    ap.add_argument("--kind", default=None, help="override the partition map")
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one rank's shard on ONE GPU; runs on more than one GPU "
+              "are not part of this build (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import ring_attention_context_amd as ra
+    from ring_attention_context_amd import runner
+
+    ra.load_library()          # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    w = synth.WORKLOADS[args.workload]
+    if args.kind:
+        w = w.with_(kind=args.kind)
+    if args.rank is not None:
+        w = w.with_(rank=args.rank)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"[bench] device {props.name} CUs={props.multi_processor_count} workload={w}")
+
+    t0 = time.perf_counter()
+    inp = synth.draw(w)
+    q, kc, vc = runner.ring_inputs(inp.q, inp.k, inp.v, w.dtype, w.kind, w.N, dev)
+    del inp
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
+
+    compute = torch.cuda.Stream(dev)
+    copy = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+    call = runner.RingCall(q, kc, vc, kind=w.kind, S=w.S, N=w.N, rank=w.rank, causal=w.causal,
+                           scale=w.scale, flags=args.flags, compute=compute, copy=copy)
+    pairs = visible_pairs_per_step(w.kind, w.S, w.N, w.rank, w.causal)
+    flops_step = [4 * w.b * w.n_q * w.d * p for p in pairs]
+    total_flops = sum(flops_step)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    ev_sets = [call.make_events() for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(compute)
+    for i in range(args.steps):
+        call(events=ev_sets[i])
+    end.record(compute)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = start.elapsed_time(end)
+    ms_per_step = wall * 1e3 / args.steps
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ev_ms:.2f} ms, "
+        f"{ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    # Dominant kernel: the attention launch of each ring step (merge fused in
+    # its epilogue); per-launch times from events on the compute stream.
+    step_ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(w.N)] for e in ev_sets])
+    kern_ms = float(step_ms.sum())
+    launches = step_ms.size
+    achieved = args.steps * total_flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": "attn_bf16_kernel" if w.dtype == "bf16" else "attn_f32_kernel",
+                "avg_launch_ms": round(kern_ms / launches, 4), "launches": launches,
+                "flops_per_launch_avg": total_flops / w.N}
+    log(f"[bench] per-step ms (median over calls): "
+        f"{np.round(np.median(step_ms, axis=0), 3).tolist()}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"[bench] cpu oracle {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), bf16 round-to-nearest-even)",
+        "config": {"workload": w.name, "b": w.b, "S": w.S, "N": w.N, "rank": w.rank,
+                   "map": w.kind, "n_q": w.n_q, "n_kv": w.n_kv, "d": w.d,
+                   "causal": w.causal, "scale": w.scale, "queries_per_rank": w.c,
+                   "visible_pairs": sum(pairs), "flags": args.flags},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "event_ms_per_step": round(ev_ms / args.steps, 4),
+        "device": props.name,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * libringattn -- one context-parallel rank's Ring Attention forward on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "Context Parallelism and Ring Attention"
+ * (hs-black.github.io, posts/scaling-context-parallel):
+ *   - ra_partition       -- §2 (contiguous split) and §6 (zig-zag, striped);
+ *   - ra_block_attn_fwd  -- §3 block statistics (m_b, l_b, o_b, lse_b) of one
+ *                           key block, with the §5 causal rule on original
+ *                           positions (§6 "the cost of reordering");
+ *   - ra_lse_merge       -- §3 boxed two-block merge, stable form;
+ *   - ra_ring_fwd        -- §4 ring loop: N steps, step r uses the K/V of
+ *                           rank (rank - r) mod N, each block merged into the
+ *                           running (o, lse). On one GPU the neighbour's send
+ *                           becomes a device-to-device prefetch into a double
+ *                           buffer (§4 "memory": six blocks, double-buffered).
+ * With N = 1 the ring call is a single dense pass: the local attention of one
+ * rank after the DeepSpeed-Ulysses all-to-all (§9; "DeepSpeed-Ulysses and
+ * hybrids", t6page.pages.dev: full sequence, h/N heads).
+ *
+ * Conventions shared by every call:
+ *   - Layouts are contiguous [b, s, heads, d] for q, k, v, o, o_b, and
+ *     [b, s, n_q] for lse, lse_b. o, o_b, lse and lse_b are always float32.
+ *   - Query head h reads key/value head h / (n_q / n_kv) (GQA groups are
+ *     contiguous runs of query heads).
+ *   - lse is a natural logarithm. A query that sees no key gets o = 0 and
+ *     lse = -inf exactly; (0, -inf) is the identity of the merge.
+ *   - Causal rule: key at global position p is visible to a query at global
+ *     position P iff p <= P (diagonal included).
+ *   - Device pointers must be 16-byte aligned. The caller owns every buffer;
+ *     the library allocates no device memory.
+ *   - Calls that take a stream are stream-ordered and return once the work
+ *     is enqueued. Argument errors are reported before anything is enqueued
+ *     (RA_ERR_INVALID_ARG / RA_ERR_UNSUPPORTED); a failed HIP call returns
+ *     RA_ERR_HIP. Faults inside kernels surface at the caller's next
+ *     synchronisation. ra_last_error() gives the message of the last failure
+ *     on the calling thread.
+ *   - Streams are hipStream_t values passed as void* (NULL = default stream).
+ */
+#ifndef RINGATTN_H
+#define RINGATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARG = 1,  /* bad size, pointer, alignment or divisibility   */
+  RA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (dtype / head dim)   */
+  RA_ERR_HIP = 3           /* a HIP runtime call failed; see ra_last_error() */
+} ra_status;
+
+typedef enum {
+  RA_PART_CONTIGUOUS = 0,  /* rank i owns positions [i*c, (i+1)*c)            */
+  RA_PART_ZIGZAG = 1,      /* rank i owns chunks C_i and C_{2N-1-i} of c/2    */
+  RA_PART_STRIPED = 2      /* rank i owns positions p with p mod N == i       */
+} ra_partition_kind;
+
+typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+/*
+ * ra_partition -- global positions of the c = S/N tokens rank `rank` owns, in
+ * its local order ("Context Parallelism and Ring Attention" §2, §6).
+ *   contiguous: pos[a] = rank*c + a
+ *   zigzag:     the sequence is cut into 2N chunks of h = c/2 tokens; rank i
+ *               holds C_i then C_{2N-1-i}, each ascending:
+ *               pos[a] = i*h + a (a < h), (2N-1-i)*h + (a-h) (a >= h)
+ *   striped:    token p goes to rank p mod N: pos[a] = a*N + rank
+ * Every map is strictly increasing in a, and the N maps partition [0, S).
+ * out_pos: HOST array of c int32, written by the call. Needs S < 2^31,
+ * N >= 1, 0 <= rank < N, S % N == 0, and S % (2N) == 0 for zig-zag; the
+ * pages do not treat remainders, so they are RA_ERR_INVALID_ARG.
+ * Makes no HIP call (usable without a GPU).
+ */
+ra_status ra_partition(int32_t kind, int64_t S, int32_t N, int32_t rank, int32_t *out_pos);
+
+/* One block of keys against a query shard. */
+typedef struct ra_attn_desc {
+  int32_t b;          /* batch                                               */
+  int32_t n_q;        /* query heads                                         */
+  int32_t n_kv;       /* key/value heads; n_q % n_kv == 0                    */
+  int32_t d;          /* head dim: 128 for bf16; 64 or 128 for f32           */
+  int64_t s_q;        /* query rows (tokens) of the shard, >= 0              */
+  int64_t s_kv;       /* key rows of the block, >= 0                         */
+  int32_t dtype;      /* ra_dtype of q, k and v                              */
+  int32_t causal;     /* 1: apply the causal rule on q_pos / kv_pos          */
+  float scale;        /* softmax scale; 0 selects 1/sqrt(d); must be >= 0    */
+  int32_t reserved;   /* must be 0                                           */
+  const int32_t *q_pos;   /* device [s_q] global positions, non-decreasing   */
+  const int32_t *kv_pos;  /* device [s_kv] global positions, non-decreasing  */
+} ra_attn_desc;
+
+/*
+ * ra_block_attn_fwd -- block statistics of "Context Parallelism and Ring
+ * Attention" §3 for the keys of one block:
+ *   m_b = max x, l_b = sum e^{x - m_b}, o_b = (1/l_b) sum e^{x - m_b} v,
+ *   lse_b = m_b + ln l_b,  x = scale * q.k  over the keys visible to the query.
+ * q: device [b, s_q, n_q, d]; k, v: device [b, s_kv, n_kv, d] (dtype);
+ * o_b: device float32 [b, s_q, n_q, d]; lse_b: device float32 [b, s_q, n_q],
+ * both fully overwritten. Rows with no visible key get (0, -inf).
+ * q_pos / kv_pos are read only when causal; positions out of order give
+ * unspecified values (never an out-of-bounds access).
+ */
+ra_status ra_block_attn_fwd(const ra_attn_desc *desc, const void *q, const void *k,
+                            const void *v, float *o_b, float *lse_b, void *stream);
+
+/*
+ * ra_lse_merge -- in place (o, lse) <- merge((o, lse), (o_b, lse_b)), the
+ * boxed merge of "Context Parallelism and Ring Attention" §3 in its stable
+ * form: M = max(lse, lse_b), lse' = M + ln(e^{lse-M} + e^{lse_b-M}),
+ * o' = e^{lse-lse'} o + e^{lse_b-lse'} o_b. A row with lse = lse_b = -inf
+ * becomes (0, -inf).
+ * rows: number of (token, head) rows; o, o_b: device float32 [rows, d];
+ * lse, lse_b: device float32 [rows]. d % 4 == 0 and 1 <= d <= 256.
+ */
+ra_status ra_lse_merge(int64_t rows, int32_t d, float *o, float *lse, const float *o_b,
+                       const float *lse_b, void *stream);
+
+/* ra_ring_desc.flags */
+#define RA_RING_SERIALIZE 1      /* run the K/V prefetch copies on `compute`  */
+#define RA_RING_UNFUSED_MERGE 2  /* write (o_b, lse_b) to the workspace and
+                                    merge with ra_lse_merge's kernel, instead
+                                    of merging in the attention epilogue     */
+
+typedef struct ra_ring_desc {
+  int32_t b, n_q, n_kv, d;  /* as in ra_attn_desc                            */
+  int32_t dtype;            /* ra_dtype of q and the K/V chunks              */
+  int32_t causal;           /* 1: causal rule on global positions            */
+  float scale;              /* 0 selects 1/sqrt(d)                           */
+  int32_t kind;             /* ra_partition_kind of the sequence split       */
+  int64_t S;                /* total tokens of the sequence                  */
+  int32_t N;                /* ring size (context-parallel degree), >= 1     */
+  int32_t rank;             /* the rank whose queries are computed           */
+  int32_t flags;            /* RA_RING_* bits                                */
+  int32_t reserved;         /* must be 0                                     */
+  void **step_events;       /* optional: N+1 hipEvent_t, recorded on
+                               `compute` before step 0 and after each step   */
+} ra_ring_desc;
+
+/* Workspace bytes ra_ring_fwd needs for *desc (same validation as the call). */
+ra_status ra_ring_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
+
+/*
+ * ra_ring_fwd -- the ring loop of "Context Parallelism and Ring Attention" §4
+ * for rank `rank`, replayed on one GPU.
+ * q:        device [b, c, n_q, d], the rank's tokens in its local order
+ *           (c = S/N; see ra_partition for the order).
+ * k_chunks, v_chunks: device [N, b, c, n_kv, d]; chunk j holds rank j's
+ *           tokens in rank j's local order.
+ * o, lse:   device float32 [b, c, n_q, d] and [b, c, n_q], overwritten with
+ *           the merged result over all N blocks.
+ * workspace: device, >= ra_ring_workspace_bytes(); holds the double buffer
+ *           for the incoming K/V chunk and the position maps. Its contents on
+ *           entry do not matter.
+ * Step r computes the block of chunk (rank - r) mod N; the copy of the next
+ * step's chunk into the idle half of the double buffer runs on `copy` while
+ * step r computes on `compute` (or on `compute` with RA_RING_SERIALIZE).
+ * On return all work is enqueued and `compute` is ordered after every copy;
+ * `copy` first waits for the work already enqueued on `compute`.
+ * Calls that share a workspace must be ordered on `compute`.
+ */
+ra_status ra_ring_fwd(const ra_ring_desc *desc, const void *q, const void *k_chunks,
+                      const void *v_chunks, float *o, float *lse, void *workspace,
+                      size_t workspace_bytes, void *compute, void *copy);
+
+/* Static text of a status code. */
+const char *ra_status_str(int32_t status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *ra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RINGATTN_H */

@@ -1,0 +1,55 @@
+// Internal declarations shared by the host entry points and the kernels of
+// libringattn. Not part of the public interface (include/ringattn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ringattn.h"
+
+namespace ra {
+
+// Arguments of one attention launch: the queries of a shard against one block
+// of keys. Layouts as in ringattn.h; o / lse are the block outputs when
+// merge == 0, or the running (o, lse) to merge into when merge == 1.
+struct AttnArgs {
+  const void *q;
+  const void *k;
+  const void *v;
+  float *o;
+  float *lse;
+  const int32_t *q_pos;
+  const int32_t *kv_pos;
+  int64_t s_q;
+  int64_t s_kv;
+  int32_t b;
+  int32_t n_q;
+  int32_t n_kv;
+  int32_t d;
+  float scale;   // softmax scale (natural units), > 0
+  int32_t causal;
+  int32_t merge;
+};
+
+// Records a failure message for ra_last_error() and returns the status.
+ra_status fail(ra_status st, const char *fmt, ...);
+// Checks a HIP return code; records the HIP error text on failure.
+ra_status hip_check(hipError_t err, const char *what);
+// Clears the thread's last-error message.
+void clear_error();
+
+// Validates an attention descriptor plus its data pointers.
+ra_status validate_attn(const ra_attn_desc *d, const void *q, const void *k, const void *v,
+                        const void *o, const void *lse);
+
+// Kernel launchers (enqueue only; return the launch status).
+hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_lse_merge(int64_t rows, int32_t d, float *o, float *lse, const float *o_b,
+                            const float *lse_b, hipStream_t stream);
+hipError_t launch_positions(int32_t kind, int64_t S, int32_t N, int32_t *pos, hipStream_t stream);
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace ra

@@ -1,0 +1,291 @@
+// ra_ring_fwd: the ring loop of "Context Parallelism and Ring Attention" §4
+// for one rank, replayed on one GPU.
+//
+// The pages' loop: at step r the rank holds the K/V block that rank
+// (rank - r) mod N started with, computes its block statistics against the
+// local queries, merges them into the running (o, lse) with the §3 merge, and
+// meanwhile sends its block on and receives the next one (double buffer,
+// §4 "memory"). Here the "receive" is a device-to-device copy of the next
+// chunk into the idle half of a double buffer on a second stream, ordered by
+// events against the compute stream:
+//   copy(r+1 -> buf[(r+1)&1]) waits for step r-1 (the last reader of that half)
+//   step r waits for copy(r -> buf[r&1]).
+// Step 0 reads the rank's own chunk in place and writes (o, lse) directly
+// (merging into the identity (0, -inf) is a no-op). Later steps merge in the
+// attention kernel's epilogue, or, with RA_RING_UNFUSED_MERGE, write
+// (o_b, lse_b) to the workspace and run the standalone merge kernel.
+#include <climits>
+#include <cmath>
+#include <unordered_map>
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Positions of every rank's tokens: pos[j * c + a] = map_j(a) (§2, §6).
+__global__ void positions_kernel(int32_t kind, int64_t S, int32_t N, int32_t *pos) {
+  const int64_t c = S / N;
+  const int64_t h = c / 2;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < S;
+       i += stride) {
+    const int64_t j = i / c, a = i - j * c;
+    int64_t p;
+    if (kind == RA_PART_CONTIGUOUS)
+      p = j * c + a;
+    else if (kind == RA_PART_ZIGZAG)
+      p = a < h ? j * h + a : (2 * static_cast<int64_t>(N) - 1 - j) * h + (a - h);
+    else
+      p = a * N + j;
+    pos[i] = static_cast<int32_t>(p);
+  }
+}
+
+struct Plan {
+  int64_t c = 0;
+  size_t esize = 0;
+  size_t chunk_bytes = 0;   // one K (or V) chunk [b, c, n_kv, d]
+  size_t pos_off = 0, kv_off[2] = {0, 0}, ob_off = 0, lseb_off = 0, total = 0;
+  bool fused = true, serialize = false;
+};
+
+ra_status make_plan(const ra_ring_desc *r, Plan *p) {
+  if (!r) return fail(RA_ERR_INVALID_ARG, "ring: desc is NULL");
+  if (r->N < 1) return fail(RA_ERR_INVALID_ARG, "ring: N = %d must be >= 1", r->N);
+  if (r->rank < 0 || r->rank >= r->N)
+    return fail(RA_ERR_INVALID_ARG, "ring: rank %d outside [0, %d)", r->rank, r->N);
+  if (r->S < 0 || r->S > INT32_MAX - 1)
+    return fail(RA_ERR_INVALID_ARG, "ring: S = %lld outside [0, 2^31 - 1)", (long long)r->S);
+  if (r->S % r->N) return fail(RA_ERR_INVALID_ARG, "ring: S %% N != 0");
+  if (r->kind == RA_PART_ZIGZAG && r->S % (2 * static_cast<int64_t>(r->N)))
+    return fail(RA_ERR_INVALID_ARG, "ring: zig-zag needs S %% 2N == 0");
+  if (r->kind != RA_PART_CONTIGUOUS && r->kind != RA_PART_ZIGZAG && r->kind != RA_PART_STRIPED)
+    return fail(RA_ERR_INVALID_ARG, "ring: unknown partition kind %d", r->kind);
+  if (r->flags & ~(RA_RING_SERIALIZE | RA_RING_UNFUSED_MERGE))
+    return fail(RA_ERR_INVALID_ARG, "ring: unknown flag bits 0x%x", r->flags);
+  if (r->reserved != 0) return fail(RA_ERR_INVALID_ARG, "ring: reserved must be 0");
+  // Shape / dtype checks shared with the block call.
+  ra_attn_desc ad{};
+  ad.b = r->b;
+  ad.n_q = r->n_q;
+  ad.n_kv = r->n_kv;
+  ad.d = r->d;
+  ad.s_q = 0;
+  ad.s_kv = 0;
+  ad.dtype = r->dtype;
+  ad.causal = r->causal;
+  ad.scale = r->scale;
+  ra_status st = validate_attn(&ad, nullptr, nullptr, nullptr, nullptr, nullptr);
+  if (st != RA_OK) return st;
+  p->c = r->S / r->N;
+  p->esize = r->dtype == RA_BF16 ? 2 : 4;
+  p->chunk_bytes = static_cast<size_t>(r->b) * p->c * r->n_kv * r->d * p->esize;
+  p->fused = !(r->flags & RA_RING_UNFUSED_MERGE);
+  p->serialize = (r->flags & RA_RING_SERIALIZE) != 0;
+  size_t off = 0;
+  p->pos_off = off;
+  off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
+  if (r->N > 1) {
+    for (int i = 0; i < 2; ++i) {
+      p->kv_off[i] = off;
+      off += 2 * align_up(p->chunk_bytes);
+    }
+  }
+  if (!p->fused && r->N > 1) {
+    const size_t rows = static_cast<size_t>(r->b) * p->c * r->n_q;
+    p->ob_off = off;
+    off += align_up(rows * r->d * sizeof(float));
+    p->lseb_off = off;
+    off += align_up(rows * sizeof(float));
+  }
+  p->total = off;
+  return RA_OK;
+}
+
+struct RingEvents {
+  hipEvent_t start, ready[2], freed[2];
+};
+
+// Per-thread, per-device events used to order the two streams.
+ra_status ring_events(RingEvents **out) {
+  thread_local std::unordered_map<int, RingEvents> cache;
+  int dev = 0;
+  ra_status st = hip_check(hipGetDevice(&dev), "ring: hipGetDevice");
+  if (st != RA_OK) return st;
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    RingEvents ev{};
+    hipEvent_t *all[5] = {&ev.start, &ev.ready[0], &ev.ready[1], &ev.freed[0], &ev.freed[1]};
+    for (hipEvent_t *e : all) {
+      st = hip_check(hipEventCreateWithFlags(e, hipEventDisableTiming), "ring: hipEventCreate");
+      if (st != RA_OK) return st;
+    }
+    it = cache.emplace(dev, ev).first;
+  }
+  *out = &it->second;
+  return RA_OK;
+}
+
+}  // namespace
+
+hipError_t launch_positions(int32_t kind, int64_t S, int32_t N, int32_t *pos,
+                            hipStream_t stream) {
+  if (S == 0) return hipSuccess;
+  int64_t blocks = (S + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  positions_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(kind, S, N, pos);
+  return hipGetLastError();
+}
+
+}  // namespace ra
+
+extern "C" ra_status ra_ring_workspace_bytes(const ra_ring_desc *desc, size_t *bytes) {
+  ra::clear_error();
+  if (!bytes) return ra::fail(RA_ERR_INVALID_ARG, "ra_ring_workspace_bytes: bytes is NULL");
+  ra::Plan p;
+  ra_status st = ra::make_plan(desc, &p);
+  if (st != RA_OK) return st;
+  *bytes = p.total;
+  return RA_OK;
+}
+
+extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const void *k_chunks,
+                                 const void *v_chunks, float *o, float *lse, void *workspace,
+                                 size_t workspace_bytes, void *compute, void *copy) {
+  using ra::fail;
+  using ra::hip_check;
+  ra::clear_error();
+  ra::Plan P;
+  ra_status st = ra::make_plan(r, &P);
+  if (st != RA_OK) return st;
+  const bool empty = r->b == 0 || P.c == 0;
+  if (!empty) {
+    if (!q || !k_chunks || !v_chunks || !o || !lse)
+      return fail(RA_ERR_INVALID_ARG, "ra_ring_fwd: NULL q / k_chunks / v_chunks / o / lse");
+    if (!ra::aligned16(q) || !ra::aligned16(k_chunks) || !ra::aligned16(v_chunks) ||
+        !ra::aligned16(o))
+      return fail(RA_ERR_INVALID_ARG, "ra_ring_fwd: q / k / v / o not 16-byte aligned");
+    if (P.chunk_bytes % 16)
+      return fail(RA_ERR_INVALID_ARG, "ra_ring_fwd: chunk size not a multiple of 16 bytes");
+    if (!workspace || !ra::aligned16(workspace))
+      return fail(RA_ERR_INVALID_ARG, "ra_ring_fwd: workspace NULL or not 16-byte aligned");
+    if (workspace_bytes < P.total)
+      return fail(RA_ERR_INVALID_ARG, "ra_ring_fwd: workspace has %zu bytes, needs %zu",
+                  workspace_bytes, P.total);
+  }
+  hipStream_t sc = static_cast<hipStream_t>(compute);
+  hipStream_t sp = static_cast<hipStream_t>(copy);
+  const bool serialize = P.serialize || sp == sc;
+  hipEvent_t *step_ev = reinterpret_cast<hipEvent_t *>(r->step_events);
+  if (empty) {
+    if (step_ev)
+      for (int i = 0; i <= r->N; ++i) {
+        st = hip_check(hipEventRecord(step_ev[i], sc), "ra_ring_fwd: step event");
+        if (st != RA_OK) return st;
+      }
+    return RA_OK;
+  }
+
+  ra::RingEvents *ev = nullptr;
+  if (!serialize && r->N > 1) {
+    st = ra::ring_events(&ev);
+    if (st != RA_OK) return st;
+  }
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  int32_t *pos = reinterpret_cast<int32_t *>(ws + P.pos_off);
+  st = hip_check(ra::launch_positions(r->kind, r->S, r->N, pos, sc), "ra_ring_fwd: positions");
+  if (st != RA_OK) return st;
+  if (ev) {
+    // The copy stream reads k/v chunks the caller may have just written on `compute`.
+    st = hip_check(hipEventRecord(ev->start, sc), "ra_ring_fwd: event record");
+    if (st == RA_OK) st = hip_check(hipStreamWaitEvent(sp, ev->start, 0), "ra_ring_fwd: wait");
+    if (st != RA_OK) return st;
+  }
+  if (step_ev) {
+    st = hip_check(hipEventRecord(step_ev[0], sc), "ra_ring_fwd: step event");
+    if (st != RA_OK) return st;
+  }
+
+  const unsigned char *kc = static_cast<const unsigned char *>(k_chunks);
+  const unsigned char *vc = static_cast<const unsigned char *>(v_chunks);
+  const size_t CB = P.chunk_bytes;
+  unsigned char *kbuf[2] = {ws + P.kv_off[0], ws + P.kv_off[1]};
+  unsigned char *vbuf[2] = {ws + P.kv_off[0] + ra::align_up(CB), ws + P.kv_off[1] + ra::align_up(CB)};
+  float *o_b = reinterpret_cast<float *>(ws + P.ob_off);
+  float *lse_b = reinterpret_cast<float *>(ws + P.lseb_off);
+  const int N = r->N, rank = r->rank;
+
+  ra::AttnArgs a{};
+  a.q = q;
+  a.s_q = P.c;
+  a.s_kv = P.c;
+  a.b = r->b;
+  a.n_q = r->n_q;
+  a.n_kv = r->n_kv;
+  a.d = r->d;
+  a.scale = r->scale > 0.f ? r->scale : 1.0f / std::sqrt(static_cast<float>(r->d));
+  a.causal = r->causal;
+  a.q_pos = pos + static_cast<int64_t>(rank) * P.c;
+
+  for (int step = 0; step < N; ++step) {
+    const int src = ((rank - step) % N + N) % N;
+    if (step + 1 < N) {
+      // Prefetch the next step's chunk into the idle half of the double buffer.
+      const int nsrc = ((rank - step - 1) % N + N) % N;
+      const int buf = (step + 1) & 1;
+      hipStream_t cs = serialize ? sc : sp;
+      if (!serialize && step >= 2) {
+        st = hip_check(hipStreamWaitEvent(sp, ev->freed[buf], 0), "ra_ring_fwd: wait freed");
+        if (st != RA_OK) return st;
+      }
+      st = hip_check(hipMemcpyAsync(kbuf[buf], kc + static_cast<size_t>(nsrc) * CB, CB,
+                                    hipMemcpyDeviceToDevice, cs),
+                     "ra_ring_fwd: K copy");
+      if (st == RA_OK)
+        st = hip_check(hipMemcpyAsync(vbuf[buf], vc + static_cast<size_t>(nsrc) * CB, CB,
+                                      hipMemcpyDeviceToDevice, cs),
+                       "ra_ring_fwd: V copy");
+      if (st == RA_OK && !serialize)
+        st = hip_check(hipEventRecord(ev->ready[buf], sp), "ra_ring_fwd: record ready");
+      if (st != RA_OK) return st;
+    }
+    if (step >= 1 && !serialize) {
+      st = hip_check(hipStreamWaitEvent(sc, ev->ready[step & 1], 0), "ra_ring_fwd: wait ready");
+      if (st != RA_OK) return st;
+    }
+    if (step == 0) {
+      a.k = kc + static_cast<size_t>(rank) * CB;
+      a.v = vc + static_cast<size_t>(rank) * CB;
+    } else {
+      a.k = kbuf[step & 1];
+      a.v = vbuf[step & 1];
+    }
+    a.kv_pos = pos + static_cast<int64_t>(src) * P.c;
+    const bool unfused_merge = !P.fused && step > 0;
+    a.o = unfused_merge ? o_b : o;
+    a.lse = unfused_merge ? lse_b : lse;
+    a.merge = (P.fused && step > 0) ? 1 : 0;
+    hipError_t err = r->dtype == RA_BF16 ? ra::launch_attn_bf16(a, sc) : ra::launch_attn_f32(a, sc);
+    st = hip_check(err, "ra_ring_fwd: attention launch");
+    if (st != RA_OK) return st;
+    if (unfused_merge) {
+      const int64_t rows = static_cast<int64_t>(r->b) * P.c * r->n_q;
+      st = hip_check(ra::launch_lse_merge(rows, r->d, o, lse, o_b, lse_b, sc),
+                     "ra_ring_fwd: merge launch");
+      if (st != RA_OK) return st;
+    }
+    if (step >= 1 && !serialize) {
+      st = hip_check(hipEventRecord(ev->freed[step & 1], sc), "ra_ring_fwd: record freed");
+      if (st != RA_OK) return st;
+    }
+    if (step_ev) {
+      st = hip_check(hipEventRecord(step_ev[step + 1], sc), "ra_ring_fwd: step event");
+      if (st != RA_OK) return st;
+    }
+  }
+  return RA_OK;
+}
