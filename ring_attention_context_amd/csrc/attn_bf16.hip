@@ -6,29 +6,42 @@
 // tile by tile with a running max, running sum and unnormalised output (the
 // single-GPU form of the same identity, §3). The causal rule of §5 is applied
 // on original positions (§6 "the cost of reordering"); positions are
-// non-decreasing, so whole tiles past a query tile's last position are never
+// non-decreasing, so tiles past a query tile's last position are never
 // loaded (the tile skipping of §7), and only tiles that straddle the
 // diagonal, or the ragged last tile, evaluate the element mask.
 //
 // Work decomposition (d = 128):
-//   * a wave owns 32 query tokens of one query head; a workgroup of 4 waves
-//     owns TB = 4 / HW consecutive 32-token blocks of HW heads that share one
-//     key/value head (GQA), so each K/V tile staged in LDS serves every
-//     query row of the workgroup;
-//   * K/V tiles of 64 keys: K is stored row-major ([key][d]) and V transposed
-//     ([d][key]) in LDS, both padded so the 16-byte MFMA operand reads of a
-//     wave are bank-conflict free;
+//   * a wave owns 32 query tokens of one query head; a workgroup of 8 waves
+//     owns TB = 8 / HW consecutive 32-token blocks of HW heads that share one
+//     key/value head (GQA), so every K/V tile staged in LDS serves all eight
+//     waves (two per SIMD);
+//   * K/V tiles of 64 keys go from HBM straight into LDS (buffer loads with
+//     the LDS destination, no register staging), through a ring of three
+//     stages: one barrier per tile, and the load of tile t+2 overlaps the
+//     math on tiles t and t+1. Out-of-range keys come back as zeros from the
+//     buffer descriptor's bounds check;
+//   * both tiles are row-major in LDS with the 16-byte chunks of each 256-byte
+//     row XOR-swizzled by the row index, so the MFMA operand reads are
+//     bank-conflict free: K rows with ds_read_b128, V^T operands with the
+//     gfx950 transposing read ds_read_b64_tr_b16;
 //   * scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: each lane then holds 32 keys of ONE query, so
-//     the row max and row sum are in-lane plus one exchange with the lane 32
-//     away, and the fp32 probabilities convert in place into the B operand of
-//     O^T = V^T P^T (the same MFMA shape), whose accumulator keeps one query
-//     per lane -- the rescale by e^{m_old - m_new} is a per-lane scalar;
-//   * exponentials run in base 2 (v_exp_f32) with the scale folded in:
-//     p = 2^(s * scale * log2(e) - m), lse is converted back to natural log.
+//     row max and row sum are in-lane plus one exchange with the lane 32
+//     away, and the probabilities convert in place into the B operand of
+//     O^T = V^T P^T, whose accumulator keeps one query per lane;
+//   * software pipeline inside each wave: the score MFMAs of tile t+1 are
+//     issued together with the exponentials of tile t, and the P V MFMAs of
+//     tile t together with the max / mask of tile t+1;
+//   * exponentials run in base 2 (v_exp_f32) with the scale folded into one
+//     FMA; the running max is updated lazily: the accumulator is rescaled only
+//     when a row max grows by more than 2^8 (exact: o and l share the same
+//     reference, so o = acc / l is unchanged).
 // Workgroups are ordered heaviest query tile first (later positions see more
-// keys under the causal rule).
+// keys under the causal rule); consecutive workgroups cover the KV heads of one
+// token block, so with the round-robin dispatch over the 8 XCDs each XCD's L2
+// serves a fixed KV head.
 #include <climits>
+#include <type_traits>
 
 #include "ra_internal.h"
 
@@ -36,30 +49,34 @@ namespace ra {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr int D = 128;
-constexpr int QW = 32;                 // query tokens per wave
-constexpr int WAVES = 4;
+constexpr int QW = 32;                       // query tokens per wave
+constexpr int WAVES = 8;
 constexpr int THREADS = WAVES * 64;
-constexpr int BK = 64;                 // keys per tile
-constexpr int K_STRIDE = D * 2 + 16;   // bytes per key row of K in LDS
-constexpr int VT_STRIDE = BK * 2 + 16; // bytes per d row of V^T in LDS
-constexpr int K_BYTES = BK * K_STRIDE;
-constexpr int VT_BYTES = D * VT_STRIDE;
-constexpr int LDS_BYTES = K_BYTES + VT_BYTES + BK * 4;
+constexpr int BK = 64;                       // keys per tile
+constexpr int ROW_B = D * 2;                 // bytes per key row
+constexpr int TILE_B = BK * ROW_B;           // 16 KiB
+constexpr int NSTAGE = 3;
+constexpr int LOADS_PER_WAVE = TILE_B / (1024 * WAVES);  // 1 KiB per wave instruction
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float TAU = 8.f;                   // lazy-rescale slack, log2 units
+constexpr int BUF_DWORD3 = 0x00020000;       // raw buffer, 32-bit data format
+
+static_assert(LOADS_PER_WAVE * 1024 * WAVES == TILE_B, "tile split over waves");
+
+// 16-byte chunk swizzle of a row: a 4-bit rotation of the row index.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float swap_halves(float x) {
-  // Value of the lane 32 away (lanes l and l ^ 32 hold the two key halves of
-  // the same query).
-  return __shfl_xor(x, 32);
-}
+// Value of the lane 32 away (lanes l and l ^ 32 hold the two key halves of a query).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
 // Number of keys with position <= p in the non-decreasing kv_pos[0, n).
 __device__ __forceinline__ int64_t count_le(const int32_t *kv_pos, int64_t n, int32_t p) {
@@ -74,12 +91,35 @@ __device__ __forceinline__ int64_t count_le(const int32_t *kv_pos, int64_t n, in
   return lo;
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int32_t>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), n,
+                                           BUF_DWORD3);
+}
+
+// Waits until this wave's own HBM->LDS loads have landed (vmcnt = 0; the other
+// counters are left alone). A barrier after it publishes the data to all waves.
+__device__ __forceinline__ void wait_own_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int HW>
-__global__ __launch_bounds__(THREADS, 2) void attn_bf16_kernel(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char *k_lds = smem;
-  unsigned char *vt_lds = smem + K_BYTES;
-  int32_t *pos_lds = reinterpret_cast<int32_t *>(smem + K_BYTES + VT_BYTES);
+__global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
+  // One LDS object per stage and operand: the compiler then sees that the
+  // asynchronous loads into one stage never alias the reads of the others and
+  // does not drain them before every LDS read.
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE_B], k_lds1[TILE_B],
+      k_lds2[TILE_B];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE_B], v_lds1[TILE_B],
+      v_lds2[TILE_B];
+  __shared__ __attribute__((aligned(16))) int32_t p_lds0[BK], p_lds1[BK], p_lds2[BK];
+  auto k_stage = [&](auto s) -> unsigned char * {
+    return decltype(s)::value == 0 ? k_lds0 : (decltype(s)::value == 1 ? k_lds1 : k_lds2);
+  };
+  auto v_stage = [&](auto s) -> unsigned char * {
+    return decltype(s)::value == 0 ? v_lds0 : (decltype(s)::value == 1 ? v_lds1 : v_lds2);
+  };
+  auto p_stage = [&](auto s) -> int32_t * {
+    return decltype(s)::value == 0 ? p_lds0 : (decltype(s)::value == 1 ? p_lds1 : p_lds2);
+  };
 
   constexpr int TB = WAVES / HW;  // 32-token blocks per workgroup
   const int tid = threadIdx.x;
@@ -97,10 +137,10 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bf16_kernel(AttnArgs a) {
   const int64_t id = blockIdx.x;
   const int64_t tb = ntb - 1 - id / inner;  // heaviest (latest) token block first
   int64_t rem = id % inner;
-  const int hgi = static_cast<int>(rem % hgroups);
-  rem /= hgroups;
   const int kvh = static_cast<int>(rem % a.n_kv);
-  const int bi = static_cast<int>(rem / a.n_kv);
+  rem /= a.n_kv;
+  const int hgi = static_cast<int>(rem % hgroups);
+  const int bi = static_cast<int>(rem / hgroups);
 
   const int64_t wg_tok0 = tb * tok_per_wg;
   const int64_t wg_tok_last = min(wg_tok0 + tok_per_wg, a.s_q) - 1;
@@ -112,8 +152,8 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bf16_kernel(AttnArgs a) {
   const bool tok_ok = tok < a.s_q;
 
   // ---- key range of the workgroup (causal: keys up to its last position) ----
-  // Non-causal: every valid key (position INT_MIN) is visible and keys past
-  // the block (position INT_MAX) are not, so queries take INT_MAX - 1.
+  // Non-causal: every key is visible, so a query takes position INT_MAX - 1
+  // and the tile tests below never skip.
   int64_t nkeys = a.s_kv;
   int32_t w_qmin = INT_MAX - 1, w_qmax = INT_MAX - 1;
   if (a.causal) {
@@ -123,7 +163,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bf16_kernel(AttnArgs a) {
       w_qmax = a.q_pos[w_tok_last];
     }
   }
-  const int ntiles = static_cast<int>((nkeys + BK - 1) / BK);
+  const int nt = static_cast<int>((nkeys + BK - 1) / BK);
 
   // ---- this lane's query: B operand of S^T = K Q^T (8 bf16 per k-step) ----
   const uint16_t *qg = static_cast<const uint16_t *>(a.q);
@@ -139,105 +179,113 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bf16_kernel(AttnArgs a) {
   const int32_t qpos = !a.causal ? INT_MAX - 1 : (tok_ok ? a.q_pos[tok] : INT_MIN);
   const float sl2 = a.scale * LOG2E;
 
-  // ---- global -> register staging of one K/V tile ----
-  // K: thread (chunk kc = tid % 16, rows kr + 16 j): 16 lanes read one 256-byte row.
-  // V: thread (key quad vq = tid % 16, chunk vc = tid / 16): rows 4 vq + j, so the
-  //    register transpose yields 4 consecutive keys of one d for an 8-byte LDS write.
-  const int kc = tid & 15, kr = tid >> 4;
-  const int vq = tid & 15, vc = tid >> 4;
-  const uint16_t *kg = static_cast<const uint16_t *>(a.k);
-  const uint16_t *vg = static_cast<const uint16_t *>(a.v);
-  const int64_t kv_row_stride = static_cast<int64_t>(a.n_kv) * D;  // elements per token
-  const int64_t kv_base = (static_cast<int64_t>(bi) * a.s_kv * a.n_kv + kvh) * D;
-  u32x4 kst[4], vst[4];
-  int32_t pst = 0;
+  // ---- per-lane LDS offsets of the MFMA operands (within one stage) ----
+  // K: lane (col, hi) reads key row kb*32 + col, logical chunk 2*ds + hi.
+  uint32_t koff[D / 16];
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds)
+    koff[ds] = col * ROW_B + ((((2 * ds + hi) ^ swz(col & 15))) << 4);
+  // V^T via the transposing read: in each 16-lane group gq, lane s reads 8 bytes
+  // of key row r (4 rows per group) so that lane j of the group receives
+  // V[k0 + 0..3][d0 + j]; call c covers keys {0..3, 8..11} + 4*(gq>>1) of a
+  // 16-key step, matching the k-slots of P in the B operand.
+  uint32_t voff[2][D / 32];
+  {
+    const int gq = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r = ((gq >> 1) << 2) + (s >> 2) + 8 * c;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int lc = db * 4 + ((gq & 1) << 1) + ((s & 3) >> 1);
+        voff[c][db] = r * ROW_B + ((lc ^ swz(r)) << 4) + ((s & 1) << 3);
+      }
+    }
+  }
 
-  auto load_tile = [&](int t) {
+  // ---- direct HBM -> LDS loads of one K/V tile (and its key positions) ----
+  const unsigned char *kg = static_cast<const unsigned char *>(a.k);
+  const unsigned char *vg = static_cast<const unsigned char *>(a.v);
+  const int64_t kv_row_bytes = static_cast<int64_t>(a.n_kv) * D * 2;
+  const int64_t kv_base = (static_cast<int64_t>(bi) * a.s_kv * a.n_kv + kvh) * D * 2;
+  uint32_t goff[LOADS_PER_WAVE];  // lane's byte offset within the tile's rows
+#pragma unroll
+  for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+    const int row = 4 * (wave + WAVES * i) + (lane >> 4);
+    const int lc = (lane & 15) ^ swz(row & 15);
+    goff[i] = static_cast<uint32_t>(row * kv_row_bytes + lc * 16);
+  }
+  auto issue_tile = [&](int t, auto stage) {
     const int64_t key0 = static_cast<int64_t>(t) * BK;
+    const int64_t left = a.s_kv - key0;  // rows before the end of the block
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + kv_base + key0 * kv_row_bytes,
+                                                (left - 1) * kv_row_bytes + D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + kv_base + key0 * kv_row_bytes,
+                                                (left - 1) * kv_row_bytes + D * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t key = key0 + kr + 16 * j;
-      kst[j] = key < a.s_kv
-                   ? *reinterpret_cast<const u32x4 *>(kg + kv_base + key * kv_row_stride + kc * 8)
-                   : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+      const int r0 = 4 * (wave + WAVES * i);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (LDS_AS void *)(k_stage(stage) + r0 * ROW_B), 16, goff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (LDS_AS void *)(v_stage(stage) + r0 * ROW_B), 16, goff[i], 0, 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t key = key0 + 4 * vq + j;
-      vst[j] = key < a.s_kv
-                   ? *reinterpret_cast<const u32x4 *>(vg + kv_base + key * kv_row_stride + vc * 8)
-                   : u32x4{0, 0, 0, 0};
+    if (a.causal && wave == 0) {
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.kv_pos + key0, left * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (LDS_AS void *)p_stage(stage), 4, lane * 4,
+                                               0, 0, 0);
     }
-    if (tid < BK) {
-      const int64_t key = key0 + tid;
-      pst = key >= a.s_kv ? INT_MAX : (a.causal ? a.kv_pos[key] : INT_MIN);
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4 *>(k_lds + (kr + 16 * j) * K_STRIDE + kc * 16) = kst[j];
-    // Keys 4 vq .. 4 vq + 3 sit in a 16-key group; inside a group, position
-    // (gg * 8 + hh * 4 + j) holds key (hh * 8 + gg * 4 + j), so the 8 keys an
-    // MFMA lane needs for one k-step are contiguous.
-    const int grp = vq >> 2, q4 = vq & 3;
-    const int col_elem = grp * 16 + (q4 & 1) * 8 + (q4 >> 1) * 4;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {  // dword w of each row = d pair (vc*8 + 2w, +1)
-      const uint32_t x0 = vst[0][w], x1 = vst[1][w], x2 = vst[2][w], x3 = vst[3][w];
-      const u32x2 even{(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-      const u32x2 odd{(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-      const int d0 = vc * 8 + 2 * w;
-      *reinterpret_cast<u32x2 *>(vt_lds + d0 * VT_STRIDE + col_elem * 2) = even;
-      *reinterpret_cast<u32x2 *>(vt_lds + (d0 + 1) * VT_STRIDE + col_elem * 2) = odd;
-    }
-    if (tid < BK) pos_lds[tid] = pst;
   };
 
   // ---- running state: one query per lane ----
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY;  // running max, in units of log2 (scaled scores)
+  float m_run = -INFINITY;  // reference max for the exponentials (log2 units)
   float l_run = 0.f;        // this lane's half of the running sum
+  float alpha = 1.f;        // rescale factor pending for acc / l_run
+  bool pending = false;
+  bool done = !wave_has_rows || nt == 0;
+  f32x16 sc[2];             // scores of the current tile
 
-  if (ntiles > 0) load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // every wave is done with the previous tile
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
+  auto tile_pos = [&](auto stage, int i) -> int32_t { return p_stage(stage)[i]; };
+  // Whole tile after this wave's last query (causal): nothing visible here or later.
+  auto tile_skip = [&](auto stage) -> bool { return a.causal && tile_pos(stage, 0) > w_qmax; };
 
-    const int64_t key0 = static_cast<int64_t>(t) * BK;
-    const int32_t tile_pmin = pos_lds[0];
-    const int32_t tile_pmax = pos_lds[BK - 1];
-    // Tile entirely after this wave's last query: nothing visible.
-    if (!wave_has_rows || tile_pmin > w_qmax) continue;
-    const bool need_mask = key0 + BK > a.s_kv || tile_pmax > w_qmin;
-
-    // S^T[key][query] = K Q^T; block kb covers keys kb*32 .. kb*32+31.
-    f32x16 s[2];
+  // Scores S^T = K Q^T of the K tile in `stage`.
+  auto qk = [&](auto stage, f32x16 *s) {
+    const unsigned char *kb_base = k_stage(stage);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const unsigned char *krow = k_lds + (kb * 32 + col) * K_STRIDE + hi * 16;
+    for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(krow + ds * 32);
+    for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kb_base + koff[ds] + kb * 32 * ROW_B);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ds], s[kb], 0, 0, 0);
       }
-    }
-    // Accumulator element e of block kb is key kb*32 + (e/4)*8 + hi*4 + e%4.
-    if (need_mask) {
+  };
+
+  // Mask (diagonal / ragged tiles), row max and lazy rescale decision for the
+  // scores of tile t held in `stage`.
+  auto prepare = [&](int t, auto stage, f32x16 *s) {
+    const int64_t key0 = static_cast<int64_t>(t) * BK;
+    const bool ragged = key0 + BK > a.s_kv;
+    if (ragged || (a.causal && tile_pos(stage, BK - 1) > w_qmin)) {
+      // Branch-free selects: key index past the block, or position after the query.
+      const int lim = ragged ? static_cast<int>(a.s_kv - key0) : BK;
+      const int32_t *pp = p_stage(stage);
+      const int32_t qp = a.causal ? qpos : INT_MAX;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-          const int32_t *pp = pos_lds + kb * 32 + e4 * 8 + hi * 4;
+          const int kk = kb * 32 + e4 * 8 + hi * 4;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (pp[j] > qpos) s[kb][e4 * 4 + j] = -INFINITY;
+          for (int j = 0; j < 4; ++j) {
+            const bool out = (kk + j >= lim) | (pp[kk + j] > qp);
+            s[kb][e4 * 4 + j] = out ? -INFINITY : s[kb][e4 * 4 + j];
+          }
         }
     }
     float mx = -INFINITY;
@@ -245,37 +293,101 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+    mx = fmaxf(mx, swap_halves(mx)) * sl2;
+    if (__any(mx > m_run + TAU)) {
+      const float m_new = fmaxf(m_run, mx);
+      // 0 when only m_run is -inf; 1 for a row that has seen no key at all
+      alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
+      m_run = m_new;
+      pending = true;
+    }
+  };
 
-    // P (bf16) in the B-operand layout of O^T += V^T P^T: k-step ks covers
-    // keys ks*16 .. ks*16+15 and uses accumulator elements (ks%2)*8 .. +7 of
-    // block ks/2, i.e. keys {hi*4 + 0..3, 8 + hi*4 + 0..3} of the 16.
-    bf16x8 pb[4];
+  // P = 2^(S * scale * log2 e - m) as the bf16 B operand of O^T += V^T P^T:
+  // k-step ks covers keys ks*16 .. ks*16+15 and uses accumulator elements
+  // (ks%2)*8 .. +7 of block ks/2, i.e. keys {hi*4 + 0..3, 8 + hi*4 + 0..3}.
+  auto softmax = [&](const f32x16 *s, bf16x8 *pb) {
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    if (pending) l_run *= alpha;
+    // The row sum uses the fp32 probabilities (before bf16 rounding), so lse
+    // carries no bf16 error; four partial sums keep the dependency chains short.
+    float lp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = exp2_fast(fmaf(s[ks >> 1][(ks & 1) * 8 + e], sl2, -m_use));
-        l_run += p;
+        lp[e & 3] += p;
         pb[ks][e] = static_cast<__bf16>(p);
       }
     }
+    l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+  };
+
+  // O^T += V^T P^T with the V tile in `stage` (after any pending rescale).
+  auto pv = [&](auto stage, const bf16x8 *pb) {
+    if (pending) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const unsigned char *vrow = vt_lds + (db * 32 + col) * VT_STRIDE + hi * 16;
+      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+      pending = false;
+    }
+    const unsigned char *vb = v_stage(stage);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vrow + ks * 32);
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(vb + voff[0][db] + ks * 16 * ROW_B));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(vb + voff[1][db] + ks * 16 * ROW_B));
+        const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], acc[db], 0, 0, 0);
       }
+  };
+
+  // ---- prologue: tiles 0 and 1 in flight, scores of tile 0 ----
+  using St0 = std::integral_constant<int, 0>;
+  using St1 = std::integral_constant<int, 1>;
+  using St2 = std::integral_constant<int, 2>;
+  if (nt > 0) issue_tile(0, St0{});
+  if (nt > 1) issue_tile(1, St1{});
+  wait_own_loads();
+  __syncthreads();
+  if (!done && tile_skip(St0{})) done = true;
+  if (!done) {
+    qk(St0{}, sc);
+    prepare(0, St0{}, sc);
+  }
+
+  // ---- main loop; tile t lives in stage t % 3 (compile-time per unrolled step) ----
+  auto step = [&](auto stage_c, int t) {
+    constexpr int S = decltype(stage_c)::value;
+    using SC = std::integral_constant<int, S>;
+    using SN = std::integral_constant<int, (S + 1) % NSTAGE>;
+    using SL = std::integral_constant<int, (S + 2) % NSTAGE>;
+    wait_own_loads();  // this wave's part of tile t+1 has landed ...
+    __syncthreads();   // ... and everyone's; every wave is done with tile t-1
+    if (t + 2 < nt) issue_tile(t + 2, SL{});
+    if (!done) {
+      const bool have_next = t + 1 < nt && !tile_skip(SN{});
+      f32x16 sn[2];
+      bf16x8 pb[4];
+      qk(SN{}, sn);        // scores of tile t+1 (unused if !have_next)
+      softmax(sc, pb);     // probabilities of tile t
+      pv(SC{}, pb);
+      if (have_next) {
+        prepare(t + 1, SN{}, sn);
+        sc[0] = sn[0];
+        sc[1] = sn[1];
+      } else {
+        done = true;
+      }
     }
+  };
+  for (int t = 0; t < nt; t += NSTAGE) {
+    step(St0{}, t);
+    if (t + 1 < nt) step(St1{}, t + 1);
+    if (t + 2 < nt) step(St2{}, t + 2);
   }
 
   // ---- epilogue: o_b = acc / l, lse_b = (m + log2 l) ln 2; optional merge ----
@@ -327,7 +439,7 @@ hipError_t launch_hw(const AttnArgs &a, hipStream_t stream) {
   const int64_t blocks = ntb * a.b * a.n_kv * ((a.n_q / a.n_kv) / HW);
   if (blocks == 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  attn_bf16_kernel<HW><<<static_cast<unsigned>(blocks), THREADS, LDS_BYTES, stream>>>(a);
+  attn_bf16_kernel<HW><<<static_cast<unsigned>(blocks), THREADS, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -335,6 +447,7 @@ hipError_t launch_hw(const AttnArgs &a, hipStream_t stream) {
 
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t stream) {
   const int g = a.n_q / a.n_kv;
+  if (g % 8 == 0) return launch_hw<8>(a, stream);
   if (g % 4 == 0) return launch_hw<4>(a, stream);
   if (g % 2 == 0) return launch_hw<2>(a, stream);
   return launch_hw<1>(a, stream);
