@@ -15,11 +15,14 @@ Prints progress on stderr and ONE JSON line on stdout.
 """
 
 import argparse
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PEAK_F32_MFMA_TFLOPS = 157.3
@@ -47,6 +50,26 @@ def visible_pairs_per_step(kind, S, N, rank, causal):
     return out
 
 
+def committed_traffic(w):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary, if it was taken on this workload with the current kernel source
+    (else None)."""
+    if w.name != "llama3_70b_128k_zigzag" or w.rank != 0 or w.kind != "zigzag":
+        return None
+    try:
+        text = open(os.path.join(ROOT, "profiles",
+                                 "attn_bf16_llama3_70b_128k_zigzag_counters.md")).read()
+        src = open(os.path.join(ROOT, "ring_attention_context_amd", "csrc", "attn_bf16.hip"),
+                   "rb").read()
+    except OSError:
+        return None
+    m = re.search(r"traffic = ([\d,]+) bytes per launch", text)
+    h = re.search(r"sha256 = ([0-9a-f]{64})", text)
+    if not m or not h or h.group(1) != hashlib.sha256(src).hexdigest():
+        return None
+    return int(m.group(1).replace(",", ""))
+
+
 def cpu_baseline(w, seconds_hint=15.0):
     """Time the fp64 CPU oracle (as it stands) on a bounded sample of the same
     workload: a few query rows x all heads against the full sequence."""
@@ -59,9 +82,10 @@ def cpu_baseline(w, seconds_hint=15.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    # size the sample so the oracle runs roughly seconds_hint seconds
-    per_row = w.n_q * w.S * (4 * w.d + 20) / 2.0      # flops-ish per row, causal ~S/2 keys
-    rows_n = int(max(8, min(256, seconds_hint * 2.0e9 / per_row)))
+    # size the sample so the oracle runs roughly seconds_hint seconds (the NumPy
+    # oracle sustains roughly 25 GFLOP/s of fp64 on a 16-core host)
+    per_row = 4 * w.d * w.n_q * (w.S / 2.0 if w.causal else w.S)
+    rows_n = int(max(8, min(512, seconds_hint * 2.5e10 / per_row)))
     rows = synth.sample_rows(w.c, rows_n, w.seed)
     inp = synth.draw(w, q_rows=rows)
     q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)[rows]
@@ -88,6 +112,9 @@ def main():
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device-to-device copy (a known-size "
+                         "reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -120,6 +147,14 @@ def main():
     q, kc, vc = runner.ring_inputs(inp.q, inp.k, inp.v, w.dtype, w.kind, w.N, dev)
     del inp
     log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
+
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] calibration copy: 268435456 bytes read + 268435456 bytes written")
 
     compute = torch.cuda.Stream(dev)
     copy = torch.cuda.Stream(dev)
@@ -159,7 +194,8 @@ def main():
     achieved = args.steps * total_flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": committed_traffic(w),
                 "kernel": "attn_bf16_kernel" if w.dtype == "bf16" else "attn_f32_kernel",
                 "avg_launch_ms": round(kern_ms / launches, 4), "launches": launches,
                 "flops_per_launch_avg": total_flops / w.N}
