@@ -101,6 +101,84 @@ def cpu_baseline(w, seconds_hint=15.0):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def time_ring(w, q, kc, vc, warmup, steps, flags=0):
+    """Mean ms per ra_ring_fwd call and the median per-step ms (step events)."""
+    import numpy as np
+    import torch
+    from ring_attention_context_amd import runner
+    dev = q.device
+    compute, copy = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    call = runner.RingCall(q, kc, vc, kind=w.kind, S=w.S, N=w.N, rank=w.rank, causal=w.causal,
+                           scale=w.scale, flags=flags, compute=compute, copy=copy)
+    for _ in range(warmup):
+        call()
+    evs = [call.make_events() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(events=evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_ms = np.median([[e[i].elapsed_time(e[i + 1]) for i in range(w.N)] for e in evs], axis=0)
+    return ms, step_ms.tolist()
+
+
+def run_sweep(path, warmup, steps):
+    """Every workload at its measured rank, then the 128K / 70B shape with the
+    contiguous, zig-zag and striped maps for all 8 ranks (per-step times give
+    the ring's step-max timeline and the measured load-balance efficiency)."""
+    import numpy as np
+    import torch
+    import synth
+    from ring_attention_context_amd import runner
+    dev = torch.device("cuda:0")
+    out = {"workloads": [], "imbalance": []}
+    for name, w in synth.WORKLOADS.items():
+        inp = synth.draw(w)
+        q, kc, vc = runner.ring_inputs(inp.q, inp.k, inp.v, w.dtype, w.kind, w.N, dev)
+        del inp
+        ms, step_ms = time_ring(w, q, kc, vc, warmup, steps)
+        pairs = sum(visible_pairs_per_step(w.kind, w.S, w.N, w.rank, w.causal))
+        tf = 4 * w.b * w.n_q * w.d * pairs / (ms * 1e-3) / 1e12
+        rec = {"workload": name, "kind": w.kind, "rank": w.rank, "ms": ms, "tflops": tf,
+               "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS, "step_ms": step_ms,
+               "visible_pairs": pairs, "dtype": w.dtype}
+        out["workloads"].append(rec)
+        log(f"[sweep] {name}: {ms:.3f} ms/call, {tf:.1f} TFLOP/s")
+        del q, kc, vc
+        torch.cuda.empty_cache()
+    base = synth.WORKLOADS["llama3_70b_128k_zigzag"]
+    inp = synth.draw(base)
+    for kind in ("contiguous", "zigzag", "striped"):
+        w0 = base.with_(kind=kind)
+        q = runner.host_to_device(inp.q, w0.dtype, dev)
+        kc = runner.chunk_kv(runner.host_to_device(inp.k, w0.dtype, dev), kind, w0.N)
+        vc = runner.chunk_kv(runner.host_to_device(inp.v, w0.dtype, dev), kind, w0.N)
+        t = np.zeros((w0.N, w0.N))
+        work = np.zeros((w0.N, w0.N), dtype=np.int64)
+        for rank in range(w0.N):
+            w = w0.with_(rank=rank)
+            ms, step_ms = time_ring(w, q, kc, vc, warmup, steps)
+            t[rank] = step_ms
+            work[rank] = visible_pairs_per_step(kind, w.S, w.N, rank, True)
+            log(f"[sweep] {kind} rank {rank}: {ms:.3f} ms/call")
+        ring_ms = float(t.max(axis=0).sum())
+        eta_meas = float(t.sum() / w0.N / ring_ms)
+        eta_elem = float(work.sum() / w0.N / work.max(axis=0).sum())
+        flops = 4 * w0.b * w0.n_q * w0.d * work.sum() / w0.N
+        out["imbalance"].append({
+            "kind": kind, "step_ms": t.tolist(), "pairs": work.tolist(),
+            "ring_ms_step_max": ring_ms, "eta_measured": eta_meas, "eta_element": eta_elem,
+            "ring_tflops_per_rank": flops / (ring_ms * 1e-3) / 1e12})
+        log(f"[sweep] {kind}: ring (step-max) {ring_ms:.2f} ms, eta measured {eta_meas:.4f}, "
+            f"element-level {eta_elem:.4f}")
+        del q, kc, vc
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    log(f"[sweep] wrote {path}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +190,9 @@ def main():
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--sweep", default=None,
+                    help="write a JSON file with every workload and the per-rank map "
+                         "imbalance study (no contract line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size "
                          "reference for HBM byte counters)")
@@ -132,6 +213,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        run_sweep(args.sweep, args.warmup, max(2, args.steps // 3))
+        return
 
     w = synth.WORKLOADS[args.workload]
     if args.kind:
