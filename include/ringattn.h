@@ -62,6 +62,16 @@ typedef enum {
 
 typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
 
+/* Layout of v in ra_block_attn_fwd. */
+typedef enum {
+  RA_V_ROWS = 0,        /* [b, s_kv, n_kv, d], the layout of k                */
+  RA_V_TRANSPOSED = 1   /* [b, n_kv, d, s_kv]: element (i, s, h, e) at
+                           ((i*n_kv + h)*d + e)*s_kv + s; bf16 only, and
+                           s_kv % 8 == 0 (16-byte aligned rows). Produced by
+                           ra_v_transpose. The kernel then reads V^T tiles
+                           with plain 16-byte LDS reads.                     */
+} ra_v_layout;
+
 /*
  * ra_partition -- global positions of the c = S/N tokens rank `rank` owns, in
  * its local order ("Context Parallelism and Ring Attention" §2, §6).
@@ -89,7 +99,7 @@ typedef struct ra_attn_desc {
   int32_t dtype;      /* ra_dtype of q, k and v                              */
   int32_t causal;     /* 1: apply the causal rule on q_pos / kv_pos          */
   float scale;        /* softmax scale; 0 selects 1/sqrt(d); must be >= 0    */
-  int32_t reserved;   /* must be 0                                           */
+  int32_t v_layout;   /* ra_v_layout of v (RA_V_ROWS unless stated)         */
   const int32_t *q_pos;   /* device [s_q] global positions, non-decreasing   */
   const int32_t *kv_pos;  /* device [s_kv] global positions, non-decreasing  */
 } ra_attn_desc;
@@ -99,7 +109,8 @@ typedef struct ra_attn_desc {
  * Attention" §3 for the keys of one block:
  *   m_b = max x, l_b = sum e^{x - m_b}, o_b = (1/l_b) sum e^{x - m_b} v,
  *   lse_b = m_b + ln l_b,  x = scale * q.k  over the keys visible to the query.
- * q: device [b, s_q, n_q, d]; k, v: device [b, s_kv, n_kv, d] (dtype);
+ * q: device [b, s_q, n_q, d]; k: device [b, s_kv, n_kv, d] (dtype);
+ * v: device [b, s_kv, n_kv, d], or [b, n_kv, d, s_kv] with RA_V_TRANSPOSED;
  * o_b: device float32 [b, s_q, n_q, d]; lse_b: device float32 [b, s_q, n_q],
  * both fully overwritten. Rows with no visible key get (0, -inf).
  * q_pos / kv_pos are read only when causal; positions out of order give
@@ -107,6 +118,16 @@ typedef struct ra_attn_desc {
  */
 ra_status ra_block_attn_fwd(const ra_attn_desc *desc, const void *q, const void *k,
                             const void *v, float *o_b, float *lse_b, void *stream);
+
+/*
+ * ra_v_transpose -- vt <- v with the token and channel axes exchanged per
+ * head: v [b, s, n_kv, d] -> vt [b, n_kv, d, s] (the RA_V_TRANSPOSED layout
+ * of ra_block_attn_fwd). Values are moved bit for bit, not converted.
+ * dtype RA_BF16 or RA_F32; v and vt are device buffers of b*s*n_kv*d
+ * elements that must not overlap. b * n_kv <= 65535.
+ */
+ra_status ra_v_transpose(int32_t b, int64_t s, int32_t n_kv, int32_t d, int32_t dtype,
+                         const void *v, void *vt, void *stream);
 
 /*
  * ra_lse_merge -- in place (o, lse) <- merge((o, lse), (o_b, lse_b)), the
@@ -155,7 +176,9 @@ ra_status ra_ring_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
  *           the merged result over all N blocks.
  * workspace: device, >= ra_ring_workspace_bytes(); holds the double buffer
  *           for the incoming K/V chunk and the position maps. Its contents on
- *           entry do not matter.
+ *           entry do not matter. For bf16 with c % 8 == 0 the V half of each
+ *           buffer holds the chunk transposed (RA_V_TRANSPOSED, written by the
+ *           copy stream), including the rank's own chunk before step 0.
  * Step r computes the block of chunk (rank - r) mod N; the copy of the next
  * step's chunk into the idle half of the double buffer runs on `copy` while
  * step r computes on `compute` (or on `compute` with RA_RING_SERIALIZE).

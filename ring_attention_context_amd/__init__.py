@@ -20,6 +20,8 @@ from ._lib import (  # noqa: F401
     RA_PART_ZIGZAG,
     RA_RING_SERIALIZE,
     RA_RING_UNFUSED_MERGE,
+    RA_V_ROWS,
+    RA_V_TRANSPOSED,
     LIB_PATH,
     RingAttnError,
     load_library,
@@ -30,5 +32,6 @@ from ._lib import (  # noqa: F401
     ra_ring_fwd,
     ra_ring_workspace_bytes,
     ra_status_str,
+    ra_v_transpose,
     ring_desc,
 )

@@ -18,11 +18,12 @@ RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, 1, 2, 3
 RA_PART_CONTIGUOUS, RA_PART_ZIGZAG, RA_PART_STRIPED = 0, 1, 2
 RA_F32, RA_BF16 = 0, 1
 RA_RING_SERIALIZE, RA_RING_UNFUSED_MERGE = 1, 2
+RA_V_ROWS, RA_V_TRANSPOSED = 0, 1
 
 KINDS = {"contiguous": RA_PART_CONTIGUOUS, "zigzag": RA_PART_ZIGZAG, "striped": RA_PART_STRIPED}
 
-EXPORTED = ("ra_partition", "ra_block_attn_fwd", "ra_lse_merge", "ra_ring_workspace_bytes",
-            "ra_ring_fwd", "ra_status_str", "ra_last_error")
+EXPORTED = ("ra_partition", "ra_block_attn_fwd", "ra_v_transpose", "ra_lse_merge",
+            "ra_ring_workspace_bytes", "ra_ring_fwd", "ra_status_str", "ra_last_error")
 
 
 class RingAttnError(RuntimeError):
@@ -35,7 +36,7 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [("b", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("s_q", ctypes.c_int64), ("s_kv", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("reserved", ctypes.c_int32), ("q_pos", ctypes.c_void_p),
+                ("v_layout", ctypes.c_int32), ("q_pos", ctypes.c_void_p),
                 ("kv_pos", ctypes.c_void_p)]
 
 
@@ -63,12 +64,13 @@ def load_library(path=None):
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.ra_partition.argtypes = [i32, i64, i32, i32, vp]
     lib.ra_block_attn_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp]
+    lib.ra_v_transpose.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp]
     lib.ra_lse_merge.argtypes = [i64, i32, vp, vp, vp, vp, vp]
     lib.ra_ring_workspace_bytes.argtypes = [ctypes.POINTER(RingDesc), ctypes.POINTER(ctypes.c_size_t)]
     lib.ra_ring_fwd.argtypes = [ctypes.POINTER(RingDesc), vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                 vp, vp]
-    for name in ("ra_partition", "ra_block_attn_fwd", "ra_lse_merge", "ra_ring_workspace_bytes",
-                 "ra_ring_fwd"):
+    for name in ("ra_partition", "ra_block_attn_fwd", "ra_v_transpose", "ra_lse_merge",
+                 "ra_ring_workspace_bytes", "ra_ring_fwd"):
         getattr(lib, name).restype = i32
     lib.ra_status_str.argtypes = [i32]
     lib.ra_status_str.restype = ctypes.c_char_p
@@ -136,18 +138,29 @@ def ra_partition(kind, S, N, rank):
 
 
 def ra_block_attn_fwd(q, k, v, o_b, lse_b, *, causal, scale=0.0, q_pos=None, kv_pos=None,
-                      stream=None):
-    """q [b, s_q, n_q, d], k / v [b, s_kv, n_kv, d] (bf16 or f32, same dtype);
+                      v_transposed=False, stream=None):
+    """q [b, s_q, n_q, d], k [b, s_kv, n_kv, d] (bf16 or f32, same dtype); v like k, or
+    [b, n_kv, d, s_kv] with ``v_transposed`` (bf16, see :func:`ra_v_transpose`);
     writes o_b float32 [b, s_q, n_q, d] and lse_b float32 [b, s_q, n_q].
     q_pos / kv_pos: int32 device tensors of global positions (causal only)."""
     _need_contiguous(q, k, v, o_b, lse_b, q_pos, kv_pos)
     desc = AttnDesc(b=q.shape[0], n_q=q.shape[2], n_kv=k.shape[2], d=q.shape[3],
                     s_q=q.shape[1], s_kv=k.shape[1], dtype=_dtype_code(q), causal=int(causal),
-                    scale=scale, reserved=0,
+                    scale=scale, v_layout=RA_V_TRANSPOSED if v_transposed else RA_V_ROWS,
                     q_pos=None if q_pos is None else q_pos.data_ptr(),
                     kv_pos=None if kv_pos is None else kv_pos.data_ptr())
     _check(load_library().ra_block_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                             _ptr(o_b), _ptr(lse_b), _stream(stream)))
+
+
+def ra_v_transpose(v, vt, stream=None):
+    """vt [b, n_kv, d, s] <- v [b, s, n_kv, d] (bf16 or f32, moved bit for bit)."""
+    _need_contiguous(v, vt)
+    b, s, n_kv, d = v.shape
+    if tuple(vt.shape) != (b, n_kv, d, s) or vt.dtype != v.dtype:
+        raise RingAttnError(RA_ERR_INVALID_ARG, "vt must be [b, n_kv, d, s] of v's dtype")
+    _check(load_library().ra_v_transpose(b, s, n_kv, d, _dtype_code(v), _ptr(v), _ptr(vt),
+                                         _stream(stream)))
 
 
 def ra_lse_merge(o, lse, o_b, lse_b, stream=None):

@@ -19,7 +19,14 @@ ra_status validate_attn(const ra_attn_desc *d, const void *q, const void *k, con
     return fail(RA_ERR_INVALID_ARG, "attention: more than 2^31 - 1 rows");
   if (!(d->scale >= 0.f) || std::isinf(d->scale))
     return fail(RA_ERR_INVALID_ARG, "attention: scale must be finite and >= 0");
-  if (d->reserved != 0) return fail(RA_ERR_INVALID_ARG, "attention: reserved must be 0");
+  if (d->v_layout != RA_V_ROWS && d->v_layout != RA_V_TRANSPOSED)
+    return fail(RA_ERR_INVALID_ARG, "attention: unknown v_layout %d", d->v_layout);
+  if (d->v_layout == RA_V_TRANSPOSED) {
+    if (d->dtype != RA_BF16)
+      return fail(RA_ERR_UNSUPPORTED, "attention: RA_V_TRANSPOSED needs bf16");
+    if (d->s_kv % 8)
+      return fail(RA_ERR_INVALID_ARG, "attention: RA_V_TRANSPOSED needs s_kv %% 8 == 0");
+  }
   if (d->causal != 0 && d->causal != 1)
     return fail(RA_ERR_INVALID_ARG, "attention: causal must be 0 or 1");
   if (d->dtype == RA_BF16) {
@@ -71,6 +78,7 @@ extern "C" ra_status ra_block_attn_fwd(const ra_attn_desc *desc, const void *q, 
   a.scale = desc->scale > 0.f ? desc->scale : 1.0f / std::sqrt(static_cast<float>(desc->d));
   a.causal = desc->causal;
   a.merge = 0;
+  a.v_layout = desc->v_layout;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = desc->dtype == RA_BF16 ? ra::launch_attn_bf16(a, s) : ra::launch_attn_f32(a, s);
   return ra::hip_check(err, "ra_block_attn_fwd launch");

@@ -3,9 +3,9 @@
 // Computes, for the keys of one block, the statistics of "Context
 // Parallelism and Ring Attention" §3: m_b = max x, l_b = sum e^{x - m_b},
 // o_b = (1/l_b) sum e^{x - m_b} v, lse_b = m_b + ln l_b, scanning the block
-// tile by tile with a running max, running sum and unnormalised output (the
-// single-GPU form of the same identity, §3). The causal rule of §5 is applied
-// on original positions (§6 "the cost of reordering"); positions are
+// tile by tile with a running reference, running sum and unnormalised output
+// (the single-GPU form of the same identity, §3). The causal rule of §5 is
+// applied on original positions (§6 "the cost of reordering"); positions are
 // non-decreasing, so tiles past a query tile's last position are never
 // loaded (the tile skipping of §7), and only tiles that straddle the
 // diagonal, or the ragged last tile, evaluate the element mask.
@@ -16,26 +16,43 @@
 //     key/value head (GQA), so every K/V tile staged in LDS serves all eight
 //     waves (two per SIMD);
 //   * K/V tiles of 64 keys go from HBM straight into LDS (buffer loads with
-//     the LDS destination, no register staging), through a ring of three
-//     stages: one barrier per tile, and the load of tile t+2 overlaps the
-//     math on tiles t and t+1. Out-of-range keys come back as zeros from the
-//     buffer descriptor's bounds check;
-//   * both tiles are row-major in LDS with the 16-byte chunks of each 256-byte
-//     row XOR-swizzled by the row index, so the MFMA operand reads are
-//     bank-conflict free: K rows with ds_read_b128, V^T operands with the
-//     gfx950 transposing read ds_read_b64_tr_b16;
+//     the LDS destination, no register staging) through a ring of four
+//     stages, one barrier per tile; out-of-range keys come back as zeros from
+//     the buffer descriptor's bounds check;
+//   * K rows are row-major in LDS with the 16-byte chunks of each 256-byte row
+//     XOR-swizzled by the row index, so the operand reads (ds_read_b128) are
+//     bank-conflict free. V comes either row-major (read with the gfx950
+//     transposing ds_read_b64_tr_b16) or already transposed, V^T [d, keys]
+//     (VT = true; plain ds_read_b128 of 128-byte rows, swizzled the same way),
+//     which moves a third of the LDS bytes per instruction of the former;
 //   * scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16: each lane then holds 32 keys of ONE query, so
-//     row max and row sum are in-lane plus one exchange with the lane 32
-//     away, and the probabilities convert in place into the B operand of
-//     O^T = V^T P^T, whose accumulator keeps one query per lane;
-//   * software pipeline inside each wave: the score MFMAs of tile t+1 are
-//     issued together with the exponentials of tile t, and the P V MFMAs of
-//     tile t together with the max / mask of tile t+1;
+//     v_mfma_f32_32x32x16_bf16: each lane then holds keys of ONE query, so
+//     row reductions are in-lane plus one exchange with the lane 32 away
+//     (v_permlane32_swap), and the probabilities convert in place into the B
+//     operand of O^T = V^T P^T, whose accumulator keeps one query per lane.
+//     With V^T the K rows are read in a permuted order (bits 2 and 3 of the
+//     row swapped) so that each lane's probabilities are 8 consecutive keys,
+//     the k-slots of one 16-byte V^T read;
+//   * each tile runs in two phases: phase 1 issues the score MFMAs of tile
+//     t+1 and the exponentials of tile t; phase 2 issues the P V MFMAs of tile
+//     t. Waves w and w+4 share a SIMD; the second group runs the two phases
+//     in the opposite order (P V of tile t-1 first), so the pair overlaps one
+//     wave's exponentials with the other's MFMAs. The fourth LDS stage keeps
+//     tile t-1 resident for that group while tile t+2 streams in;
 //   * exponentials run in base 2 (v_exp_f32) with the scale folded into one
-//     FMA; the running max is updated lazily: the accumulator is rescaled only
-//     when a row max grows by more than 2^8 (exact: o and l share the same
-//     reference, so o = acc / l is unchanged).
+//     FMA. The reference of the exponentials is updated lazily from the tile
+//     sum instead of a per-tile max: probabilities are formed against the
+//     current reference, and when a row's tile sum exceeds 2^8 the reference
+//     moves up by log2 of it, so later probabilities stay near 1. A tile is
+//     redone with its true row max only when a row has no reference yet or
+//     the sum leaves [0, 2^32] (a score far above the reference). The result
+//     is exact for any reference (o = acc / l, lse = ref + log2 l) as long as
+//     nothing overflows, which those bounds guarantee;
+//   * two row sums: l over the fp32 probabilities gives lse, and l^ over the
+//     bf16-rounded probabilities that enter P V (one v_dot2 per pair) divides
+//     the accumulator, so o is a convex combination of V rows with exactly the
+//     weights the MFMA used: a dominant key contributes its V row with no
+//     rounding error, which matters for peaked rows.
 // Workgroups are ordered heaviest query tile first (later positions see more
 // keys under the causal rule); consecutive workgroups cover the KV heads of one
 // token block, so with the round-robin dispatch over the 8 XCDs each XCD's L2
@@ -50,9 +67,11 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
+#define INLINE __attribute__((always_inline))
 
 constexpr int D = 128;
 constexpr int QW = 32;                       // query tokens per wave
@@ -60,8 +79,9 @@ constexpr int WAVES = 8;
 constexpr int THREADS = WAVES * 64;
 constexpr int BK = 64;                       // keys per tile
 constexpr int ROW_B = D * 2;                 // bytes per key row
+constexpr int VT_ROW_B = BK * 2;             // bytes per d-row of a V^T tile
 constexpr int TILE_B = BK * ROW_B;           // 16 KiB
-constexpr int NSTAGE = 3;
+constexpr int NSTAGE = 4;
 constexpr int LOADS_PER_WAVE = TILE_B / (1024 * WAVES);  // 1 KiB per wave instruction
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -70,13 +90,24 @@ constexpr int BUF_DWORD3 = 0x00020000;       // raw buffer, 32-bit data format
 
 static_assert(LOADS_PER_WAVE * 1024 * WAVES == TILE_B, "tile split over waves");
 
-// 16-byte chunk swizzle of a row: a 4-bit rotation of the row index.
+// 16-byte chunk swizzle of a 256-byte K row: a 4-bit rotation of the row index.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// 16-byte chunk swizzle of a 128-byte V^T row.
+__device__ __forceinline__ int swz_vt(int r) { return (r >> 1) & 7; }
+// K row read by lane column c when V is transposed: bits 2 and 3 swapped.
+__device__ __forceinline__ int kperm(int c) { return (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value of the lane 32 away (lanes l and l ^ 32 hold the two key halves of a query).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+// Max / sum over the lane pair (l, l ^ 32), which holds the two key halves of a query.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Number of keys with position <= p in the non-decreasing kv_pos[0, n).
 __device__ __forceinline__ int64_t count_le(const int32_t *kv_pos, int64_t n, int32_t p) {
@@ -101,24 +132,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 // counters are left alone). A barrier after it publishes the data to all waves.
 __device__ __forceinline__ void wait_own_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int HW>
+template <int HW, bool VT>
 __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // One LDS object per stage and operand: the compiler then sees that the
   // asynchronous loads into one stage never alias the reads of the others and
   // does not drain them before every LDS read.
   __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE_B], k_lds1[TILE_B],
-      k_lds2[TILE_B];
+      k_lds2[TILE_B], k_lds3[TILE_B];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE_B], v_lds1[TILE_B],
-      v_lds2[TILE_B];
-  __shared__ __attribute__((aligned(16))) int32_t p_lds0[BK], p_lds1[BK], p_lds2[BK];
-  auto k_stage = [&](auto s) -> unsigned char * {
-    return decltype(s)::value == 0 ? k_lds0 : (decltype(s)::value == 1 ? k_lds1 : k_lds2);
+      v_lds2[TILE_B], v_lds3[TILE_B];
+  __shared__ __attribute__((aligned(16))) int32_t p_lds0[BK], p_lds1[BK], p_lds2[BK], p_lds3[BK];
+  auto k_stage = [&](auto s) INLINE -> unsigned char * {
+    constexpr int v = decltype(s)::value;
+    return v == 0 ? k_lds0 : v == 1 ? k_lds1 : v == 2 ? k_lds2 : k_lds3;
   };
-  auto v_stage = [&](auto s) -> unsigned char * {
-    return decltype(s)::value == 0 ? v_lds0 : (decltype(s)::value == 1 ? v_lds1 : v_lds2);
+  auto v_stage = [&](auto s) INLINE -> unsigned char * {
+    constexpr int v = decltype(s)::value;
+    return v == 0 ? v_lds0 : v == 1 ? v_lds1 : v == 2 ? v_lds2 : v_lds3;
   };
-  auto p_stage = [&](auto s) -> int32_t * {
-    return decltype(s)::value == 0 ? p_lds0 : (decltype(s)::value == 1 ? p_lds1 : p_lds2);
+  auto p_stage = [&](auto s) INLINE -> int32_t * {
+    constexpr int v = decltype(s)::value;
+    return v == 0 ? p_lds0 : v == 1 ? p_lds1 : v == 2 ? p_lds2 : p_lds3;
   };
 
   constexpr int TB = WAVES / HW;  // 32-token blocks per workgroup
@@ -127,6 +161,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   const int lane = tid & 63;
   const int col = lane & 31;  // query within the wave
   const int hi = lane >> 5;   // which half of the MFMA k-slots this lane holds
+  const bool grp_b = wave >= WAVES / 2;  // runs its tile phases in the opposite order
 
   // ---- workgroup -> (batch, kv head, head group, token block) ----
   const int g = a.n_q / a.n_kv;
@@ -180,17 +215,24 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   const float sl2 = a.scale * LOG2E;
 
   // ---- per-lane LDS offsets of the MFMA operands (within one stage) ----
-  // K: lane (col, hi) reads key row kb*32 + col, logical chunk 2*ds + hi.
+  // K: lane (col, hi) reads key row krow (+32 for the second key block),
+  // logical chunk 2*ds + hi.
+  const int krow = VT ? kperm(col) : col;
   uint32_t koff[D / 16];
 #pragma unroll
   for (int ds = 0; ds < D / 16; ++ds)
-    koff[ds] = col * ROW_B + ((((2 * ds + hi) ^ swz(col & 15))) << 4);
-  // V^T via the transposing read: in each 16-lane group gq, lane s reads 8 bytes
-  // of key row r (4 rows per group) so that lane j of the group receives
+    koff[ds] = krow * ROW_B + ((((2 * ds + hi) ^ swz(krow & 15))) << 4);
+  // V^T operand of k-step ks: with V^T staged, lane (col, hi) reads d-row col
+  // (+32 per d block), keys ks*16 + hi*8 .. +7. With V row-major, the
+  // transposing read: in each 16-lane group gq, lane s reads 8 bytes of key
+  // row r (4 rows per group) so that lane j of the group receives
   // V[k0 + 0..3][d0 + j]; call c covers keys {0..3, 8..11} + 4*(gq>>1) of a
   // 16-key step, matching the k-slots of P in the B operand.
   uint32_t voff[2][D / 32];
-  {
+  if constexpr (VT) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) voff[0][ks] = col * VT_ROW_B + (((2 * ks + hi) ^ swz_vt(col)) << 4);
+  } else {
     const int gq = lane >> 4, s = lane & 15;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -208,27 +250,41 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   const unsigned char *vg = static_cast<const unsigned char *>(a.v);
   const int64_t kv_row_bytes = static_cast<int64_t>(a.n_kv) * D * 2;
   const int64_t kv_base = (static_cast<int64_t>(bi) * a.s_kv * a.n_kv + kvh) * D * 2;
-  uint32_t goff[LOADS_PER_WAVE];  // lane's byte offset within the tile's rows
+  // V^T [b, n_kv, d, s_kv]: d-rows of s_kv keys.
+  const int64_t vt_stride = a.s_kv * 2;
+  const int64_t vt_base = (static_cast<int64_t>(bi) * a.n_kv + kvh) * D * vt_stride;
+  uint32_t goff[LOADS_PER_WAVE], vgoff[LOADS_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+    // K (and row-major V): 4 rows of 256 bytes per instruction.
     const int row = 4 * (wave + WAVES * i) + (lane >> 4);
     const int lc = (lane & 15) ^ swz(row & 15);
     goff[i] = static_cast<uint32_t>(row * kv_row_bytes + lc * 16);
+    // V^T: 8 d-rows of 128 bytes per instruction.
+    const int vrow = 8 * (wave + WAVES * i) + (lane >> 3);
+    vgoff[i] = static_cast<uint32_t>(vrow * vt_stride + (((lane & 7) ^ swz_vt(vrow)) << 4));
   }
-  auto issue_tile = [&](int t, auto stage) {
+  auto issue_tile = [&](int t, auto stage) INLINE {
     const int64_t key0 = static_cast<int64_t>(t) * BK;
     const int64_t left = a.s_kv - key0;  // rows before the end of the block
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + kv_base + key0 * kv_row_bytes,
                                                 (left - 1) * kv_row_bytes + D * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + kv_base + key0 * kv_row_bytes,
-                                                (left - 1) * kv_row_bytes + D * 2);
+    // V^T: keys past the block in a d-row read the next d-row's first keys
+    // (finite values that meet a zero probability) or, for the last row,
+    // zeros from the bounds check.
+    const __amdgpu_buffer_rsrc_t rv =
+        VT ? make_rsrc(vg + vt_base + key0 * 2, (D - 1) * vt_stride + left * 2)
+           : make_rsrc(vg + kv_base + key0 * kv_row_bytes, (left - 1) * kv_row_bytes + D * 2);
 #pragma unroll
     for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-      const int r0 = 4 * (wave + WAVES * i);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (LDS_AS void *)(k_stage(stage) + r0 * ROW_B), 16, goff[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (LDS_AS void *)(v_stage(stage) + r0 * ROW_B), 16, goff[i], 0, 0, 0);
+          rk, (LDS_AS void *)(k_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16, goff[i], 0, 0, 0);
+      if constexpr (VT)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (LDS_AS void *)(v_stage(stage) + (wave + WAVES * i) * 1024), 16, vgoff[i], 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (LDS_AS void *)(v_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16, goff[i], 0, 0, 0);
     }
     if (a.causal && wave == 0) {
       const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.kv_pos + key0, left * 4);
@@ -241,34 +297,37 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY;  // reference max for the exponentials (log2 units)
-  float l_run = 0.f;        // this lane's half of the running sum
+  float m_run = -INFINITY;  // reference of the exponentials (log2 units)
+  float l_run = 0.f;        // this lane's half of the running sum (fp32 probabilities)
+  float lh_run = 0.f;       // ... of the bf16-rounded probabilities fed to P V
+  float lt = 0.f;           // this lane's half of the current tile's sum
+  float lht = 0.f;          // ... and of its bf16-rounded probabilities
   float alpha = 1.f;        // rescale factor pending for acc / l_run
-  bool pending = false;
   bool done = !wave_has_rows || nt == 0;
-  f32x16 sc[2];             // scores of the current tile
+  bool pend = false;        // second group: P V of the previous tile still to do
+  bool have_next = false;   // tile t+1 exists and is not entirely in the future
+  bf16x8 pb[4];             // probabilities of the tile whose P V is next
+  f32x16 sA[2], sB[2];      // scores of two consecutive tiles (roles alternate)
 
-  auto tile_pos = [&](auto stage, int i) -> int32_t { return p_stage(stage)[i]; };
+  auto tile_pos = [&](auto stage, int i) INLINE -> int32_t { return p_stage(stage)[i]; };
   // Whole tile after this wave's last query (causal): nothing visible here or later.
-  auto tile_skip = [&](auto stage) -> bool { return a.causal && tile_pos(stage, 0) > w_qmax; };
+  auto tile_skip = [&](auto stage) INLINE -> bool { return a.causal && tile_pos(stage, 0) > w_qmax; };
 
   // Scores S^T = K Q^T of the K tile in `stage`.
-  auto qk = [&](auto stage, f32x16 *s) {
+  auto qk = [&](auto stage, f32x16 *s) INLINE {
     const unsigned char *kb_base = k_stage(stage);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kb_base + koff[ds] + kb * 32 * ROW_B);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ds], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ds], ds == 0 ? f32x16{} : s[kb], 0, 0, 0);
       }
   };
 
-  // Mask (diagonal / ragged tiles), row max and lazy rescale decision for the
-  // scores of tile t held in `stage`.
-  auto prepare = [&](int t, auto stage, f32x16 *s) {
+  // Element mask of a diagonal or ragged tile t held in `stage`. Accumulator
+  // element e4*4 + j of key block kb holds key kk + j.
+  auto mask = [&](int t, auto stage, f32x16 *s) INLINE {
     const int64_t key0 = static_cast<int64_t>(t) * BK;
     const bool ragged = key0 + BK > a.s_kv;
     if (ragged || (a.causal && tile_pos(stage, BK - 1) > w_qmin)) {
@@ -280,7 +339,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-          const int kk = kb * 32 + e4 * 8 + hi * 4;
+          const int kk = VT ? kb * 32 + (e4 >> 1) * 16 + hi * 8 + (e4 & 1) * 4
+                            : kb * 32 + e4 * 8 + hi * 4;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const bool out = (kk + j >= lim) | (pp[kk + j] > qp);
@@ -288,113 +348,182 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
           }
         }
     }
+  };
+
+  // Row max of a tile (both key halves) in log2 units.
+  auto rowmax = [&](const f32x16 *s) INLINE -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = fmaxf(mx, swap_halves(mx)) * sl2;
-    if (__any(mx > m_run + TAU)) {
-      const float m_new = fmaxf(m_run, mx);
-      // 0 when only m_run is -inf; 1 for a row that has seen no key at all
-      alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
-      m_run = m_new;
-      pending = true;
+    return pair_max(mx) * sl2;
+  };
+
+  auto apply_rescale = [&]() INLINE {
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+      l_run *= alpha;
+      lh_run *= alpha;
+      alpha = 1.f;
     }
   };
 
-  // P = 2^(S * scale * log2 e - m) as the bf16 B operand of O^T += V^T P^T:
+  // P = 2^(S * scale * log2 e - ref) as the bf16 B operand of O^T += V^T P^T:
   // k-step ks covers keys ks*16 .. ks*16+15 and uses accumulator elements
-  // (ks%2)*8 .. +7 of block ks/2, i.e. keys {hi*4 + 0..3, 8 + hi*4 + 0..3}.
-  auto softmax = [&](const f32x16 *s, bf16x8 *pb) {
+  // (ks%2)*8 .. +7 of block ks/2. The tile sum uses the fp32 probabilities
+  // (before bf16 rounding), so lse carries no bf16 error; four partial sums
+  // keep the dependency chains short.
+  auto softmax = [&](const f32x16 *s) INLINE {
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    if (pending) l_run *= alpha;
-    // The row sum uses the fp32 probabilities (before bf16 rounding), so lse
-    // carries no bf16 error; four partial sums keep the dependency chains short.
-    float lp[4] = {0.f, 0.f, 0.f, 0.f};
+    float lp[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = exp2_fast(fmaf(s[ks >> 1][(ks & 1) * 8 + e], sl2, -m_use));
-        lp[e & 3] += p;
+        if (ks == 0 && e < 4)
+          lp[e] = p;
+        else
+          lp[e & 3] += p;
         pb[ks][e] = static_cast<__bf16>(p);
       }
     }
-    l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+    lt = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+    const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    float lh[2] = {0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        lh[e >> 2] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ks][e], pb[ks][e + 1]}, one,
+                                                     lh[e >> 2], false);
+    lht = lh[0] + lh[1];
   };
 
-  // O^T += V^T P^T with the V tile in `stage` (after any pending rescale).
-  auto pv = [&](auto stage, const bf16x8 *pb) {
-    if (pending) {
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
-      pending = false;
-    }
+  // O^T += V^T P^T with the V tile in `stage`.
+  auto pv = [&](auto stage) INLINE {
     const unsigned char *vb = v_stage(stage);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4 *)(vb + voff[0][db] + ks * 16 * ROW_B));
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4 *)(vb + voff[1][db] + ks * 16 * ROW_B));
-        const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        bf16x8 va;
+        if constexpr (VT) {
+          va = *reinterpret_cast<const bf16x8 *>(vb + voff[0][ks] + db * 32 * VT_ROW_B);
+        } else {
+          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (LDS_AS bf16x4 *)(vb + voff[0][db] + ks * 16 * ROW_B));
+          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (LDS_AS bf16x4 *)(vb + voff[1][db] + ks * 16 * ROW_B));
+          va = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        }
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], acc[db], 0, 0, 0);
       }
   };
 
-  // ---- prologue: tiles 0 and 1 in flight, scores of tile 0 ----
+  // Phase 1 of tile t: scores of tile t+1 (K in stage `sn`) on the matrix
+  // cores, probabilities of tile t (scores in `cur`) on the VALU.
+  auto phase1 = [&](int t, auto sn, const f32x16 *cur, f32x16 *nxt) INLINE {
+    apply_rescale();
+    have_next = t + 1 < nt && !tile_skip(sn);
+    qk(sn, nxt);
+    softmax(cur);
+    // Keep the probabilities in this block: otherwise the compiler sinks the
+    // exponentials past the mask branch, next to their use in P V, and the
+    // score MFMAs above lose the work they overlap with.
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 pin = pb[ks];
+      asm volatile("" ::"v"(pin));
+    }
+    const float lt_row = pair_sum(lt);
+    if (__any((m_run == -INFINITY) | !(lt_row <= 0x1p32f))) {
+      // No reference yet, or a score far above it: redo the tile against its
+      // true row max (rescaling what is accumulated so far).
+      const float m_new = fmaxf(m_run, rowmax(cur));
+      const float al = (m_run == -INFINITY || m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= al;
+      l_run *= al;
+      lh_run *= al;
+      m_run = m_new;
+      softmax(cur);
+    }
+    l_run += lt;
+    lh_run += lht;
+  };
+
+  // Phase 2 of tile t: P V with V in stage `sc`; mask of tile t+1 (positions in
+  // stage `sn`); lazy reference update from tile t's sum.
+  auto phase2 = [&](int t, auto sc, auto sn, f32x16 *nxt) INLINE {
+    if (have_next) mask(t + 1, sn, nxt);
+    pv(sc);
+    const float lt_row = pair_sum(lt);
+    const bool need = lt_row > 0x1p8f;  // 2^TAU
+    const float lg = __builtin_amdgcn_logf(lt_row);  // log2
+    alpha = need ? exp2_fast(-lg) : 1.f;
+    m_run = need ? m_run + lg : m_run;
+    done = !have_next;
+  };
+
+  // ---- prologue: tiles 0 and 1 in flight; reference from tile 0's row max ----
   using St0 = std::integral_constant<int, 0>;
   using St1 = std::integral_constant<int, 1>;
   using St2 = std::integral_constant<int, 2>;
+  using St3 = std::integral_constant<int, 3>;
   if (nt > 0) issue_tile(0, St0{});
   if (nt > 1) issue_tile(1, St1{});
   wait_own_loads();
   __syncthreads();
   if (!done && tile_skip(St0{})) done = true;
   if (!done) {
-    qk(St0{}, sc);
-    prepare(0, St0{}, sc);
+    qk(St0{}, sA);
+    mask(0, St0{}, sA);
+    m_run = rowmax(sA);
   }
+  static_assert(TAU == 8.f, "phase2 compares against 2^TAU");
 
-  // ---- main loop; tile t lives in stage t % 3 (compile-time per unrolled step) ----
-  auto step = [&](auto stage_c, int t) {
+  // ---- main loop: step t = 0 .. nt (step nt only finishes the second group's
+  // last P V). Tile t lives in stage t % 4; its scores are in sA (t even) or sB.
+  auto step = [&](auto stage_c, int t) INLINE {
     constexpr int S = decltype(stage_c)::value;
     using SC = std::integral_constant<int, S>;
     using SN = std::integral_constant<int, (S + 1) % NSTAGE>;
+    using SP = std::integral_constant<int, (S + NSTAGE - 1) % NSTAGE>;
     using SL = std::integral_constant<int, (S + 2) % NSTAGE>;
+    f32x16 *cur = (S & 1) == 0 ? sA : sB;
+    f32x16 *nxt = (S & 1) == 0 ? sB : sA;
     wait_own_loads();  // this wave's part of tile t+1 has landed ...
-    __syncthreads();   // ... and everyone's; every wave is done with tile t-1
+    __syncthreads();   // ... and everyone's; every wave is done with tile t-2
     if (t + 2 < nt) issue_tile(t + 2, SL{});
-    if (!done) {
-      const bool have_next = t + 1 < nt && !tile_skip(SN{});
-      f32x16 sn[2];
-      bf16x8 pb[4];
-      qk(SN{}, sn);        // scores of tile t+1 (unused if !have_next)
-      softmax(sc, pb);     // probabilities of tile t
-      pv(SC{}, pb);
-      if (have_next) {
-        prepare(t + 1, SN{}, sn);
-        sc[0] = sn[0];
-        sc[1] = sn[1];
-      } else {
-        done = true;
-      }
+    if (grp_b && pend) {
+      phase2(t - 1, SP{}, SC{}, cur);  // scores of tile t are in `cur`
+      pend = false;
+    }
+    if (!done && t < nt) {
+      phase1(t, SN{}, cur, nxt);
+      if (grp_b)
+        pend = true;
+      else
+        phase2(t, SC{}, SN{}, nxt);
     }
   };
-  for (int t = 0; t < nt; t += NSTAGE) {
+  for (int t = 0; t <= nt; t += NSTAGE) {
     step(St0{}, t);
-    if (t + 1 < nt) step(St1{}, t + 1);
-    if (t + 2 < nt) step(St2{}, t + 2);
+    if (t + 1 <= nt) step(St1{}, t + 1);
+    if (t + 2 <= nt) step(St2{}, t + 2);
+    if (t + 3 <= nt) step(St3{}, t + 3);
   }
+  apply_rescale();
 
-  // ---- epilogue: o_b = acc / l, lse_b = (m + log2 l) ln 2; optional merge ----
-  const float l_tot = l_run + swap_halves(l_run);
+  // ---- epilogue: o_b = acc / l^, lse_b = (ref + log2 l) ln 2; optional merge ----
+  const float l_tot = pair_sum(l_run);
+  const float lh_tot = pair_sum(lh_run);
   if (!tok_ok) return;
   const float lse_new = l_tot > 0.f ? (m_run + __log2f(l_tot)) * LN2 : -INFINITY;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f && lh_tot > 0.f ? 1.f / lh_tot : 0.f;
   const int64_t row = (bi * a.s_q + tok) * a.n_q + h;
   float w_old = 0.f, w_new = inv, lse_out = lse_new;
   if (a.merge) {
@@ -409,6 +538,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
       w_new = __expf(lse_new - lse_out) * inv;
     }
   }
+  // Accumulator element e4*4 + j of block db holds d = db*32 + e4*8 + hi*4 + j.
   float *orow = a.o + row * D + hi * 4;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -432,25 +562,30 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   if (hi == 0) a.lse[row] = lse_out;
 }
 
-template <int HW>
+template <int HW, bool VT>
 hipError_t launch_hw(const AttnArgs &a, hipStream_t stream) {
   constexpr int TB = WAVES / HW;
   const int64_t ntb = (a.s_q + TB * QW - 1) / (TB * QW);
   const int64_t blocks = ntb * a.b * a.n_kv * ((a.n_q / a.n_kv) / HW);
   if (blocks == 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  attn_bf16_kernel<HW><<<static_cast<unsigned>(blocks), THREADS, 0, stream>>>(a);
+  attn_bf16_kernel<HW, VT><<<static_cast<unsigned>(blocks), THREADS, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <bool VT>
+hipError_t launch_vt(const AttnArgs &a, hipStream_t stream) {
+  const int g = a.n_q / a.n_kv;
+  if (g % 8 == 0) return launch_hw<8, VT>(a, stream);
+  if (g % 4 == 0) return launch_hw<4, VT>(a, stream);
+  if (g % 2 == 0) return launch_hw<2, VT>(a, stream);
+  return launch_hw<1, VT>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t stream) {
-  const int g = a.n_q / a.n_kv;
-  if (g % 8 == 0) return launch_hw<8>(a, stream);
-  if (g % 4 == 0) return launch_hw<4>(a, stream);
-  if (g % 2 == 0) return launch_hw<2>(a, stream);
-  return launch_hw<1>(a, stream);
+  return a.v_layout == RA_V_TRANSPOSED ? launch_vt<true>(a, stream) : launch_vt<false>(a, stream);
 }
 
 }  // namespace ra

@@ -30,6 +30,7 @@ struct AttnArgs {
   float scale;   // softmax scale (natural units), > 0
   int32_t causal;
   int32_t merge;
+  int32_t v_layout;  // ra_v_layout of v (RA_V_TRANSPOSED: [b, n_kv, d, s_kv], bf16 only)
 };
 
 // Records a failure message for ra_last_error() and returns the status.
@@ -49,6 +50,9 @@ hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_lse_merge(int64_t rows, int32_t d, float *o, float *lse, const float *o_b,
                             const float *lse_b, hipStream_t stream);
 hipError_t launch_positions(int32_t kind, int64_t S, int32_t N, int32_t *pos, hipStream_t stream);
+// v [b, s, n_kv, d] -> vt [b, n_kv, d, s]; esize = 2 or 4 bytes per element.
+hipError_t launch_v_transpose(int32_t b, int64_t s, int32_t n_kv, int32_t d, int32_t esize,
+                              const void *v, void *vt, hipStream_t stream);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -10,10 +10,13 @@
 // events against the compute stream:
 //   copy(r+1 -> buf[(r+1)&1]) waits for step r-1 (the last reader of that half)
 //   step r waits for copy(r -> buf[r&1]).
-// Step 0 reads the rank's own chunk in place and writes (o, lse) directly
-// (merging into the identity (0, -inf) is a no-op). Later steps merge in the
-// attention kernel's epilogue, or, with RA_RING_UNFUSED_MERGE, write
-// (o_b, lse_b) to the workspace and run the standalone merge kernel.
+// For bf16 (with c % 8 == 0) the copy of V is a transpose into the V^T
+// layout the attention kernel reads fastest, and the rank's own V chunk is
+// transposed into buffer half 0 before step 0 as well; K of step 0 is read in
+// place. Step 0 writes (o, lse) directly (merging into the identity
+// (0, -inf) is a no-op). Later steps merge in the attention kernel's
+// epilogue, or, with RA_RING_UNFUSED_MERGE, write (o_b, lse_b) to the
+// workspace and run the standalone merge kernel.
 #include <climits>
 #include <cmath>
 #include <unordered_map>
@@ -51,6 +54,7 @@ struct Plan {
   size_t chunk_bytes = 0;   // one K (or V) chunk [b, c, n_kv, d]
   size_t pos_off = 0, kv_off[2] = {0, 0}, ob_off = 0, lseb_off = 0, total = 0;
   bool fused = true, serialize = false;
+  bool vt = false;          // V chunks staged transposed (bf16, c % 8 == 0)
 };
 
 ra_status make_plan(const ra_ring_desc *r, Plan *p) {
@@ -86,10 +90,12 @@ ra_status make_plan(const ra_ring_desc *r, Plan *p) {
   p->chunk_bytes = static_cast<size_t>(r->b) * p->c * r->n_kv * r->d * p->esize;
   p->fused = !(r->flags & RA_RING_UNFUSED_MERGE);
   p->serialize = (r->flags & RA_RING_SERIALIZE) != 0;
+  p->vt = r->dtype == RA_BF16 && p->c % 8 == 0 && p->c > 0 &&
+          static_cast<int64_t>(r->b) * r->n_kv <= 65535;
   size_t off = 0;
   p->pos_off = off;
   off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
-  if (r->N > 1) {
+  if (r->N > 1 || p->vt) {
     for (int i = 0; i < 2; ++i) {
       p->kv_off[i] = off;
       off += 2 * align_up(p->chunk_bytes);
@@ -191,7 +197,7 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
   }
 
   ra::RingEvents *ev = nullptr;
-  if (!serialize && r->N > 1) {
+  if (!serialize && (r->N > 1 || P.vt)) {
     st = ra::ring_events(&ev);
     if (st != RA_OK) return st;
   }
@@ -231,39 +237,53 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
   a.causal = r->causal;
   a.q_pos = pos + static_cast<int64_t>(rank) * P.c;
 
+  // Fill buffer half (step & 1) with the chunk of `step` (K copied, V copied
+  // or transposed); step 0 needs only its V, and only when transposing.
+  hipStream_t cs = serialize ? sc : sp;
+  auto uses_buf = [&](int step) { return step >= 1 || P.vt; };
+  auto fill = [&](int step) -> ra_status {
+    const int src = ((rank - step) % N + N) % N;
+    const int buf = step & 1;
+    ra_status s2 = RA_OK;
+    if (!serialize && step >= 2 && uses_buf(step - 2))
+      s2 = hip_check(hipStreamWaitEvent(sp, ev->freed[buf], 0), "ra_ring_fwd: wait freed");
+    if (s2 == RA_OK && step >= 1)
+      s2 = hip_check(hipMemcpyAsync(kbuf[buf], kc + static_cast<size_t>(src) * CB, CB,
+                                    hipMemcpyDeviceToDevice, cs),
+                     "ra_ring_fwd: K copy");
+    if (s2 == RA_OK) {
+      if (P.vt)
+        s2 = hip_check(ra::launch_v_transpose(r->b, P.c, r->n_kv, r->d, 2,
+                                              vc + static_cast<size_t>(src) * CB, vbuf[buf], cs),
+                       "ra_ring_fwd: V transpose");
+      else
+        s2 = hip_check(hipMemcpyAsync(vbuf[buf], vc + static_cast<size_t>(src) * CB, CB,
+                                      hipMemcpyDeviceToDevice, cs),
+                       "ra_ring_fwd: V copy");
+    }
+    if (s2 == RA_OK && !serialize)
+      s2 = hip_check(hipEventRecord(ev->ready[buf], sp), "ra_ring_fwd: record ready");
+    return s2;
+  };
+  if (P.vt) {
+    st = fill(0);
+    if (st != RA_OK) return st;
+  }
+  a.v_layout = P.vt ? RA_V_TRANSPOSED : RA_V_ROWS;
+
   for (int step = 0; step < N; ++step) {
     const int src = ((rank - step) % N + N) % N;
     if (step + 1 < N) {
       // Prefetch the next step's chunk into the idle half of the double buffer.
-      const int nsrc = ((rank - step - 1) % N + N) % N;
-      const int buf = (step + 1) & 1;
-      hipStream_t cs = serialize ? sc : sp;
-      if (!serialize && step >= 2) {
-        st = hip_check(hipStreamWaitEvent(sp, ev->freed[buf], 0), "ra_ring_fwd: wait freed");
-        if (st != RA_OK) return st;
-      }
-      st = hip_check(hipMemcpyAsync(kbuf[buf], kc + static_cast<size_t>(nsrc) * CB, CB,
-                                    hipMemcpyDeviceToDevice, cs),
-                     "ra_ring_fwd: K copy");
-      if (st == RA_OK)
-        st = hip_check(hipMemcpyAsync(vbuf[buf], vc + static_cast<size_t>(nsrc) * CB, CB,
-                                      hipMemcpyDeviceToDevice, cs),
-                       "ra_ring_fwd: V copy");
-      if (st == RA_OK && !serialize)
-        st = hip_check(hipEventRecord(ev->ready[buf], sp), "ra_ring_fwd: record ready");
+      st = fill(step + 1);
       if (st != RA_OK) return st;
     }
-    if (step >= 1 && !serialize) {
+    if (uses_buf(step) && !serialize) {
       st = hip_check(hipStreamWaitEvent(sc, ev->ready[step & 1], 0), "ra_ring_fwd: wait ready");
       if (st != RA_OK) return st;
     }
-    if (step == 0) {
-      a.k = kc + static_cast<size_t>(rank) * CB;
-      a.v = vc + static_cast<size_t>(rank) * CB;
-    } else {
-      a.k = kbuf[step & 1];
-      a.v = vbuf[step & 1];
-    }
+    a.k = step == 0 ? kc + static_cast<size_t>(rank) * CB : kbuf[step & 1];
+    a.v = uses_buf(step) ? vbuf[step & 1] : vc + static_cast<size_t>(rank) * CB;
     a.kv_pos = pos + static_cast<int64_t>(src) * P.c;
     const bool unfused_merge = !P.fused && step > 0;
     a.o = unfused_merge ? o_b : o;
@@ -278,7 +298,7 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
                      "ra_ring_fwd: merge launch");
       if (st != RA_OK) return st;
     }
-    if (step >= 1 && !serialize) {
+    if (uses_buf(step) && !serialize) {
       st = hip_check(hipEventRecord(ev->freed[step & 1], sc), "ra_ring_fwd: record freed");
       if (st != RA_OK) return st;
     }

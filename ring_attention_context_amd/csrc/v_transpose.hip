@@ -1,0 +1,86 @@
+// ra_v_transpose: v [b, s, n_kv, d] -> vt [b, n_kv, d, s].
+//
+// Data movement only. The bf16 attention kernel reads V^T tiles (d-rows of
+// keys) with plain 16-byte LDS reads; the ring produces that layout for each
+// incoming chunk on its copy stream. HBM-bound: each element is read once and
+// written once, through a 64 x 64 LDS tile so that both the reads (along d)
+// and the writes (along s) are contiguous across the wave.
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+constexpr int TS = 64;  // tile edge (tokens and channels)
+
+template <typename T>
+__global__ __launch_bounds__(256) void v_transpose_kernel(const T *__restrict__ v,
+                                                          T *__restrict__ vt, int64_t s,
+                                                          int32_t n_kv, int32_t d) {
+  // +2 elements of padding: a column read walks rows at an odd dword stride.
+  __shared__ T tile[TS][TS + 2];
+  const int tid = threadIdx.x;
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * TS;
+  const int e0 = blockIdx.y * TS;
+  const int bh = blockIdx.z;  // bi * n_kv + h
+  const int bi = bh / n_kv, h = bh - bi * n_kv;
+  const int c = tid & (TS - 1), r0 = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < TS / 4; ++i) {
+    const int r = r0 + 4 * i;
+    const int64_t si = s0 + r;
+    const int e = e0 + c;
+    T x = T(0);
+    if (si < s && e < d) x = v[((bi * s + si) * n_kv + h) * d + e];
+    tile[r][c] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TS / 4; ++i) {
+    const int r = r0 + 4 * i;  // channel within the tile
+    const int64_t si = s0 + c;
+    const int e = e0 + r;
+    if (si < s && e < d) vt[(static_cast<int64_t>(bh) * d + e) * s + si] = tile[c][r];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_v_transpose(int32_t b, int64_t s, int32_t n_kv, int32_t d, int32_t esize,
+                              const void *v, void *vt, hipStream_t stream) {
+  if (b == 0 || s == 0) return hipSuccess;
+  const int64_t gx = (s + TS - 1) / TS;
+  const int64_t gy = (d + TS - 1) / TS;
+  const int64_t gz = static_cast<int64_t>(b) * n_kv;
+  if (gx > INT32_MAX || gz > 65535) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy), static_cast<unsigned>(gz));
+  if (esize == 2)
+    v_transpose_kernel<uint16_t><<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(v),
+                                                           static_cast<uint16_t *>(vt), s, n_kv, d);
+  else
+    v_transpose_kernel<uint32_t><<<grid, 256, 0, stream>>>(static_cast<const uint32_t *>(v),
+                                                           static_cast<uint32_t *>(vt), s, n_kv, d);
+  return hipGetLastError();
+}
+
+}  // namespace ra
+
+extern "C" ra_status ra_v_transpose(int32_t b, int64_t s, int32_t n_kv, int32_t d, int32_t dtype,
+                                    const void *v, void *vt, void *stream) {
+  ra::clear_error();
+  if (b < 0 || s < 0 || n_kv < 1 || d < 1)
+    return ra::fail(RA_ERR_INVALID_ARG, "ra_v_transpose: negative size or zero heads / d");
+  if (dtype != RA_BF16 && dtype != RA_F32)
+    return ra::fail(RA_ERR_UNSUPPORTED, "ra_v_transpose: unknown dtype %d", dtype);
+  if (static_cast<int64_t>(b) * n_kv > 65535)
+    return ra::fail(RA_ERR_INVALID_ARG, "ra_v_transpose: b * n_kv > 65535");
+  if (b == 0 || s == 0) return RA_OK;
+  if (!v || !vt) return ra::fail(RA_ERR_INVALID_ARG, "ra_v_transpose: NULL v / vt");
+  const int32_t esize = dtype == RA_BF16 ? 2 : 4;
+  const uintptr_t bytes = static_cast<uintptr_t>(b) * s * n_kv * d * esize;
+  const uintptr_t pv = reinterpret_cast<uintptr_t>(v), pt = reinterpret_cast<uintptr_t>(vt);
+  if (pv < pt + bytes && pt < pv + bytes)
+    return ra::fail(RA_ERR_INVALID_ARG, "ra_v_transpose: v and vt overlap");
+  return ra::hip_check(ra::launch_v_transpose(b, s, n_kv, d, esize, v, vt,
+                                              static_cast<hipStream_t>(stream)),
+                       "ra_v_transpose launch");
+}

@@ -93,7 +93,7 @@ def test_status_strings():
 
 def _attn_desc(**kw):
     base = dict(b=1, n_q=4, n_kv=2, d=128, s_q=64, s_kv=64, dtype=ra.RA_BF16, causal=0,
-                scale=0.0, reserved=0, q_pos=None, kv_pos=None)
+                scale=0.0, v_layout=ra.RA_V_ROWS, q_pos=None, kv_pos=None)
     base.update(kw)
     return _lib.AttnDesc(**base)
 
@@ -113,7 +113,9 @@ UNALIGNED = ctypes.c_void_p(0x1004)
     (dict(scale=float("nan")), ra.RA_ERR_INVALID_ARG),
     (dict(causal=1), ra.RA_ERR_INVALID_ARG),        # causal without positions
     (dict(causal=2), ra.RA_ERR_INVALID_ARG),
-    (dict(reserved=1), ra.RA_ERR_INVALID_ARG),
+    (dict(v_layout=2), ra.RA_ERR_INVALID_ARG),      # unknown V layout
+    (dict(v_layout=1, dtype=ra.RA_F32), ra.RA_ERR_UNSUPPORTED),  # V^T is bf16 only
+    (dict(v_layout=1, s_kv=60), ra.RA_ERR_INVALID_ARG),          # V^T rows 16-byte aligned
 ])
 def test_block_attn_argument_errors(kw, code):
     lib = ra.load_library()
@@ -161,8 +163,11 @@ def test_ring_workspace_bytes():
     rows = 256 * 8
     assert ra.ra_ring_workspace_bytes(unfused) == (ra.ra_ring_workspace_bytes(desc)
                                                    + align(rows * 128 * 4) + align(rows * 4))
-    # N = 1 (one dense pass): no double buffer
-    assert ra.ra_ring_workspace_bytes(_ring(N=1, rank=0)) == align(1024 * 4)
+    # N = 1 (one dense pass): bf16 still stages the transposed V chunk
+    one_chunk = 1 * 1024 * 2 * 128 * 2
+    assert ra.ra_ring_workspace_bytes(_ring(N=1, rank=0)) == align(1024 * 4) + 2 * 2 * align(one_chunk)
+    # ... float32 reads K and V in place: no double buffer
+    assert ra.ra_ring_workspace_bytes(_ring(N=1, rank=0, dtype=ra.RA_F32)) == align(1024 * 4)
 
 
 @pytest.mark.parametrize("kw", [
@@ -183,6 +188,20 @@ def test_ring_small_workspace_rejected_before_enqueue():
     assert st == ra.RA_ERR_INVALID_ARG and "workspace" in ra.ra_last_error()
     st = lib.ra_ring_fwd(ctypes.byref(desc), FAKE, FAKE, None, FAKE, FAKE, FAKE, need, None, None)
     assert st == ra.RA_ERR_INVALID_ARG
+
+
+def test_v_transpose_argument_errors():
+    lib = ra.load_library()
+    ok_args = (1, 64, 2, 128)
+    assert lib.ra_v_transpose(*ok_args, 7, FAKE, ctypes.c_void_p(0x100000), None) == ra.RA_ERR_UNSUPPORTED
+    assert lib.ra_v_transpose(-1, 64, 2, 128, ra.RA_BF16, FAKE, FAKE, None) == ra.RA_ERR_INVALID_ARG
+    assert lib.ra_v_transpose(1, 64, 0, 128, ra.RA_BF16, FAKE, FAKE, None) == ra.RA_ERR_INVALID_ARG
+    assert lib.ra_v_transpose(*ok_args, ra.RA_BF16, None, FAKE, None) == ra.RA_ERR_INVALID_ARG
+    # overlapping source and destination
+    assert lib.ra_v_transpose(*ok_args, ra.RA_BF16, FAKE, ctypes.c_void_p(0x1010), None) == ra.RA_ERR_INVALID_ARG
+    assert lib.ra_v_transpose(300, 64, 256, 128, ra.RA_BF16, FAKE, FAKE, None) == ra.RA_ERR_INVALID_ARG
+    # nothing to move: OK without pointers or a GPU
+    assert lib.ra_v_transpose(1, 0, 2, 128, ra.RA_BF16, None, None, None) == ra.RA_OK
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -83,6 +83,26 @@ def test_small_ring_matches_oracle(case):
     compare(o, lse, ro, rl, dtype, str(case))
 
 
+@pytest.mark.parametrize("case", [("zigzag", 80, 4, 1), ("contiguous", 200, 2, 1),
+                                  ("striped", 36, 3, 2), ("zigzag", 4 * 2 * 7, 4, 3)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_small_ring_rows_layout_fallback(case):
+    """bf16 rings whose chunk length c is not a multiple of 8 keep V row-major
+    (plain copies, transposing LDS reads) instead of the transposed staging."""
+    kind, S, N, rank = case
+    print(f"ring fallback {case}", flush=True)
+    w = synth.Workload("odd_c", 1, S, N, kind, 8, 2, 128, "bf16", 1.0, True, seed=S + N,
+                       rank=rank)
+    assert w.c % 8 != 0
+    inp = synth.draw(w)
+    q, kc, vc = device_inputs(w, inp)
+    _, o, lse = run_ring(w, q, kc, vc)
+    ro, rl = oatt.naive_attention(inp.q64, inp.k64, inp.v64,
+                                  opart.partition_map(kind, S, N, rank), np.arange(S), True,
+                                  w.scale)
+    compare(o, lse, ro, rl, "bf16", str(case))
+
+
 def _flag_case(dtype="bf16"):
     w = synth.Workload("flags", 1, 4096, 4, "zigzag", 8, 1, 128, dtype, 1.0, True, seed=77,
                        rank=1)
