@@ -34,8 +34,8 @@
 //     row swapped) so that each lane's probabilities are 8 consecutive keys,
 //     the k-slots of one 16-byte V^T read;
 //   * each tile runs in two phases: phase 1 issues the score MFMAs of tile
-//     t+1 and the exponentials of tile t; phase 2 issues the P V MFMAs of tile
-//     t. Waves w and w+4 share a SIMD; the second group runs the two phases
+//     t+1 interleaved, k-step by k-step, with the exponentials of tile t;
+//     phase 2 issues the P V MFMAs of tile t. Waves w and w+4 share a SIMD; the second group runs the two phases
 //     in the opposite order (P V of tile t-1 first), so the pair overlaps one
 //     wave's exponentials with the other's MFMAs. The fourth LDS stage keeps
 //     tile t-1 resident for that group while tile t+2 streams in;
@@ -402,6 +402,55 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     lht = lh[0] + lh[1];
   };
 
+  // Phase-1 body: the score MFMAs of the next tile interleaved with the
+  // probabilities of the current one, one k-step at a time behind hard
+  // scheduling fences (left to itself the compiler clusters the MFMAs and the
+  // VALU work apart). Each k-step issues the K reads two steps ahead, the two
+  // score MFMAs, then a quarter of one key block's probabilities (4 per
+  // lane), which the VALU works through while the MFMAs run.
+  auto qk_softmax = [&](auto stage, f32x16 *s, const f32x16 *cur) INLINE {
+    const unsigned char *kb_base = k_stage(stage);
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    bf16x8 ka[3][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        ka[j][kb] = *reinterpret_cast<const bf16x8 *>(kb_base + koff[j] + kb * 32 * ROW_B);
+    float lp[4] = {0.f, 0.f, 0.f, 0.f};
+    float lh[2] = {0.f, 0.f};
+    const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      if (ds + 2 < D / 16) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          ka[(ds + 2) % 3][kb] =
+              *reinterpret_cast<const bf16x8 *>(kb_base + koff[ds + 2] + kb * 32 * ROW_B);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds % 3][kb], qreg[ds],
+                                                        ds == 0 ? f32x16{} : s[kb], 0, 0, 0);
+      // probabilities of k-slots ks = ds / 2, e = (ds % 2) * 4 .. +3
+      const int ks = ds >> 1, e0 = (ds & 1) * 4;
+      float pf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pf[j] = exp2_fast(fmaf(cur[ks >> 1][(ks & 1) * 8 + e0 + j], sl2, -m_use));
+        lp[j] += pf[j];
+        pb[ks][e0 + j] = static_cast<__bf16>(pf[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j += 2)
+        lh[j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ks][e0 + j], pb[ks][e0 + j + 1]},
+                                                     one, lh[j >> 1], false);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lt = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+    lht = lh[0] + lh[1];
+  };
+
   // O^T += V^T P^T with the V tile in `stage`.
   auto pv = [&](auto stage) INLINE {
     const unsigned char *vb = v_stage(stage);
@@ -428,16 +477,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   auto phase1 = [&](int t, auto sn, const f32x16 *cur, f32x16 *nxt) INLINE {
     apply_rescale();
     have_next = t + 1 < nt && !tile_skip(sn);
-    qk(sn, nxt);
-    softmax(cur);
-    // Keep the probabilities in this block: otherwise the compiler sinks the
-    // exponentials past the mask branch, next to their use in P V, and the
-    // score MFMAs above lose the work they overlap with.
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 pin = pb[ks];
-      asm volatile("" ::"v"(pin));
-    }
+    qk_softmax(sn, nxt, cur);
     const float lt_row = pair_sum(lt);
     if (__any((m_run == -INFINITY) | !(lt_row <= 0x1p32f))) {
       // No reference yet, or a score far above it: redo the tile against its
