@@ -26,10 +26,13 @@ Modules:
   (secondary, block-then-merge oracle), and the ring schedule.
 * :mod:`oracle.partition` -- contiguous / zig-zag / striped token maps,
   visible-pair counts, tile classification and ring efficiency.
+* :mod:`oracle.backward` -- the gradients of softmax attention (plain
+  definition by the chain rule), one block's contributions with the global
+  lse (§3 backward paragraph), and the ring backward (§4).
 
-Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+Parity status: every function here is pinned by ``tests/test_oracle*.py``
 against closed forms, brute force, a library special case or numbers the
 pages print. No function is "parity unpinned".
 """
 
-from . import attention, partition  # noqa: F401
+from . import attention, backward, partition  # noqa: F401
