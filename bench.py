@@ -11,6 +11,11 @@ Metric: causal-adjusted TFLOP/s = 4 * b * n_q * d * (visible query/key pairs)
 / time, and its fraction of the MI355X dense bf16 MFMA peak (2516.6 TFLOP/s =
 256 CU x 4096 flop/clk x 2.4 GHz).
 
+With --backward the step is one ``ra_ring_bwd`` call instead (the ring
+backward: dQ of the rank and its contributions to every block's dK, dV), and
+the metric counts 10 * b * n_q * d flop per visible pair (the five matmuls of
+the attention backward, 2.5x the forward).
+
 Prints progress on stderr and ONE JSON line on stdout.
 """
 
@@ -28,6 +33,8 @@ PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "causal-adjusted attention TFLOP/s per rank shard + % of bf16 MFMA peak"
+METRIC_BWD = ("causal-adjusted attention backward TFLOP/s per rank shard (10*d flop per visible "
+              "pair and head) + % of bf16 MFMA peak")
 
 
 def log(msg):
@@ -99,6 +106,120 @@ def cpu_baseline(w, seconds_hint=15.0):
             "sample": f"{len(rows)} of {w.c} query rows x {w.n_q} heads vs all {w.S} keys "
                       f"(fp64 NumPy naive softmax, {t:.1f} s, {pairs} visible pairs)",
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline_bwd(w, seconds_hint=15.0):
+    """Time the fp64 backward oracle (as it stands) on a bounded sample: a few
+    query rows x all heads against the full sequence (their dq and their
+    contributions to every key's dk, dv)."""
+    import numpy as np
+    import synth
+    from oracle import backward as obwd
+    from oracle import partition as opart
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    per_row = 10 * w.d * w.n_q * (w.S / 2.0 if w.causal else w.S)
+    rows_n = int(max(4, min(256, seconds_hint * 1.0e10 / per_row)))
+    rows = synth.sample_rows(w.c, rows_n, w.seed)
+    inp = synth.draw(w, q_rows=rows)
+    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)[rows]
+    rng = np.random.default_rng(w.seed + 1000)
+    do = rng.standard_normal(inp.q64.shape)
+    t0 = time.perf_counter()
+    obwd.naive_attention_bwd(inp.q64, inp.k64, inp.v64, do, q_pos, np.arange(w.S), w.causal,
+                             w.scale)
+    t = time.perf_counter() - t0
+    pairs = opart.visible_pairs(q_pos, np.arange(w.S), w.causal)
+    flops = 10 * w.b * w.n_q * w.d * pairs
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {w.c} query rows x {w.n_q} heads vs all {w.S} keys "
+                      f"(fp64 NumPy backward by the chain rule, {t:.1f} s, {pairs} visible pairs)",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def run_backward(args, w, q, kc, vc, dev, props):
+    """Time ra_ring_bwd (one rank's ring backward) and print its JSON line."""
+    import numpy as np
+    import torch
+    import synth
+    import ring_attention_context_amd as ra
+    from ring_attention_context_amd import runner
+    call = runner.RingCall(q, kc, vc, kind=w.kind, S=w.S, N=w.N, rank=w.rank, causal=w.causal,
+                           scale=w.scale)
+    o, lse = call()                       # the rank's global o and lse (forward, untimed)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed + 1000)
+    do = runner.host_to_device(synth.bf16_bits(rng.standard_normal(tuple(q.shape),
+                                                                   dtype=np.float32)),
+                               "bf16", dev)
+    dq = torch.empty(tuple(q.shape), dtype=torch.float32, device=dev)
+    dkc = torch.zeros(tuple(kc.shape), dtype=torch.float32, device=dev)
+    dvc = torch.zeros_like(dkc)
+    pairs = visible_pairs_per_step(w.kind, w.S, w.N, w.rank, w.causal)
+    total_flops = sum(10 * w.b * w.n_q * w.d * p for p in pairs)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(w.N + 1)]
+          for _ in range(args.steps)]
+    for e in ev:
+        for x in e:
+            x.record()
+    desc_plain, _ = ra.ring_desc(b=w.b, n_q=w.n_q, n_kv=w.n_kv, d=w.d, dtype=ra.RA_BF16,
+                                 causal=w.causal, kind=w.kind, S=w.S, N=w.N, rank=w.rank,
+                                 scale=w.scale)
+    ws = torch.empty(ra.ra_ring_bwd_workspace_bytes(desc_plain), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        ra.ra_ring_bwd(desc_plain, q, kc, vc, o, lse, do, dq, dkc, dvc, ws, stream)
+    torch.cuda.synchronize()
+    log(f"[bench-bwd] warmup {args.warmup} done")
+    keep = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        desc, k = ra.ring_desc(b=w.b, n_q=w.n_q, n_kv=w.n_kv, d=w.d, dtype=ra.RA_BF16,
+                               causal=w.causal, kind=w.kind, S=w.S, N=w.N, rank=w.rank,
+                               scale=w.scale, step_events=ev[i])
+        keep.append(k)
+        ra.ra_ring_bwd(desc, q, kc, vc, o, lse, do, dq, dkc, dvc, ws, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    step_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(w.N)] for e in ev])
+    kern_ms = float(step_ms.sum())
+    achieved = args.steps * total_flops / (kern_ms * 1e-3) / 1e12
+    log(f"[bench-bwd] {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s; "
+        f"per-step ms {np.round(np.median(step_ms, axis=0), 3).tolist()}")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(w, args.cpu_seconds)
+    out = {
+        "metric": METRIC_BWD,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), bf16 round-to-nearest-even)",
+        "config": {"workload": w.name, "pass": "backward", "b": w.b, "S": w.S, "N": w.N,
+                   "rank": w.rank, "map": w.kind, "n_q": w.n_q, "n_kv": w.n_kv, "d": w.d,
+                   "causal": w.causal, "scale": w.scale, "queries_per_rank": w.c,
+                   "visible_pairs": sum(pairs)},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "bwd_dq_kernel + bwd_dkdv_kernel per step",
+                     "avg_launch_ms": round(kern_ms / step_ms.size, 4),
+                     "launches": int(step_ms.size),
+                     "flops_per_launch_avg": total_flops / w.N},
+        "cpu_baseline": cpu,
+        "device": props.name,
+    }
+    print(json.dumps(out), flush=True)
 
 
 def time_ring(w, q, kc, vc, warmup, steps, flags=0):
@@ -193,6 +314,8 @@ def main():
     ap.add_argument("--sweep", default=None,
                     help="write a JSON file with every workload and the per-rank map "
                          "imbalance study (no contract line)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the ring backward (ra_ring_bwd) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size "
                          "reference for HBM byte counters)")
@@ -240,6 +363,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("[bench] calibration copy: 268435456 bytes read + 268435456 bytes written")
+
+    if args.backward:
+        run_backward(args, w, q, kc, vc, dev, props)
+        return
 
     compute = torch.cuda.Stream(dev)
     copy = torch.cuda.Stream(dev)

@@ -190,6 +190,64 @@ ra_status ra_ring_fwd(const ra_ring_desc *desc, const void *q, const void *k_chu
                       const void *v_chunks, float *o, float *lse, void *workspace,
                       size_t workspace_bytes, void *compute, void *copy);
 
+/*
+ * Backward ("Context Parallelism and Ring Attention" §3, backward paragraph;
+ * §4 for the ring). With the GLOBAL lse of a query (the forward's output) the
+ * probability of key j is p_j = e^{x_j - lse} on any block; with
+ * D = dout . o per query:
+ *   dv_j += p_j dout,  dx_j = p_j (dout . v_j - D),
+ *   dq += scale sum_j dx_j k_j,  dk_j += scale sum_q dx_j q   (x = scale q.k).
+ * The causal rule is the forward's.
+ */
+
+/*
+ * ra_attn_bwd_delta -- delta[r] = sum_e dout[r, e] * o[r, e] (the scalar D).
+ * rows = b * s * n_q; dout: device [rows, d] of dtype (RA_BF16 or RA_F32);
+ * o: device float32 [rows, d]; delta: device float32 [rows]. d in {64, 128}.
+ */
+ra_status ra_attn_bwd_delta(int64_t rows, int32_t d, int32_t dtype, const void *dout,
+                            const float *o, float *delta, void *stream);
+
+/*
+ * ra_block_attn_bwd -- one key block's gradient contributions, ADDED into
+ * dq, dk and dv (callers accumulate blocks; zero them first for one block).
+ * desc: as for ra_block_attn_fwd (bf16, d = 128, v_layout RA_V_ROWS only;
+ * others are RA_ERR_UNSUPPORTED). q, dout: device [b, s_q, n_q, d] bf16;
+ * k, v: device [b, s_kv, n_kv, d] bf16; lse: device float32 [b, s_q, n_q],
+ * the query's global lse (natural log; -inf for a query with no visible key
+ * anywhere); delta: device float32 [b, s_q, n_q] from ra_attn_bwd_delta;
+ * dq: device float32 [b, s_q, n_q, d]; dk, dv: device float32
+ * [b, s_kv, n_kv, d] (a key/value head collects every query head of its
+ * group). Two kernels run in order on `stream`.
+ */
+ra_status ra_block_attn_bwd(const ra_attn_desc *desc, const void *q, const void *k,
+                            const void *v, const void *dout, const float *lse,
+                            const float *delta, float *dq, float *dk, float *dv, void *stream);
+
+/* Workspace bytes ra_ring_bwd needs: positions (S int32) and D (b*c*n_q floats). */
+ra_status ra_ring_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
+
+/*
+ * ra_ring_bwd -- the ring backward for rank `rank`, replayed on one GPU.
+ * desc: as for ra_ring_fwd (bf16, d = 128; flags 0 or RA_RING_SERIALIZE,
+ * which changes nothing here: one stream).
+ * q, dout: device [b, c, n_q, d] bf16, the rank's tokens in its local order;
+ * o, lse: device float32 [b, c, n_q, d] and [b, c, n_q], the rank's forward
+ * outputs (global o and lse); k_chunks, v_chunks: device [N, b, c, n_kv, d]
+ * bf16 as for ra_ring_fwd.
+ * dq: device float32 [b, c, n_q, d], overwritten with the rank's dQ.
+ * dk_chunks, dv_chunks: device float32 [N, b, c, n_kv, d]; this rank's
+ * contribution to block j's dK, dV is ADDED to slot j. These slots stand for
+ * the gradient buffers that travel the ring with each block: calling every
+ * rank on the same slots sums the sequence's dK, dV.
+ * Step r works on block (rank - r) mod N, read in place; N+1 step events
+ * (optional) are recorded before step 0 and after each step.
+ */
+ra_status ra_ring_bwd(const ra_ring_desc *desc, const void *q, const void *k_chunks,
+                      const void *v_chunks, const float *o, const float *lse, const void *dout,
+                      float *dq, float *dk_chunks, float *dv_chunks, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* Static text of a status code. */
 const char *ra_status_str(int32_t status);
 

@@ -25,10 +25,14 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     RingAttnError,
     load_library,
+    ra_attn_bwd_delta,
+    ra_block_attn_bwd,
     ra_block_attn_fwd,
     ra_last_error,
     ra_lse_merge,
     ra_partition,
+    ra_ring_bwd,
+    ra_ring_bwd_workspace_bytes,
     ra_ring_fwd,
     ra_ring_workspace_bytes,
     ra_status_str,

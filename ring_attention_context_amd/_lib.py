@@ -23,7 +23,8 @@ RA_V_ROWS, RA_V_TRANSPOSED = 0, 1
 KINDS = {"contiguous": RA_PART_CONTIGUOUS, "zigzag": RA_PART_ZIGZAG, "striped": RA_PART_STRIPED}
 
 EXPORTED = ("ra_partition", "ra_block_attn_fwd", "ra_v_transpose", "ra_lse_merge",
-            "ra_ring_workspace_bytes", "ra_ring_fwd", "ra_status_str", "ra_last_error")
+            "ra_ring_workspace_bytes", "ra_ring_fwd", "ra_attn_bwd_delta", "ra_block_attn_bwd",
+            "ra_ring_bwd_workspace_bytes", "ra_ring_bwd", "ra_status_str", "ra_last_error")
 
 
 class RingAttnError(RuntimeError):
@@ -69,8 +70,16 @@ def load_library(path=None):
     lib.ra_ring_workspace_bytes.argtypes = [ctypes.POINTER(RingDesc), ctypes.POINTER(ctypes.c_size_t)]
     lib.ra_ring_fwd.argtypes = [ctypes.POINTER(RingDesc), vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                 vp, vp]
+    lib.ra_attn_bwd_delta.argtypes = [i64, i32, i32, vp, vp, vp, vp]
+    lib.ra_block_attn_bwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp]
+    lib.ra_ring_bwd_workspace_bytes.argtypes = [ctypes.POINTER(RingDesc),
+                                                ctypes.POINTER(ctypes.c_size_t)]
+    lib.ra_ring_bwd.argtypes = [ctypes.POINTER(RingDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                ctypes.c_size_t, vp]
     for name in ("ra_partition", "ra_block_attn_fwd", "ra_v_transpose", "ra_lse_merge",
-                 "ra_ring_workspace_bytes", "ra_ring_fwd"):
+                 "ra_ring_workspace_bytes", "ra_ring_fwd", "ra_attn_bwd_delta",
+                 "ra_block_attn_bwd", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd"):
         getattr(lib, name).restype = i32
     lib.ra_status_str.argtypes = [i32]
     lib.ra_status_str.restype = ctypes.c_char_p
@@ -172,6 +181,29 @@ def ra_lse_merge(o, lse, o_b, lse_b, stream=None):
                                        _stream(stream)))
 
 
+def ra_attn_bwd_delta(dout, o, delta, stream=None):
+    """delta [..] <- sum over the last axis of dout * o (dout bf16 or f32, o f32)."""
+    _need_contiguous(dout, o, delta)
+    d = o.shape[-1]
+    _check(load_library().ra_attn_bwd_delta(delta.numel(), d, _dtype_code(dout), _ptr(dout),
+                                            _ptr(o), _ptr(delta), _stream(stream)))
+
+
+def ra_block_attn_bwd(q, k, v, dout, lse, delta, dq, dk, dv, *, causal, scale=0.0, q_pos=None,
+                      kv_pos=None, stream=None):
+    """dq, dk, dv (float32) += the gradient contributions of key block (k, v)
+    for queries q with upstream gradient dout, global lse and delta = dout . o."""
+    _need_contiguous(q, k, v, dout, lse, delta, dq, dk, dv, q_pos, kv_pos)
+    desc = AttnDesc(b=q.shape[0], n_q=q.shape[2], n_kv=k.shape[2], d=q.shape[3],
+                    s_q=q.shape[1], s_kv=k.shape[1], dtype=_dtype_code(q), causal=int(causal),
+                    scale=scale, v_layout=RA_V_ROWS,
+                    q_pos=None if q_pos is None else q_pos.data_ptr(),
+                    kv_pos=None if kv_pos is None else kv_pos.data_ptr())
+    _check(load_library().ra_block_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
+                                            _ptr(dk), _ptr(dv), _stream(stream)))
+
+
 def ring_desc(*, b, n_q, n_kv, d, dtype, causal, kind, S, N, rank, scale=0.0, flags=0,
               step_events=None):
     """Build the C ring descriptor. ``step_events``: list of N + 1 torch.cuda.Event
@@ -199,3 +231,20 @@ def ra_ring_fwd(desc, q, k_chunks, v_chunks, o, lse, workspace, compute=None, co
     _check(load_library().ra_ring_fwd(ctypes.byref(desc), _ptr(q), _ptr(k_chunks),
                                       _ptr(v_chunks), _ptr(o), _ptr(lse), _ptr(workspace),
                                       ws_bytes, _stream(compute), _stream(copy)))
+
+
+def ra_ring_bwd_workspace_bytes(desc):
+    out = ctypes.c_size_t(0)
+    _check(load_library().ra_ring_bwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
+
+
+def ra_ring_bwd(desc, q, k_chunks, v_chunks, o, lse, dout, dq, dk_chunks, dv_chunks, workspace,
+                stream=None):
+    """Ring backward of one rank; see ringattn.h. dk_chunks / dv_chunks are added to."""
+    _need_contiguous(q, k_chunks, v_chunks, o, lse, dout, dq, dk_chunks, dv_chunks, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().ra_ring_bwd(ctypes.byref(desc), _ptr(q), _ptr(k_chunks),
+                                      _ptr(v_chunks), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                      _ptr(dk_chunks), _ptr(dv_chunks), _ptr(workspace),
+                                      ws_bytes, _stream(stream)))

@@ -33,6 +33,32 @@ struct AttnArgs {
   int32_t v_layout;  // ra_v_layout of v (RA_V_TRANSPOSED: [b, n_kv, d, s_kv], bf16 only)
 };
 
+// Arguments of one backward launch (one key block against a query shard):
+// q, dout [b, s_q, n_q, d]; k, v [b, s_kv, n_kv, d]; lse, delta [b, s_q, n_q]
+// (the global lse of the forward and D = dout . o); dq [b, s_q, n_q, d] and
+// dk, dv [b, s_kv, n_kv, d] float32, accumulated into.
+struct BwdArgs {
+  const void *q;
+  const void *k;
+  const void *v;
+  const void *dout;
+  const float *lse;
+  const float *delta;
+  float *dq;
+  float *dk;
+  float *dv;
+  const int32_t *q_pos;
+  const int32_t *kv_pos;
+  int64_t s_q;
+  int64_t s_kv;
+  int32_t b;
+  int32_t n_q;
+  int32_t n_kv;
+  int32_t d;
+  float scale;
+  int32_t causal;
+};
+
 // Records a failure message for ra_last_error() and returns the status.
 ra_status fail(ra_status st, const char *fmt, ...);
 // Checks a HIP return code; records the HIP error text on failure.
@@ -50,6 +76,11 @@ hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_lse_merge(int64_t rows, int32_t d, float *o, float *lse, const float *o_b,
                             const float *lse_b, hipStream_t stream);
 hipError_t launch_positions(int32_t kind, int64_t S, int32_t N, int32_t *pos, hipStream_t stream);
+// D = dout . o per row (rows = b * s * n_q, d elements each; esize of dout 2 or 4).
+hipError_t launch_bwd_delta(int64_t rows, int32_t d, int32_t esize, const void *dout,
+                            const float *o, float *delta, hipStream_t stream);
+// dq, dk, dv += the gradient contributions of one key block (bf16, d = 128).
+hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 // v [b, s, n_kv, d] -> vt [b, n_kv, d, s]; esize = 2 or 4 bytes per element.
 hipError_t launch_v_transpose(int32_t b, int64_t s, int32_t n_kv, int32_t d, int32_t esize,
                               const void *v, void *vt, hipStream_t stream);

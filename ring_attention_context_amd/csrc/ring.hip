@@ -138,6 +138,20 @@ ra_status ring_events(RingEvents **out) {
 
 }  // namespace
 
+__global__ void fill_zero_kernel(float *p, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    p[i] = 0.f;
+}
+
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  fill_zero_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_positions(int32_t kind, int64_t S, int32_t N, int32_t *pos,
                             hipStream_t stream) {
   if (S == 0) return hipSuccess;
@@ -306,6 +320,139 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
       st = hip_check(hipEventRecord(step_ev[step + 1], sc), "ra_ring_fwd: step event");
       if (st != RA_OK) return st;
     }
+  }
+  return RA_OK;
+}
+
+// ---------------------------------------------------------------- backward ring
+//
+// The ring backward of "Context Parallelism and Ring Attention" §3 (backward
+// paragraph) and §4 for one rank: D = dout . o once; at step r the rank holds
+// the K/V block of rank (rank - r) mod N and adds that block's contribution
+// to its dQ and to the block's dK, dV. On a ring the accumulated dK, dV of a
+// block travel with it; here the caller's per-block output slots play that
+// role (this rank's contribution is added to whatever they hold), and the
+// blocks are read in place on one stream.
+
+namespace ra {
+namespace {
+
+struct BwdPlan {
+  int64_t c = 0;
+  size_t chunk_elems = 0;  // one K (or V) chunk [b, c, n_kv, d]
+  size_t pos_off = 0, delta_off = 0, total = 0;
+};
+
+ra_status make_bwd_plan(const ra_ring_desc *r, BwdPlan *p) {
+  if (!r) return fail(RA_ERR_INVALID_ARG, "ring bwd: desc is NULL");
+  if (r->flags & ~RA_RING_SERIALIZE)
+    return fail(RA_ERR_INVALID_ARG, "ring bwd: only RA_RING_SERIALIZE may be set (0x%x)", r->flags);
+  ra_ring_desc fwd = *r;
+  fwd.flags = 0;
+  Plan fp;
+  ra_status st = make_plan(&fwd, &fp);
+  if (st != RA_OK) return st;
+  if (r->dtype != RA_BF16 || r->d != 128)
+    return fail(RA_ERR_UNSUPPORTED, "ring bwd: bf16 with d = 128 only");
+  p->c = fp.c;
+  p->chunk_elems = static_cast<size_t>(r->b) * fp.c * r->n_kv * r->d;
+  size_t off = 0;
+  p->pos_off = off;
+  off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
+  p->delta_off = off;
+  off += align_up(static_cast<size_t>(r->b) * fp.c * r->n_q * sizeof(float));
+  p->total = off;
+  return RA_OK;
+}
+
+}  // namespace
+}  // namespace ra
+
+extern "C" ra_status ra_ring_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *bytes) {
+  ra::clear_error();
+  if (!bytes) return ra::fail(RA_ERR_INVALID_ARG, "ra_ring_bwd_workspace_bytes: bytes is NULL");
+  ra::BwdPlan p;
+  ra_status st = ra::make_bwd_plan(desc, &p);
+  if (st != RA_OK) return st;
+  *bytes = p.total;
+  return RA_OK;
+}
+
+extern "C" ra_status ra_ring_bwd(const ra_ring_desc *r, const void *q, const void *k_chunks,
+                                 const void *v_chunks, const float *o, const float *lse,
+                                 const void *dout, float *dq, float *dk_chunks, float *dv_chunks,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  using ra::fail;
+  using ra::hip_check;
+  ra::clear_error();
+  ra::BwdPlan P;
+  ra_status st = ra::make_bwd_plan(r, &P);
+  if (st != RA_OK) return st;
+  hipStream_t sc = static_cast<hipStream_t>(stream);
+  hipEvent_t *step_ev = reinterpret_cast<hipEvent_t *>(r->step_events);
+  const bool empty = r->b == 0 || P.c == 0;
+  if (empty) {
+    if (step_ev)
+      for (int i = 0; i <= r->N; ++i) {
+        st = hip_check(hipEventRecord(step_ev[i], sc), "ra_ring_bwd: step event");
+        if (st != RA_OK) return st;
+      }
+    return RA_OK;
+  }
+  if (!q || !k_chunks || !v_chunks || !o || !lse || !dout || !dq || !dk_chunks || !dv_chunks)
+    return fail(RA_ERR_INVALID_ARG, "ra_ring_bwd: NULL input or output");
+  const void *ptrs[] = {q, k_chunks, v_chunks, o, dout, dq, dk_chunks, dv_chunks};
+  for (const void *p : ptrs)
+    if (!ra::aligned16(p)) return fail(RA_ERR_INVALID_ARG, "ra_ring_bwd: pointer not 16-byte aligned");
+  if ((P.chunk_elems * 2) % 16)
+    return fail(RA_ERR_INVALID_ARG, "ra_ring_bwd: chunk size not a multiple of 16 bytes");
+  if (!workspace || !ra::aligned16(workspace))
+    return fail(RA_ERR_INVALID_ARG, "ra_ring_bwd: workspace NULL or not 16-byte aligned");
+  if (workspace_bytes < P.total)
+    return fail(RA_ERR_INVALID_ARG, "ra_ring_bwd: workspace has %zu bytes, needs %zu",
+                workspace_bytes, P.total);
+
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  int32_t *pos = reinterpret_cast<int32_t *>(ws + P.pos_off);
+  float *delta = reinterpret_cast<float *>(ws + P.delta_off);
+  const int64_t rows = static_cast<int64_t>(r->b) * P.c * r->n_q;
+  st = hip_check(ra::launch_positions(r->kind, r->S, r->N, pos, sc), "ra_ring_bwd: positions");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_bwd_delta(rows, r->d, 2, dout, o, delta, sc), "ra_ring_bwd: delta");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_fill_zero(dq, rows * r->d, sc), "ra_ring_bwd: zero dq");
+  if (st == RA_OK && step_ev) st = hip_check(hipEventRecord(step_ev[0], sc), "ra_ring_bwd: step event");
+  if (st != RA_OK) return st;
+
+  ra::BwdArgs a{};
+  a.q = q;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.s_q = P.c;
+  a.s_kv = P.c;
+  a.b = r->b;
+  a.n_q = r->n_q;
+  a.n_kv = r->n_kv;
+  a.d = r->d;
+  a.scale = r->scale > 0.f ? r->scale : 1.0f / std::sqrt(static_cast<float>(r->d));
+  a.causal = r->causal;
+  a.q_pos = pos + static_cast<int64_t>(r->rank) * P.c;
+  const unsigned char *kc = static_cast<const unsigned char *>(k_chunks);
+  const unsigned char *vc = static_cast<const unsigned char *>(v_chunks);
+  const int N = r->N;
+  for (int step = 0; step < N; ++step) {
+    const int src = ((r->rank - step) % N + N) % N;
+    a.k = kc + static_cast<size_t>(src) * P.chunk_elems * 2;
+    a.v = vc + static_cast<size_t>(src) * P.chunk_elems * 2;
+    a.kv_pos = pos + static_cast<int64_t>(src) * P.c;
+    a.dk = dk_chunks + static_cast<size_t>(src) * P.chunk_elems;
+    a.dv = dv_chunks + static_cast<size_t>(src) * P.chunk_elems;
+    st = hip_check(ra::launch_attn_bwd_bf16(a, sc), "ra_ring_bwd: backward launch");
+    if (st == RA_OK && step_ev)
+      st = hip_check(hipEventRecord(step_ev[step + 1], sc), "ra_ring_bwd: step event");
+    if (st != RA_OK) return st;
   }
   return RA_OK;
 }

@@ -207,3 +207,31 @@ def test_v_transpose_argument_errors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ra.RingAttnError):
         _lib.load_library(str(tmp_path / "nope.so"))
+
+
+def test_backward_argument_errors():
+    lib = ra.load_library()
+    # delta: d, dtype, pointers
+    assert lib.ra_attn_bwd_delta(4, 96, ra.RA_BF16, FAKE, FAKE, FAKE, None) == ra.RA_ERR_UNSUPPORTED
+    assert lib.ra_attn_bwd_delta(4, 128, 9, FAKE, FAKE, FAKE, None) == ra.RA_ERR_UNSUPPORTED
+    assert lib.ra_attn_bwd_delta(4, 128, ra.RA_BF16, None, FAKE, FAKE, None) == ra.RA_ERR_INVALID_ARG
+    assert lib.ra_attn_bwd_delta(0, 128, ra.RA_BF16, None, None, None, None) == ra.RA_OK
+    # block backward: bf16 / d = 128 / row-major V only; validation before any launch
+    for kw, code in ((dict(dtype=ra.RA_F32), ra.RA_ERR_UNSUPPORTED),
+                     (dict(v_layout=ra.RA_V_TRANSPOSED), ra.RA_ERR_UNSUPPORTED),
+                     (dict(n_q=3), ra.RA_ERR_INVALID_ARG)):
+        desc = _attn_desc(**kw)
+        st = lib.ra_block_attn_bwd(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, None)
+        assert st == code, (kw, ra.ra_last_error())
+    desc = _attn_desc()
+    assert lib.ra_block_attn_bwd(ctypes.byref(desc), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, None) == ra.RA_ERR_INVALID_ARG
+    # ring backward: same ring validation, plus bf16 only and no merge flags
+    with pytest.raises(ra.RingAttnError):
+        ra.ra_ring_bwd_workspace_bytes(_ring(dtype=ra.RA_F32))
+    with pytest.raises(ra.RingAttnError):
+        ra.ra_ring_bwd_workspace_bytes(_ring(flags=ra.RA_RING_UNFUSED_MERGE))
+    def align(x):
+        return (x + 255) // 256 * 256
+    assert ra.ra_ring_bwd_workspace_bytes(_ring()) == align(1024 * 4) + align(256 * 8 * 4)

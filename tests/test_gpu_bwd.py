@@ -1,0 +1,183 @@
+"""GPU parity of the backward path (ra_attn_bwd_delta, ra_block_attn_bwd,
+ra_ring_bwd) against the fp64 backward oracle, through the C ABI.
+
+Tolerance: the MFMAs consume P and dS rounded to bf16 (relative error 2^-9 per
+element) and accumulate in fp32, so each gradient is compared as
+max |g - g_ref| <= 1e-2 * max |g_ref| + 1e-4: about five times the
+per-element rounding, and far below what a wrong term, sign, scale or mask
+produces (tests/test_oracle_bwd.py shows those move the gradients by O(1))."""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import ring_attention_context_amd as ra
+import synth
+from gpu_util import rand_inputs, require_gpu, to_device
+from oracle import attention as oatt
+from oracle import backward as obwd
+from oracle import partition as opart
+from ring_attention_context_amd import runner
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL, TOL_ABS = 1e-2, 1e-4
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def grad_close(got, want, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert not np.isnan(got).any(), f"{what}: NaN"
+    err = float(np.max(np.abs(got - want))) if want.size else 0.0
+    scale = float(np.max(np.abs(want))) if want.size else 0.0
+    assert err <= TOL_REL * scale + TOL_ABS, f"{what}: max err {err:.3g} vs max |ref| {scale:.3g}"
+    return err, scale
+
+
+def test_delta_matches_numpy():
+    rng = np.random.default_rng(1)
+    for shape, dt in (((2, 77, 4, 128), "bf16"), ((1, 33, 3, 64), "f32"), ((1, 5, 2, 128), "f32")):
+        print(f"delta {shape} {dt}", flush=True)
+        do, do64 = rand_inputs(shape, dt, rng)
+        o = rng.standard_normal(shape).astype(np.float32)
+        tdo = to_device(do, dt)
+        to = torch.from_numpy(o).cuda()
+        delta = torch.full(shape[:-1], float("nan"), device="cuda")
+        ra.ra_attn_bwd_delta(tdo, to, delta)
+        torch.cuda.synchronize()
+        want = obwd.delta(o, do64)
+        np.testing.assert_allclose(delta.cpu().numpy(), want, rtol=1e-5, atol=1e-5)
+
+
+def run_block_bwd(host, o, lse, q_pos, kv_pos, causal, scale):
+    q, k, v, do = (to_device(x, "bf16") for x in host)
+    b, s_q, n_q, d = q.shape
+    s_kv, n_kv = k.shape[1], k.shape[2]
+    to = torch.from_numpy(np.ascontiguousarray(o, dtype=np.float32)).cuda()
+    tl = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).cuda()
+    delta = torch.empty((b, s_q, n_q), device="cuda")
+    ra.ra_attn_bwd_delta(do, to, delta)
+    dq = torch.zeros((b, s_q, n_q, d), device="cuda")
+    dk = torch.zeros((b, s_kv, n_kv, d), device="cuda")
+    dv = torch.zeros((b, s_kv, n_kv, d), device="cuda")
+    ra.ra_block_attn_bwd(q, k, v, do, tl, delta, dq, dk, dv, causal=causal, scale=scale,
+                         q_pos=torch.from_numpy(q_pos).cuda(),
+                         kv_pos=torch.from_numpy(kv_pos).cuda())
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+BWD_CASES = [
+    # b, s_q, s_kv, n_q, n_kv, causal, score multiplier
+    (1, 128, 256, 4, 1, False, 1.0),
+    (1, 200, 333, 8, 2, False, 1.0),     # ragged q and kv tails, g = 4
+    (2, 77, 130, 8, 4, True, 1.0),       # g = 2, batch 2, random positions
+    (1, 300, 500, 3, 3, True, 1.0),      # g = 1
+    (1, 96, 64, 12, 4, True, 1.0),       # g = 3
+    (1, 257, 640, 8, 1, True, 1.0),      # g = 8, many tiles
+    (1, 130, 700, 8, 1, True, 4.0),      # peaked softmax (scores x4)
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_block_bwd_matches_oracle(case):
+    b, s_q, s_kv, n_q, n_kv, causal, mult = case
+    print(f"block bwd {case}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(str(case).encode()))
+    q, q64 = rand_inputs((b, s_q, n_q, 128), "bf16", rng)
+    k, k64 = rand_inputs((b, s_kv, n_kv, 128), "bf16", rng)
+    v, v64 = rand_inputs((b, s_kv, n_kv, 128), "bf16", rng)
+    do, do64 = rand_inputs((b, s_q, n_q, 128), "bf16", rng)
+    span = 2 * (s_q + s_kv) + 1
+    q_pos = np.sort(rng.choice(span, s_q, replace=False)).astype(np.int32)
+    kv_pos = np.sort(rng.choice(span, s_kv, replace=False)).astype(np.int32)
+    scale = np.float32(mult / math.sqrt(128))
+    o, lse = oatt.naive_attention(q64, k64, v64, q_pos, kv_pos, causal, scale)
+    if causal:
+        assert np.isneginf(lse).any() or q_pos[0] >= kv_pos[0]
+    dq, dk, dv = run_block_bwd((q, k, v, do), o, lse, q_pos, kv_pos, causal, float(scale))
+    rq, rk, rv = obwd.naive_attention_bwd(q64, k64, v64, do64, q_pos, kv_pos, causal, scale)
+    for got, want, name in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        err, mag = grad_close(got, want, f"{case} {name}")
+        print(f"  {name}: max err {err:.2e} (max |ref| {mag:.2e})")
+    # rows with no visible key anywhere contribute nothing and get dq = 0
+    empty = np.isneginf(lse)
+    if empty.any():
+        assert not dq[empty].any()
+
+
+def test_block_bwd_accumulates():
+    """The outputs are added to: two calls give twice one call."""
+    rng = np.random.default_rng(7)
+    q, q64 = rand_inputs((1, 64, 4, 128), "bf16", rng)
+    k, k64 = rand_inputs((1, 96, 2, 128), "bf16", rng)
+    v, v64 = rand_inputs((1, 96, 2, 128), "bf16", rng)
+    do, do64 = rand_inputs((1, 64, 4, 128), "bf16", rng)
+    pos_q = np.arange(32, 96, dtype=np.int32)
+    pos_k = np.arange(96, dtype=np.int32)
+    o, lse = oatt.naive_attention(q64, k64, v64, pos_q, pos_k, True, 1 / math.sqrt(128))
+    tq, tk, tv, tdo = (to_device(x, "bf16") for x in (q, k, v, do))
+    tl = torch.from_numpy(lse.astype(np.float32)).cuda()
+    delta = torch.empty((1, 64, 4), device="cuda")
+    ra.ra_attn_bwd_delta(tdo, torch.from_numpy(o.astype(np.float32)).cuda(), delta)
+    outs = [torch.zeros((1, 64, 4, 128), device="cuda"), torch.zeros((1, 96, 2, 128), device="cuda"),
+            torch.zeros((1, 96, 2, 128), device="cuda")]
+    kw = dict(causal=True, q_pos=torch.from_numpy(pos_q).cuda(), kv_pos=torch.from_numpy(pos_k).cuda())
+    ra.ra_block_attn_bwd(tq, tk, tv, tdo, tl, delta, *outs, **kw)
+    once = [t.clone() for t in outs]
+    ra.ra_block_attn_bwd(tq, tk, tv, tdo, tl, delta, *outs, **kw)
+    torch.cuda.synchronize()
+    for a, b2 in zip(once, outs):
+        assert torch.equal(2 * a, b2)
+
+
+RING_CASES = [("contiguous", 2), ("zigzag", 4), ("striped", 4), ("zigzag", 1), ("contiguous", 4)]
+
+
+@pytest.mark.parametrize("case", RING_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_ring_bwd_all_ranks_reassemble_sequence_gradients(case):
+    kind, N = case
+    print(f"ring bwd {case}", flush=True)
+    S = 192 * 2 * N
+    w = synth.Workload("bwd", 1, S, N, kind, 8, 2, 128, "bf16", 1.0, True, seed=60 + N)
+    rng = np.random.default_rng(60 + N)
+    full = synth.draw(w.with_(N=1, kind="contiguous", rank=0))      # q for every token
+    k64, v64 = full.k64, full.v64
+    do_bits = synth.bf16_bits(rng.standard_normal(full.q.shape, dtype=np.float32))
+    do64 = synth.bf16_to_f32(do_bits).astype(np.float64)
+    want = obwd.naive_attention_bwd(full.q64, k64, v64, do64, np.arange(S), np.arange(S), True,
+                                    w.scale)
+    kc = runner.chunk_kv(runner.host_to_device(full.k, "bf16", "cuda"), kind, N)
+    vc = runner.chunk_kv(runner.host_to_device(full.v, "bf16", "cuda"), kind, N)
+    dkc = torch.zeros((N,) + tuple(kc.shape[1:]), device="cuda")
+    dvc = torch.zeros_like(dkc)
+    for rank in range(N):
+        pos = opart.partition_map(kind, S, N, rank)
+        o, lse = oatt.naive_attention(full.q64[:, pos], k64, v64, pos, np.arange(S), True, w.scale)
+        q = runner.host_to_device(full.q[:, pos], "bf16", "cuda")
+        do = runner.host_to_device(do_bits[:, pos], "bf16", "cuda")
+        desc, _ = ra.ring_desc(b=1, n_q=8, n_kv=2, d=128, dtype=ra.RA_BF16, causal=True, kind=kind,
+                               S=S, N=N, rank=rank, scale=float(w.scale))
+        ws = torch.empty(ra.ra_ring_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xFF)
+        dq = torch.full(q.shape, float("nan"), device="cuda")
+        ra.ra_ring_bwd(desc, q, kc, vc, torch.from_numpy(o.astype(np.float32)).cuda(),
+                       torch.from_numpy(lse.astype(np.float32)).cuda(), do, dq, dkc, dvc, ws)
+        torch.cuda.synchronize()
+        grad_close(dq.cpu().numpy(), want[0][:, pos], f"{case} rank {rank} dq")
+    dk = np.zeros_like(k64)
+    dv = np.zeros_like(v64)
+    dkh, dvh = dkc.cpu().numpy(), dvc.cpu().numpy()
+    for j in range(N):
+        pj = opart.partition_map(kind, S, N, j)
+        dk[:, pj] = dkh[j]
+        dv[:, pj] = dvh[j]
+    grad_close(dk, want[1], f"{case} dk")
+    grad_close(dv, want[2], f"{case} dv")
