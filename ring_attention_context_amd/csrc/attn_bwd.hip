@@ -17,9 +17,11 @@
 //     dQ^T += K^T dS^T (K^T operands by the transposing ds_read_b64_tr_b16).
 //     Every lane holds one query, so lse and D are per-lane constants;
 //   * bwd_dkdv_kernel (bf16, d = 128): a wave owns 32 keys of one key/value
-//     head, with its K and V rows in registers; 4 waves share each block of 32
+//     head, with its K and V rows in registers; 4 waves share each block of 64
 //     queries (q, do, lse, D, positions) staged in LDS, for every query head of
-//     the GQA group. Per block: S = Q K^T and dP = dO V^T (Q and dO rows by
+//     the GQA group, and work through it in 32-row sub-blocks, reading each
+//     sub-block's LDS operands up front. Per sub-block: S = Q K^T and
+//     dP = dO V^T (Q and dO rows by
 //     ds_read_b128), then dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T by
 //     the transposing read), so each lane ends up holding d-values of one key.
 // P and dS enter the MFMAs as bf16; every accumulation is fp32. dq, dk and dv
@@ -377,8 +379,9 @@ constexpr int KV_WAVES = 4;
 constexpr int KV_THREADS = KV_WAVES * 64;
 constexpr int KV_KW = 32;                    // keys per wave
 constexpr int KV_KT = KV_WAVES * KV_KW;      // keys per workgroup
-constexpr int KV_QB = 32;                    // queries per staged block
-constexpr int KV_TILE_B = KV_QB * ROW_B;     // 8 KiB (q or do)
+constexpr int KV_QB = 64;                    // queries per staged block (two 32-row sub-blocks)
+constexpr int KV_SUB = 32;
+constexpr int KV_TILE_B = KV_QB * ROW_B;     // 16 KiB (q or do)
 constexpr int KV_LOADS = KV_TILE_B / (1024 * KV_WAVES);
 
 __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
       q_lds2[KV_TILE_B];
   __shared__ __attribute__((aligned(16))) unsigned char d_lds0[KV_TILE_B], d_lds1[KV_TILE_B],
       d_lds2[KV_TILE_B];
-  // per stage: lse (64 floats), delta (64 floats), positions (64 int32); entries >= 32 unused
+  // per stage: lse (64 floats), delta (64 floats), positions (64 int32) of the block's rows
   __shared__ __attribute__((aligned(16))) float l_lds0[64], l_lds1[64], l_lds2[64];
   __shared__ __attribute__((aligned(16))) float e_lds0[64], e_lds1[64], e_lds2[64];
   __shared__ __attribute__((aligned(16))) int32_t p_lds0[64], p_lds1[64], p_lds2[64];
@@ -528,30 +531,42 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
 
-  // S accumulator: lane holds key `col`; element a holds query row
-  // (a/4)*8 + hi*4 + a%4 of the block.
-  auto process = [&](int it, auto stage) INLINE {
-    int64_t q0;
-    int h;
-    blk_of(it, &q0, &h);
-    (void)h;
-    const int32_t *pp = p_stage(stage);
-    // Whole block before the wave's first key (causal): nothing visible.
-    if (a.causal && pp[min<int64_t>(KV_QB, a.s_q - q0) - 1] < w_kmin) return;
+  // One 32-row sub-block (rows rb .. rb+31 of the staged block). S
+  // accumulator: lane holds key `col`; element a holds sub-block row
+  // (a/4)*8 + hi*4 + a%4.
+  auto process_sub = [&](int64_t q0, int rb, auto stage) INLINE {
+    const int32_t *pp = p_stage(stage) + rb;
+    const int64_t qlim = a.s_q - q0 - rb;     // rows past the sequence are masked
+    if (qlim <= 0) return;
+    // Whole sub-block before the wave's first key (causal): nothing visible.
+    if (a.causal && pp[min<int64_t>(KV_SUB, qlim) - 1] < w_kmin) return;
     const unsigned char *qb = q_stage(stage);
     const unsigned char *db = d_stage(stage);
+    // Every LDS operand of the sub-block is read up front (one wave per SIMD:
+    // a read issued just before its MFMA would expose the whole LDS latency).
+    bf16x8 qa[D / 16], da[D / 16], qt[2][D / 32], dt[2][D / 32];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      qa[ds] = *reinterpret_cast<const bf16x8 *>(qb + rb * ROW_B + qoff[ds]);
+      da[ds] = *reinterpret_cast<const bf16x8 *>(db + rb * ROW_B + qoff[ds]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dblk = 0; dblk < D / 32; ++dblk) {
+        dt[ks][dblk] = tr_read(db, toff, dblk, rb + ks * 16);
+        qt[ks][dblk] = tr_read(qb, toff, dblk, rb + ks * 16);
+      }
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(qb + qoff[ds]);
-      const bf16x8 da = *reinterpret_cast<const bf16x8 *>(db + qoff[ds]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ds], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[ds], dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ds], kreg[ds], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ds], vreg[ds], dp, 0, 0, 0);
     }
-    const float *ll = l_stage(stage);
-    const float *ee = e_stage(stage);
-    const int64_t qlim = a.s_q - q0;          // rows past the sequence are masked
-    const bool ragged = qlim < KV_QB;
+    const float *ll = l_stage(stage) + rb;
+    const float *ee = e_stage(stage) + rb;
+    const bool ragged = qlim < KV_SUB;
     const bool diag = a.causal && pp[0] < w_kmax;  // some query sees only part of the keys
     bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -579,16 +594,22 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     // dV^T += dO^T P and dK^T += Q^T dS: A = dO^T / Q^T by the transposing read,
-    // B = P / dS (k-slots = queries of the block's 16-row steps).
+    // B = P / dS (k-slots = queries of the sub-block's 16-row steps).
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int dblk = 0; dblk < D / 32; ++dblk) {
-        dv[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(db, toff, dblk, ks * 16), pb[ks],
-                                                           dv[dblk], 0, 0, 0);
-        dk[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb, toff, dblk, ks * 16), dsb[ks],
-                                                           dk[dblk], 0, 0, 0);
+        dv[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[ks][dblk], pb[ks], dv[dblk], 0, 0, 0);
+        dk[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[ks][dblk], dsb[ks], dk[dblk], 0, 0, 0);
       }
+  };
+  auto process = [&](int it, auto stage) INLINE {
+    int64_t q0;
+    int h;
+    blk_of(it, &q0, &h);
+    (void)h;
+    process_sub(q0, 0, stage);
+    process_sub(q0, KV_SUB, stage);
   };
 
   using St0 = std::integral_constant<int, 0>;
