@@ -484,10 +484,14 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int r = 4 * (wave + KV_WAVES * i) + (lane >> 4);
     goff[i] = static_cast<uint32_t>(r * q_row_bytes + (((lane & 15) ^ swz(r & 15)) << 4));
   }
+  // Iteration it -> (query block, head): blocks from the last one down, the g
+  // heads of a block back to back. Every workgroup of a kv head then walks the
+  // same blocks in the same order (they differ only in where they stop), so
+  // workgroups resident together read each block while it is in L2.
   auto blk_of = [&](int it, int64_t *q0, int *h) INLINE {
-    const int hh = static_cast<int>(it / n_blk);
-    *q0 = (qb0 + (it - static_cast<int64_t>(hh) * n_blk)) * KV_QB;
-    *h = kvh * g + hh;
+    const int64_t j = it / g;
+    *q0 = (qb0 + n_blk - 1 - j) * KV_QB;
+    *h = kvh * g + static_cast<int>(it - j * g);
   };
   auto issue_blk = [&](int it, auto stage) INLINE {
     int64_t q0;

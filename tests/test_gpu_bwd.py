@@ -138,14 +138,17 @@ def test_block_bwd_accumulates():
         assert torch.equal(2 * a, b2)
 
 
-RING_CASES = [("contiguous", 2), ("zigzag", 4), ("striped", 4), ("zigzag", 1), ("contiguous", 4)]
+# (kind, N, S): c = S / N; c = 200 and 150 end in a ragged query block and
+# key tile.
+RING_CASES = [("contiguous", 2, 768), ("zigzag", 4, 1536), ("striped", 4, 1536),
+              ("zigzag", 1, 384), ("contiguous", 4, 1536), ("zigzag", 2, 400),
+              ("contiguous", 2, 300)]
 
 
 @pytest.mark.parametrize("case", RING_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_ring_bwd_all_ranks_reassemble_sequence_gradients(case):
-    kind, N = case
+    kind, N, S = case
     print(f"ring bwd {case}", flush=True)
-    S = 192 * 2 * N
     w = synth.Workload("bwd", 1, S, N, kind, 8, 2, 128, "bf16", 1.0, True, seed=60 + N)
     rng = np.random.default_rng(60 + N)
     full = synth.draw(w.with_(N=1, kind="contiguous", rank=0))      # q for every token
