@@ -29,10 +29,13 @@ Modules:
 * :mod:`oracle.backward` -- the gradients of softmax attention (plain
   definition by the chain rule), one block's contributions with the global
   lse (§3 backward paragraph), and the ring backward (§4).
+* :mod:`oracle.documents` -- all-gather CP (§8): the K/V of every rank
+  gathered into global order, and the rank's attention under the document
+  mask (no attention across documents) combined with the causal rule.
 
 Parity status: every function here is pinned by ``tests/test_oracle*.py``
 against closed forms, brute force, a library special case or numbers the
 pages print. No function is "parity unpinned".
 """
 
-from . import attention, backward, partition  # noqa: F401
+from . import attention, backward, documents, partition  # noqa: F401

@@ -1,0 +1,87 @@
+"""The all-gather / document-mask oracle against its pins
+(tests/oracle_doc_pins.py), and planted mistakes in it that the pins must
+catch. CPU only; touches only the oracle."""
+
+import types
+
+import numpy as np
+import pytest
+
+import oracle_doc_pins as pins
+from oracle import attention, documents, partition
+
+
+def namespace():
+    """Late-bound view of the oracle: monkeypatched functions are seen."""
+    names = ["doc_ids_from_lengths", "doc_start", "visible_docs", "masked_attention",
+             "allgather_kv", "allgather_attention", "doc_visible_pairs"]
+    ns = {n: (lambda n: lambda *a: getattr(documents, n)(*a))(n) for n in names}
+    ns["naive_attention"] = lambda *a: attention.naive_attention(*a)
+    ns["partition_map"] = lambda *a: partition.partition_map(*a)
+    return types.SimpleNamespace(**ns)
+
+
+@pytest.mark.parametrize("pin", pins.DOC_PINS, ids=lambda p: p.__name__)
+def test_doc_oracle_pin(pin):
+    pin(namespace())
+
+
+# ------------------------------------------------------------- planted mistakes
+
+real_visible = documents.visible_docs
+real_gather = documents.allgather_kv
+real_start = documents.doc_start
+real_masked = documents.masked_attention
+
+
+def visible_earlier_docs(q_pos, kv_pos, ids, causal=True):
+    """Lets a query see earlier documents too (<= on document ids)."""
+    q_pos, kv_pos, ids = np.asarray(q_pos), np.asarray(kv_pos), np.asarray(ids)
+    m = ids[kv_pos][None, :] <= ids[q_pos][:, None]
+    return m & (kv_pos[None, :] <= q_pos[:, None]) if causal else m
+
+
+def visible_no_docs(q_pos, kv_pos, ids, causal=True):
+    return partition.visible(q_pos, kv_pos, causal)
+
+
+def visible_no_causal(q_pos, kv_pos, ids, causal=True):
+    return real_visible(q_pos, kv_pos, ids, False)
+
+
+def gather_shifted(chunks, kind, S, N):
+    """Places chunk j at rank (j + 1)'s positions."""
+    chunks = np.roll(np.asarray(chunks), 1, axis=0)
+    return real_gather(chunks, kind, S, N)
+
+
+def start_off_by_one(ids):
+    s = real_start(ids)
+    return np.where(s > 0, s + 1, s)
+
+
+def masked_no_scale(q, k, v, vis, scale):
+    return real_masked(q, k, v, vis, 1.0)
+
+
+MUTANTS = {
+    "visible_earlier_docs": ("visible_docs", visible_earlier_docs),
+    "visible_no_docs": ("visible_docs", visible_no_docs),
+    "visible_no_causal": ("visible_docs", visible_no_causal),
+    "gather_shifted": ("allgather_kv", gather_shifted),
+    "start_off_by_one": ("doc_start", start_off_by_one),
+    "masked_no_scale": ("masked_attention", masked_no_scale),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_doc_pins_catch_planted_mistake(name, monkeypatch):
+    fname, fn = MUTANTS[name]
+    monkeypatch.setattr(documents, fname, fn)
+    caught = []
+    for pin in pins.DOC_PINS:
+        try:
+            pin(namespace())
+        except Exception as exc:  # noqa: BLE001 -- any failure counts as caught
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"no pin caught the planted mistake {name}"
