@@ -16,6 +16,12 @@ backward: dQ of the rank and its contributions to every block's dK, dV), and
 the metric counts 10 * b * n_q * d flop per visible pair (the five matmuls of
 the attention backward, 2.5x the forward).
 
+With --allgather the step is one ``ra_allgather_fwd`` call (all-gather
+context parallelism: K/V of every rank gathered into the sequence, one pass
+of the rank's queries over it) under a document mask, on the Llama-3-70B
+shape at 128K with packed documents; visible pairs are those inside the
+query's document and at or before it.
+
 Prints progress on stderr and ONE JSON line on stdout.
 """
 
@@ -35,6 +41,8 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "causal-adjusted attention TFLOP/s per rank shard + % of bf16 MFMA peak"
 METRIC_BWD = ("causal-adjusted attention backward TFLOP/s per rank shard (10*d flop per visible "
               "pair and head) + % of bf16 MFMA peak")
+METRIC_AG = ("document-masked causal attention TFLOP/s per rank shard, all-gather CP "
+             "(4*d flop per visible pair and head) + % of bf16 MFMA peak")
 
 
 def log(msg):
@@ -138,6 +146,117 @@ def cpu_baseline_bwd(w, seconds_hint=15.0):
             "sample": f"{len(rows)} of {w.c} query rows x {w.n_q} heads vs all {w.S} keys "
                       f"(fp64 NumPy backward by the chain rule, {t:.1f} s, {pairs} visible pairs)",
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def doc_pairs(q_pos, doc_start):
+    """Visible pairs of queries at q_pos under the document mask and the causal
+    rule: a query at p sees the positions doc_start[p] .. p."""
+    import numpy as np
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    return int((q_pos - doc_start[q_pos] + 1).sum())
+
+
+def cpu_baseline_docs(w, lengths, seconds_hint=15.0):
+    """Time the fp64 document-mask oracle (as it stands) on a bounded sample of
+    query rows x all heads against the whole sequence."""
+    import numpy as np
+    import synth
+    from oracle import documents as odoc
+    from oracle import partition as opart
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    per_row = 4 * w.d * w.n_q * w.S          # the oracle scores every key, then masks
+    rows_n = int(max(8, min(512, seconds_hint * 2.5e10 / per_row)))
+    rows = synth.sample_rows(w.c, rows_n, w.seed)
+    inp = synth.draw(w, q_rows=rows)
+    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)[rows]
+    ids = odoc.doc_ids_from_lengths(lengths)
+    k64, v64, q64 = inp.k64, inp.v64, inp.q64
+    t0 = time.perf_counter()
+    odoc.rows_attention_docs(q64, k64, v64, q_pos, ids, True, w.scale)
+    t = time.perf_counter() - t0
+    pairs = odoc.doc_visible_pairs(q_pos, ids, True)
+    flops = 4 * w.b * w.n_q * w.d * pairs
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {w.c} query rows x {w.n_q} heads vs all {w.S} keys "
+                      f"under the document mask (fp64 NumPy, {t:.1f} s, {pairs} visible pairs)",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def run_allgather(args, w, dev, props):
+    """Time ra_allgather_fwd (one rank of all-gather CP, document mask) and print
+    its JSON line."""
+    import numpy as np
+    import torch
+    import synth
+    from ring_attention_context_amd import ra_partition, runner
+    t0 = time.perf_counter()
+    inp = synth.draw(w)
+    q, kc, vc = runner.ring_inputs(inp.q, inp.k, inp.v, w.dtype, w.kind, w.N, dev)
+    del inp
+    lengths = synth.doc_lengths(w.S, w.seed)
+    starts = runner.doc_start_positions(lengths)
+    ds = torch.from_numpy(starts).to(dev)
+    log(f"[bench-ag] inputs resident in HBM ({time.perf_counter() - t0:.1f} s); "
+        f"{len(lengths)} documents")
+    stream = torch.cuda.Stream(dev)
+    call = runner.AllGatherCall(q, kc, vc, kind=w.kind, S=w.S, N=w.N, rank=w.rank,
+                                causal=True, scale=w.scale, doc_start=ds, stream=stream)
+    pairs = doc_pairs(ra_partition(w.kind, w.S, w.N, w.rank), starts)
+    total_flops = 4 * w.b * w.n_q * w.d * pairs
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    log(f"[bench-ag] warmup {args.warmup} done")
+    evs = []
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for x in e:
+            x.record(stream)
+        evs.append(e)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    kern = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    achieved = total_flops / (float(kern.mean()) * 1e-3) / 1e12
+    log(f"[bench-ag] {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s; "
+        f"attention launch {kern.mean():.3f} ms")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_docs(w, lengths, args.cpu_seconds)
+    out = {
+        "metric": METRIC_AG,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), bf16 round-to-nearest-even; seeded document lengths)",
+        "config": {"workload": w.name, "pass": "forward, all-gather CP", "b": w.b, "S": w.S,
+                   "N": w.N, "rank": w.rank, "map": w.kind, "n_q": w.n_q, "n_kv": w.n_kv,
+                   "d": w.d, "causal": True, "documents": len(lengths), "scale": w.scale,
+                   "queries_per_rank": w.c, "visible_pairs": pairs},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_bf16_kernel (one launch per call)",
+                     "avg_launch_ms": round(float(kern.mean()), 4), "launches": len(kern),
+                     "flops_per_launch_avg": total_flops},
+        "cpu_baseline": cpu,
+        "device": props.name,
+    }
+    print(json.dumps(out), flush=True)
 
 
 def run_backward(args, w, q, kc, vc, dev, props):
@@ -316,6 +435,9 @@ def main():
                          "imbalance study (no contract line)")
     ap.add_argument("--backward", action="store_true",
                     help="time the ring backward (ra_ring_bwd) instead of the forward")
+    ap.add_argument("--allgather", action="store_true",
+                    help="time all-gather CP with a document mask (ra_allgather_fwd) on the "
+                         "llama3_70b_128k_allgather_docs workload (or --workload of that family)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size "
                          "reference for HBM byte counters)")
@@ -339,6 +461,18 @@ def main():
 
     if args.sweep:
         run_sweep(args.sweep, args.warmup, max(2, args.steps // 3))
+        return
+
+    if args.allgather:
+        name = (args.workload if args.workload in synth.ALLGATHER_WORKLOADS
+                else "llama3_70b_128k_allgather_docs")
+        w = synth.ALLGATHER_WORKLOADS[name]
+        if args.rank is not None:
+            w = w.with_(rank=args.rank)
+        dev = torch.device("cuda:0")
+        props = torch.cuda.get_device_properties(dev)
+        log(f"[bench-ag] device {props.name} CUs={props.multi_processor_count} workload={w}")
+        run_allgather(args, w, dev, props)
         return
 
     w = synth.WORKLOADS[args.workload]

@@ -14,6 +14,10 @@
  *                           running (o, lse). On one GPU the neighbour's send
  *                           becomes a device-to-device prefetch into a double
  *                           buffer (§4 "memory": six blocks, double-buffered).
+ *   - ra_allgather_fwd   -- §8 all-gather CP: the K/V of all ranks gathered
+ *                           into the whole sequence, then one pass of the
+ *                           rank's queries over it, optionally under the
+ *                           document mask (no attention across documents).
  * With N = 1 the ring call is a single dense pass: the local attention of one
  * rank after the DeepSpeed-Ulysses all-to-all (§9; "DeepSpeed-Ulysses and
  * hybrids", t6page.pages.dev: full sequence, h/N heads).
@@ -102,6 +106,10 @@ typedef struct ra_attn_desc {
   int32_t v_layout;   /* ra_v_layout of v (RA_V_ROWS unless stated)         */
   const int32_t *q_pos;   /* device [s_q] global positions, non-decreasing   */
   const int32_t *kv_pos;  /* device [s_kv] global positions, non-decreasing  */
+  const int32_t *q_doc_start;  /* device [s_q] or NULL: document mask. The
+                           global position where the query's document starts
+                           (<= its q_pos, non-decreasing); a key is visible
+                           only if q_doc_start <= kv_pos. Needs causal = 1.  */
 } ra_attn_desc;
 
 /*
@@ -115,6 +123,9 @@ typedef struct ra_attn_desc {
  * both fully overwritten. Rows with no visible key get (0, -inf).
  * q_pos / kv_pos are read only when causal; positions out of order give
  * unspecified values (never an out-of-bounds access).
+ * With q_doc_start, key j is visible to query a iff
+ * q_doc_start[a] <= kv_pos[j] <= q_pos[a]: the causal rule plus the
+ * document mask of §8 when documents are runs of consecutive positions.
  */
 ra_status ra_block_attn_fwd(const ra_attn_desc *desc, const void *q, const void *k,
                             const void *v, float *o_b, float *lse_b, void *stream);
@@ -160,6 +171,13 @@ typedef struct ra_ring_desc {
   int32_t reserved;         /* must be 0                                     */
   void **step_events;       /* optional: N+1 hipEvent_t, recorded on
                                `compute` before step 0 and after each step   */
+  const int32_t *doc_start; /* optional device [S]: document mask (§8). For
+                               every global position p, the first position
+                               of p's document (0 <= doc_start[p] <= p,
+                               non-decreasing: documents are runs of
+                               consecutive positions). A key is visible only
+                               within the query's document. Needs causal = 1;
+                               ra_ring_fwd and ra_allgather_fwd only.       */
 } ra_ring_desc;
 
 /* Workspace bytes ra_ring_fwd needs for *desc (same validation as the call). */
@@ -189,6 +207,27 @@ ra_status ra_ring_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
 ra_status ra_ring_fwd(const ra_ring_desc *desc, const void *q, const void *k_chunks,
                       const void *v_chunks, float *o, float *lse, void *workspace,
                       size_t workspace_bytes, void *compute, void *copy);
+
+/* Workspace bytes ra_allgather_fwd needs for *desc (same validation as the call). */
+ra_status ra_allgather_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
+
+/*
+ * ra_allgather_fwd -- all-gather context parallelism ("Context Parallelism
+ * and Ring Attention" §8) for rank `rank`, replayed on one GPU: the K and V
+ * chunks of all N ranks are gathered into the whole sequence in global
+ * position order (the all-gather's result), then the rank's queries attend
+ * over every key in one pass (no merge), with the causal rule and, when
+ * desc->doc_start is set, the document mask.
+ * Arguments as for ra_ring_fwd (flags must be 0); o and lse are
+ * overwritten. step_events, if set, holds 2 hipEvent_t recorded on `stream`
+ * just before and just after the attention launch. workspace: device, >= ra_allgather_workspace_bytes();
+ * holds the positions, the gathered K and V of the sequence (for bf16 with
+ * S % 8 == 0, V also transposed, RA_V_TRANSPOSED) and the queries' document
+ * starts. Runs on `stream`.
+ */
+ra_status ra_allgather_fwd(const ra_ring_desc *desc, const void *q, const void *k_chunks,
+                           const void *v_chunks, float *o, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * Backward ("Context Parallelism and Ring Attention" §3, backward paragraph;
@@ -230,7 +269,7 @@ ra_status ra_ring_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
 /*
  * ra_ring_bwd -- the ring backward for rank `rank`, replayed on one GPU.
  * desc: as for ra_ring_fwd (bf16, d = 128; flags 0 or RA_RING_SERIALIZE,
- * which changes nothing here: one stream).
+ * which changes nothing here: one stream; doc_start must be NULL).
  * q, dout: device [b, c, n_q, d] bf16, the rank's tokens in its local order;
  * o, lse: device float32 [b, c, n_q, d] and [b, c, n_q], the rank's forward
  * outputs (global o and lse); k_chunks, v_chunks: device [N, b, c, n_kv, d]

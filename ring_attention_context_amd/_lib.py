@@ -24,7 +24,8 @@ KINDS = {"contiguous": RA_PART_CONTIGUOUS, "zigzag": RA_PART_ZIGZAG, "striped": 
 
 EXPORTED = ("ra_partition", "ra_block_attn_fwd", "ra_v_transpose", "ra_lse_merge",
             "ra_ring_workspace_bytes", "ra_ring_fwd", "ra_attn_bwd_delta", "ra_block_attn_bwd",
-            "ra_ring_bwd_workspace_bytes", "ra_ring_bwd", "ra_status_str", "ra_last_error")
+            "ra_ring_bwd_workspace_bytes", "ra_ring_bwd", "ra_allgather_workspace_bytes",
+            "ra_allgather_fwd", "ra_status_str", "ra_last_error")
 
 
 class RingAttnError(RuntimeError):
@@ -38,7 +39,7 @@ class AttnDesc(ctypes.Structure):
                 ("d", ctypes.c_int32), ("s_q", ctypes.c_int64), ("s_kv", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("v_layout", ctypes.c_int32), ("q_pos", ctypes.c_void_p),
-                ("kv_pos", ctypes.c_void_p)]
+                ("kv_pos", ctypes.c_void_p), ("q_doc_start", ctypes.c_void_p)]
 
 
 class RingDesc(ctypes.Structure):
@@ -46,7 +47,8 @@ class RingDesc(ctypes.Structure):
                 ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("kind", ctypes.c_int32), ("S", ctypes.c_int64),
                 ("N", ctypes.c_int32), ("rank", ctypes.c_int32), ("flags", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("step_events", ctypes.c_void_p)]
+                ("reserved", ctypes.c_int32), ("step_events", ctypes.c_void_p),
+                ("doc_start", ctypes.c_void_p)]
 
 
 _lib = None
@@ -77,9 +79,14 @@ def load_library(path=None):
                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.ra_ring_bwd.argtypes = [ctypes.POINTER(RingDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 ctypes.c_size_t, vp]
+    lib.ra_allgather_workspace_bytes.argtypes = [ctypes.POINTER(RingDesc),
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+    lib.ra_allgather_fwd.argtypes = [ctypes.POINTER(RingDesc), vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
     for name in ("ra_partition", "ra_block_attn_fwd", "ra_v_transpose", "ra_lse_merge",
                  "ra_ring_workspace_bytes", "ra_ring_fwd", "ra_attn_bwd_delta",
-                 "ra_block_attn_bwd", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd"):
+                 "ra_block_attn_bwd", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd",
+                 "ra_allgather_workspace_bytes", "ra_allgather_fwd"):
         getattr(lib, name).restype = i32
     lib.ra_status_str.argtypes = [i32]
     lib.ra_status_str.restype = ctypes.c_char_p
@@ -147,17 +154,20 @@ def ra_partition(kind, S, N, rank):
 
 
 def ra_block_attn_fwd(q, k, v, o_b, lse_b, *, causal, scale=0.0, q_pos=None, kv_pos=None,
-                      v_transposed=False, stream=None):
+                      v_transposed=False, q_doc_start=None, stream=None):
     """q [b, s_q, n_q, d], k [b, s_kv, n_kv, d] (bf16 or f32, same dtype); v like k, or
     [b, n_kv, d, s_kv] with ``v_transposed`` (bf16, see :func:`ra_v_transpose`);
     writes o_b float32 [b, s_q, n_q, d] and lse_b float32 [b, s_q, n_q].
-    q_pos / kv_pos: int32 device tensors of global positions (causal only)."""
-    _need_contiguous(q, k, v, o_b, lse_b, q_pos, kv_pos)
+    q_pos / kv_pos: int32 device tensors of global positions (causal only).
+    q_doc_start: int32 device tensor [s_q], the position where each query's
+    document starts (document mask; causal only)."""
+    _need_contiguous(q, k, v, o_b, lse_b, q_pos, kv_pos, q_doc_start)
     desc = AttnDesc(b=q.shape[0], n_q=q.shape[2], n_kv=k.shape[2], d=q.shape[3],
                     s_q=q.shape[1], s_kv=k.shape[1], dtype=_dtype_code(q), causal=int(causal),
                     scale=scale, v_layout=RA_V_TRANSPOSED if v_transposed else RA_V_ROWS,
                     q_pos=None if q_pos is None else q_pos.data_ptr(),
-                    kv_pos=None if kv_pos is None else kv_pos.data_ptr())
+                    kv_pos=None if kv_pos is None else kv_pos.data_ptr(),
+                    q_doc_start=None if q_doc_start is None else q_doc_start.data_ptr())
     _check(load_library().ra_block_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                             _ptr(o_b), _ptr(lse_b), _stream(stream)))
 
@@ -205,12 +215,14 @@ def ra_block_attn_bwd(q, k, v, dout, lse, delta, dq, dk, dv, *, causal, scale=0.
 
 
 def ring_desc(*, b, n_q, n_kv, d, dtype, causal, kind, S, N, rank, scale=0.0, flags=0,
-              step_events=None):
+              step_events=None, doc_start=None):
     """Build the C ring descriptor. ``step_events``: list of N + 1 torch.cuda.Event
-    (each already recorded once so that its handle exists)."""
+    (each already recorded once so that its handle exists). ``doc_start``: int32
+    device tensor [S], the first position of every position's document."""
     desc = RingDesc(b=b, n_q=n_q, n_kv=n_kv, d=d, dtype=dtype, causal=int(causal), scale=scale,
                     kind=_kind(kind), S=S, N=N, rank=rank, flags=flags, reserved=0,
-                    step_events=None)
+                    step_events=None,
+                    doc_start=None if doc_start is None else doc_start.data_ptr())
     keep = None
     if step_events is not None:
         keep = (ctypes.c_void_p * len(step_events))(*[e.cuda_event for e in step_events])
@@ -248,3 +260,18 @@ def ra_ring_bwd(desc, q, k_chunks, v_chunks, o, lse, dout, dq, dk_chunks, dv_chu
                                       _ptr(v_chunks), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                       _ptr(dk_chunks), _ptr(dv_chunks), _ptr(workspace),
                                       ws_bytes, _stream(stream)))
+
+
+def ra_allgather_workspace_bytes(desc):
+    out = ctypes.c_size_t(0)
+    _check(load_library().ra_allgather_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
+
+
+def ra_allgather_fwd(desc, q, k_chunks, v_chunks, o, lse, workspace, stream=None):
+    """All-gather CP forward of one rank; see ringattn.h. ``desc`` from :func:`ring_desc`."""
+    _need_contiguous(q, k_chunks, v_chunks, o, lse, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().ra_allgather_fwd(ctypes.byref(desc), _ptr(q), _ptr(k_chunks),
+                                           _ptr(v_chunks), _ptr(o), _ptr(lse), _ptr(workspace),
+                                           ws_bytes, _stream(stream)))

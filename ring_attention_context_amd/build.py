@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libringattn.so")
 
 SOURCES = ["status.cpp", "partition.cpp", "attn_api.cpp", "lse_merge.hip", "attn_f32.hip",
-           "attn_bf16.hip", "attn_bwd.hip", "v_transpose.hip", "ring.hip"]
+           "attn_bf16.hip", "attn_bwd.hip", "v_transpose.hip", "ring.hip", "allgather.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,197 @@
+// ra_allgather_fwd: all-gather context parallelism ("Context Parallelism and
+// Ring Attention" §8) for one rank, replayed on one GPU.
+//
+// Instead of passing K/V blocks around a ring, every rank gathers the K and
+// V of the whole sequence from its context-parallel group before attention
+// and attends with its own queries in one pass: no ring steps and no merge.
+// The page gives two reasons for this form: document masks (a sequence that
+// packs several documents must not attend across them) are easy to apply
+// with every key at its original position, and with GQA the gathered K/V are
+// small next to the O(S^2) attention. Here the gather reads the N rank chunks
+// (each in its rank's local order, the layout ra_ring_fwd takes) and writes
+// the sequence in global position order, the layout an all-gather followed by
+// the inverse token permutation of §6 produces. For bf16 V is then
+// transposed into the layout the attention kernel reads fastest. Everything
+// runs on one stream: positions, the queries' document starts, the gathers,
+// the transpose, one attention launch.
+#include <cmath>
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// full[bi, pos[j*c + a], :] = chunks[j, bi, a, :] for every rank j, batch bi
+// and local index a; rows of `row16` 16-byte units (n_kv * d elements). HBM
+// bound: each byte is read once and written once; consecutive threads move
+// consecutive 16-byte units of one row.
+__global__ __launch_bounds__(256) void kv_gather_kernel(const uint4 *__restrict__ chunks,
+                                                        uint4 *__restrict__ full,
+                                                        const int32_t *__restrict__ pos,
+                                                        int64_t c, int32_t b, int64_t S,
+                                                        int64_t row16, int64_t total) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += stride) {
+    const int64_t u = i % row16;
+    const int64_t row = i / row16;         // (j * b + bi) * c + a
+    const int64_t a = row % c;
+    const int64_t jb = row / c;
+    const int64_t bi = jb % b;
+    const int64_t j = jb / b;
+    const int64_t p = pos[j * c + a];
+    full[(bi * S + p) * row16 + u] = chunks[i];
+  }
+}
+
+hipError_t launch_kv_gather(const void *chunks, void *full, const int32_t *pos, int64_t c,
+                            int32_t N, int32_t b, int64_t S, size_t row_bytes,
+                            hipStream_t stream) {
+  const int64_t row16 = static_cast<int64_t>(row_bytes / 16);
+  const int64_t total = static_cast<int64_t>(N) * b * c * row16;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  kv_gather_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(
+      static_cast<const uint4 *>(chunks), static_cast<uint4 *>(full), pos, c, b, S, row16, total);
+  return hipGetLastError();
+}
+
+struct AgPlan {
+  int64_t c = 0;
+  size_t full_bytes = 0;    // K (or V) of the whole sequence [b, S, n_kv, d]
+  size_t pos_off = 0, kvpos_off = 0, qlo_off = 0, k_off = 0, v_off = 0, vt_off = 0, total = 0;
+  bool vt = false;          // V also transposed to [b, n_kv, d, S]
+};
+
+ra_status make_ag_plan(const ra_ring_desc *r, AgPlan *p) {
+  ra_status st = check_ring_desc(r);
+  if (st != RA_OK) return st;
+  if (r->flags != 0) return fail(RA_ERR_INVALID_ARG, "all-gather: flags must be 0 (0x%x)", r->flags);
+  const size_t esize = r->dtype == RA_BF16 ? 2 : 4;
+  p->c = r->S / r->N;
+  p->full_bytes = static_cast<size_t>(r->b) * r->S * r->n_kv * r->d * esize;
+  // V^T rows of S keys: 16-byte aligned rows, and a head's d-rows addressable
+  // with 32-bit buffer offsets.
+  p->vt = r->dtype == RA_BF16 && r->S % 8 == 0 && r->S > 0 &&
+          static_cast<int64_t>(r->b) * r->n_kv <= 65535 &&
+          static_cast<int64_t>(r->d) * r->S * 2 < (int64_t{1} << 31);
+  size_t off = 0;
+  p->pos_off = off;
+  off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
+  p->kvpos_off = off;
+  off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
+  p->qlo_off = off;
+  off += align_up(static_cast<size_t>(p->c) * sizeof(int32_t));
+  p->k_off = off;
+  off += align_up(p->full_bytes);
+  p->v_off = off;
+  off += align_up(p->full_bytes);
+  if (p->vt) {
+    p->vt_off = off;
+    off += align_up(p->full_bytes);
+  }
+  p->total = off;
+  return RA_OK;
+}
+
+}  // namespace
+}  // namespace ra
+
+extern "C" ra_status ra_allgather_workspace_bytes(const ra_ring_desc *desc, size_t *bytes) {
+  ra::clear_error();
+  if (!bytes) return ra::fail(RA_ERR_INVALID_ARG, "ra_allgather_workspace_bytes: bytes is NULL");
+  ra::AgPlan p;
+  ra_status st = ra::make_ag_plan(desc, &p);
+  if (st != RA_OK) return st;
+  *bytes = p.total;
+  return RA_OK;
+}
+
+extern "C" ra_status ra_allgather_fwd(const ra_ring_desc *r, const void *q, const void *k_chunks,
+                                      const void *v_chunks, float *o, float *lse, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  using ra::fail;
+  using ra::hip_check;
+  ra::clear_error();
+  ra::AgPlan P;
+  ra_status st = ra::make_ag_plan(r, &P);
+  if (st != RA_OK) return st;
+  if (r->b == 0 || P.c == 0) return RA_OK;
+  if (!q || !k_chunks || !v_chunks || !o || !lse)
+    return fail(RA_ERR_INVALID_ARG, "ra_allgather_fwd: NULL q / k_chunks / v_chunks / o / lse");
+  if (!ra::aligned16(q) || !ra::aligned16(k_chunks) || !ra::aligned16(v_chunks) ||
+      !ra::aligned16(o))
+    return fail(RA_ERR_INVALID_ARG, "ra_allgather_fwd: q / k / v / o not 16-byte aligned");
+  const size_t esize = r->dtype == RA_BF16 ? 2 : 4;
+  const size_t row_bytes = static_cast<size_t>(r->n_kv) * r->d * esize;
+  if (row_bytes % 16)
+    return fail(RA_ERR_INVALID_ARG, "ra_allgather_fwd: n_kv * d * element size not a multiple of 16");
+  if (!workspace || !ra::aligned16(workspace))
+    return fail(RA_ERR_INVALID_ARG, "ra_allgather_fwd: workspace NULL or not 16-byte aligned");
+  if (workspace_bytes < P.total)
+    return fail(RA_ERR_INVALID_ARG, "ra_allgather_fwd: workspace has %zu bytes, needs %zu",
+                workspace_bytes, P.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  int32_t *pos = reinterpret_cast<int32_t *>(ws + P.pos_off);
+  int32_t *kv_pos = reinterpret_cast<int32_t *>(ws + P.kvpos_off);
+  int32_t *qlo = reinterpret_cast<int32_t *>(ws + P.qlo_off);
+  unsigned char *kfull = ws + P.k_off;
+  unsigned char *vfull = ws + P.v_off;
+  unsigned char *vtfull = ws + P.vt_off;
+  const int32_t *q_pos = pos + static_cast<int64_t>(r->rank) * P.c;
+
+  // Every rank's map (to place its chunk), and the identity map of the
+  // gathered sequence (keys in global order).
+  st = hip_check(ra::launch_positions(r->kind, r->S, r->N, pos, s), "ra_allgather_fwd: positions");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_positions(RA_PART_CONTIGUOUS, r->S, 1, kv_pos, s),
+                   "ra_allgather_fwd: key positions");
+  if (st == RA_OK && r->doc_start)
+    st = hip_check(ra::launch_gather_i32(r->doc_start, q_pos, qlo, P.c, s),
+                   "ra_allgather_fwd: document starts");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_kv_gather(k_chunks, kfull, pos, P.c, r->N, r->b, r->S, row_bytes, s),
+                   "ra_allgather_fwd: K gather");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_kv_gather(v_chunks, vfull, pos, P.c, r->N, r->b, r->S, row_bytes, s),
+                   "ra_allgather_fwd: V gather");
+  if (st == RA_OK && P.vt)
+    st = hip_check(ra::launch_v_transpose(r->b, r->S, r->n_kv, r->d, 2, vfull, vtfull, s),
+                   "ra_allgather_fwd: V transpose");
+  if (st != RA_OK) return st;
+
+  hipEvent_t *ev = reinterpret_cast<hipEvent_t *>(r->step_events);
+  if (ev) {
+    st = hip_check(hipEventRecord(ev[0], s), "ra_allgather_fwd: event");
+    if (st != RA_OK) return st;
+  }
+  ra::AttnArgs a{};
+  a.q = q;
+  a.k = kfull;
+  a.v = P.vt ? vtfull : vfull;
+  a.v_layout = P.vt ? RA_V_TRANSPOSED : RA_V_ROWS;
+  a.o = o;
+  a.lse = lse;
+  a.q_pos = q_pos;
+  a.kv_pos = kv_pos;
+  a.q_lo = r->doc_start ? qlo : nullptr;
+  a.s_q = P.c;
+  a.s_kv = r->S;
+  a.b = r->b;
+  a.n_q = r->n_q;
+  a.n_kv = r->n_kv;
+  a.d = r->d;
+  a.scale = r->scale > 0.f ? r->scale : 1.0f / std::sqrt(static_cast<float>(r->d));
+  a.causal = r->causal;
+  a.merge = 0;
+  hipError_t err = r->dtype == RA_BF16 ? ra::launch_attn_bf16(a, s) : ra::launch_attn_f32(a, s);
+  st = hip_check(err, "ra_allgather_fwd: attention launch");
+  if (st == RA_OK && ev) st = hip_check(hipEventRecord(ev[1], s), "ra_allgather_fwd: event");
+  return st;
+}

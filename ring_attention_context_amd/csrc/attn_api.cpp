@@ -29,6 +29,8 @@ ra_status validate_attn(const ra_attn_desc *d, const void *q, const void *k, con
   }
   if (d->causal != 0 && d->causal != 1)
     return fail(RA_ERR_INVALID_ARG, "attention: causal must be 0 or 1");
+  if (d->q_doc_start && !d->causal)
+    return fail(RA_ERR_UNSUPPORTED, "attention: a document mask needs causal = 1");
   if (d->dtype == RA_BF16) {
     if (d->d != 128) return fail(RA_ERR_UNSUPPORTED, "attention: bf16 needs d = 128 (got %d)", d->d);
   } else if (d->dtype == RA_F32) {
@@ -69,6 +71,7 @@ extern "C" ra_status ra_block_attn_fwd(const ra_attn_desc *desc, const void *q, 
   a.lse = lse_b;
   a.q_pos = desc->q_pos;
   a.kv_pos = desc->kv_pos;
+  a.q_lo = desc->q_doc_start;
   a.s_q = desc->s_q;
   a.s_kv = desc->s_kv;
   a.b = desc->b;

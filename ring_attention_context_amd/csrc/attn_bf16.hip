@@ -8,7 +8,11 @@
 // applied on original positions (§6 "the cost of reordering"); positions are
 // non-decreasing, so tiles past a query tile's last position are never
 // loaded (the tile skipping of §7), and only tiles that straddle the
-// diagonal, or the ragged last tile, evaluate the element mask.
+// diagonal, or the ragged last tile, evaluate the element mask. With the
+// document mask of §8 (all-gather CP) each query also carries the position
+// where its document starts: the key range begins at the tile holding the
+// first query's document start, and tiles that begin before a query's
+// document start evaluate the element mask too.
 //
 // Work decomposition (d = 128):
 //   * a wave owns 32 query tokens of one query head; a workgroup of 8 waves
@@ -121,6 +125,18 @@ __device__ __forceinline__ int64_t count_le(const int32_t *kv_pos, int64_t n, in
   }
   return lo;
 }
+// Number of keys with position < p.
+__device__ __forceinline__ int64_t count_lt(const int32_t *kv_pos, int64_t n, int32_t p) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (kv_pos[mid] < p)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
   const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int32_t>(bytes));
@@ -189,16 +205,22 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // ---- key range of the workgroup (causal: keys up to its last position) ----
   // Non-causal: every key is visible, so a query takes position INT_MAX - 1
   // and the tile tests below never skip.
+  // With a document mask the range starts at the tile holding the first key
+  // of the first query's document (document starts are non-decreasing).
   int64_t nkeys = a.s_kv;
+  int64_t kbeg = 0;
   int32_t w_qmin = INT_MAX - 1, w_qmax = INT_MAX - 1;
+  int32_t w_lomax = INT_MIN;  // latest document start among the wave's queries
   if (a.causal) {
     nkeys = count_le(a.kv_pos, a.s_kv, a.q_pos[wg_tok_last]);
+    if (a.q_lo) kbeg = count_lt(a.kv_pos, a.s_kv, a.q_lo[wg_tok0]) / BK * BK;
     if (wave_has_rows) {
       w_qmin = a.q_pos[w_tok0];
       w_qmax = a.q_pos[w_tok_last];
+      if (a.q_lo) w_lomax = a.q_lo[w_tok_last];
     }
   }
-  const int nt = static_cast<int>((nkeys + BK - 1) / BK);
+  const int nt = nkeys > kbeg ? static_cast<int>((nkeys - kbeg + BK - 1) / BK) : 0;
 
   // ---- this lane's query: B operand of S^T = K Q^T (8 bf16 per k-step) ----
   const uint16_t *qg = static_cast<const uint16_t *>(a.q);
@@ -212,6 +234,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     }
   }
   const int32_t qpos = !a.causal ? INT_MAX - 1 : (tok_ok ? a.q_pos[tok] : INT_MIN);
+  const int32_t qlo = a.q_lo && tok_ok ? a.q_lo[tok] : INT_MIN;  // first visible key position
   const float sl2 = a.scale * LOG2E;
 
   // ---- per-lane LDS offsets of the MFMA operands (within one stage) ----
@@ -265,7 +288,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     vgoff[i] = static_cast<uint32_t>(vrow * vt_stride + (((lane & 7) ^ swz_vt(vrow)) << 4));
   }
   auto issue_tile = [&](int t, auto stage) INLINE {
-    const int64_t key0 = static_cast<int64_t>(t) * BK;
+    const int64_t key0 = kbeg + static_cast<int64_t>(t) * BK;
     const int64_t left = a.s_kv - key0;  // rows before the end of the block
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + kv_base + key0 * kv_row_bytes,
                                                 (left - 1) * kv_row_bytes + D * 2);
@@ -325,13 +348,16 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
       }
   };
 
-  // Element mask of a diagonal or ragged tile t held in `stage`. Accumulator
-  // element e4*4 + j of key block kb holds key kk + j.
+  // Element mask of a diagonal or ragged tile t held in `stage` (or one that
+  // starts before a query's document). Accumulator element e4*4 + j of key
+  // block kb holds key kk + j.
   auto mask = [&](int t, auto stage, f32x16 *s) INLINE {
-    const int64_t key0 = static_cast<int64_t>(t) * BK;
+    const int64_t key0 = kbeg + static_cast<int64_t>(t) * BK;
     const bool ragged = key0 + BK > a.s_kv;
-    if (ragged || (a.causal && tile_pos(stage, BK - 1) > w_qmin)) {
-      // Branch-free selects: key index past the block, or position after the query.
+    if (ragged || (a.causal && tile_pos(stage, BK - 1) > w_qmin) ||
+        (a.q_lo && tile_pos(stage, 0) < w_lomax)) {
+      // Branch-free selects: key index past the block, position after the
+      // query, or before the query's document.
       const int lim = ragged ? static_cast<int>(a.s_kv - key0) : BK;
       const int32_t *pp = p_stage(stage);
       const int32_t qp = a.causal ? qpos : INT_MAX;
@@ -343,7 +369,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
                             : kb * 32 + e4 * 8 + hi * 4;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const bool out = (kk + j >= lim) | (pp[kk + j] > qp);
+            const bool out = (kk + j >= lim) | (pp[kk + j] > qp) | (pp[kk + j] < qlo);
             s[kb][e4 * 4 + j] = out ? -INFINITY : s[kb][e4 * 4 + j];
           }
         }

@@ -742,6 +742,8 @@ extern "C" ra_status ra_block_attn_bwd(const ra_attn_desc *desc, const void *q, 
     return fail(RA_ERR_UNSUPPORTED, "ra_block_attn_bwd: bf16 with d = 128 only");
   if (desc->v_layout != RA_V_ROWS)
     return fail(RA_ERR_UNSUPPORTED, "ra_block_attn_bwd: v must be row-major (RA_V_ROWS)");
+  if (desc->q_doc_start)
+    return fail(RA_ERR_UNSUPPORTED, "ra_block_attn_bwd: no document mask in the backward");
   if (desc->b == 0 || desc->s_q == 0 || desc->s_kv == 0) return RA_OK;
   if (!dout || !delta || !dk || !dv)
     return fail(RA_ERR_INVALID_ARG, "ra_block_attn_bwd: NULL dout / delta / dk / dv");

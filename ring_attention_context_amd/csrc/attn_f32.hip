@@ -56,6 +56,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
   // Query position; non-causal uses the smallest value so every key is visible.
   const int qpos = !a.causal ? INT_MAX : (tok_ok ? a.q_pos[tok] : INT_MIN);
+  // First visible key position (document mask); INT_MIN without one.
+  const int qlo = a.q_lo && tok_ok ? a.q_lo[tok] : INT_MIN;
 
   float m_run = -INFINITY, l_run = 0.f;
   float acc[DPT];
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       float dot = 0.f;
 #pragma unroll 16
       for (int e = 0; e < D; ++e) dot = fmaf(qs[r][e], ks[kk][e], dot);
-      const bool vis = kpos[kk] <= qpos && key0 + kk < a.s_kv;
+      const bool vis = kpos[kk] <= qpos && kpos[kk] >= qlo && key0 + kk < a.s_kv;
       s[j] = vis ? dot * a.scale : -INFINITY;
       tmax = fmaxf(tmax, s[j]);
     }

@@ -21,6 +21,7 @@ struct AttnArgs {
   float *lse;
   const int32_t *q_pos;
   const int32_t *kv_pos;
+  const int32_t *q_lo;  // optional [s_q]: first visible key position (document start)
   int64_t s_q;
   int64_t s_kv;
   int32_t b;
@@ -75,6 +76,8 @@ hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_lse_merge(int64_t rows, int32_t d, float *o, float *lse, const float *o_b,
                             const float *lse_b, hipStream_t stream);
+// Checks shared by every call that takes an ra_ring_desc (all but its flags).
+ra_status check_ring_desc(const ra_ring_desc *r);
 hipError_t launch_positions(int32_t kind, int64_t S, int32_t N, int32_t *pos, hipStream_t stream);
 // D = dout . o per row (rows = b * s * n_q, d elements each; esize of dout 2 or 4).
 hipError_t launch_bwd_delta(int64_t rows, int32_t d, int32_t esize, const void *dout,
@@ -82,6 +85,9 @@ hipError_t launch_bwd_delta(int64_t rows, int32_t d, int32_t esize, const void *
 // dq, dk, dv += the gradient contributions of one key block (bf16, d = 128).
 hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 // v [b, s, n_kv, d] -> vt [b, n_kv, d, s]; esize = 2 or 4 bytes per element.
+// out[i] = src[idx[i]], i < n.
+hipError_t launch_gather_i32(const int32_t *src, const int32_t *idx, int32_t *out, int64_t n,
+                             hipStream_t stream);
 hipError_t launch_v_transpose(int32_t b, int64_t s, int32_t n_kv, int32_t d, int32_t esize,
                               const void *v, void *vt, hipStream_t stream);
 

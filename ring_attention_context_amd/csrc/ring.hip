@@ -16,7 +16,11 @@
 // place. Step 0 writes (o, lse) directly (merging into the identity
 // (0, -inf) is a no-op). Later steps merge in the attention kernel's
 // epilogue, or, with RA_RING_UNFUSED_MERGE, write (o_b, lse_b) to the
-// workspace and run the standalone merge kernel.
+// workspace and run the standalone merge kernel. With a document mask the
+// rank's queries' document starts are gathered once; every step's block
+// then applies the same per-query lower bound on key positions, which is
+// what keeps the mask right for any chunk (§8 names this per-step mask as
+// the ring's difficulty).
 #include <climits>
 #include <cmath>
 #include <unordered_map>
@@ -52,12 +56,15 @@ struct Plan {
   int64_t c = 0;
   size_t esize = 0;
   size_t chunk_bytes = 0;   // one K (or V) chunk [b, c, n_kv, d]
-  size_t pos_off = 0, kv_off[2] = {0, 0}, ob_off = 0, lseb_off = 0, total = 0;
+  size_t pos_off = 0, qlo_off = 0, kv_off[2] = {0, 0}, ob_off = 0, lseb_off = 0, total = 0;
   bool fused = true, serialize = false;
   bool vt = false;          // V chunks staged transposed (bf16, c % 8 == 0)
 };
 
-ra_status make_plan(const ra_ring_desc *r, Plan *p) {
+}  // namespace
+
+// Checks shared by every call that takes an ra_ring_desc (flags aside).
+ra_status check_ring_desc(const ra_ring_desc *r) {
   if (!r) return fail(RA_ERR_INVALID_ARG, "ring: desc is NULL");
   if (r->N < 1) return fail(RA_ERR_INVALID_ARG, "ring: N = %d must be >= 1", r->N);
   if (r->rank < 0 || r->rank >= r->N)
@@ -69,9 +76,9 @@ ra_status make_plan(const ra_ring_desc *r, Plan *p) {
     return fail(RA_ERR_INVALID_ARG, "ring: zig-zag needs S %% 2N == 0");
   if (r->kind != RA_PART_CONTIGUOUS && r->kind != RA_PART_ZIGZAG && r->kind != RA_PART_STRIPED)
     return fail(RA_ERR_INVALID_ARG, "ring: unknown partition kind %d", r->kind);
-  if (r->flags & ~(RA_RING_SERIALIZE | RA_RING_UNFUSED_MERGE))
-    return fail(RA_ERR_INVALID_ARG, "ring: unknown flag bits 0x%x", r->flags);
   if (r->reserved != 0) return fail(RA_ERR_INVALID_ARG, "ring: reserved must be 0");
+  if (r->doc_start && r->causal != 1)
+    return fail(RA_ERR_UNSUPPORTED, "ring: a document mask needs causal = 1");
   // Shape / dtype checks shared with the block call.
   ra_attn_desc ad{};
   ad.b = r->b;
@@ -83,8 +90,16 @@ ra_status make_plan(const ra_ring_desc *r, Plan *p) {
   ad.dtype = r->dtype;
   ad.causal = r->causal;
   ad.scale = r->scale;
-  ra_status st = validate_attn(&ad, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return validate_attn(&ad, nullptr, nullptr, nullptr, nullptr, nullptr);
+}
+
+namespace {
+
+ra_status make_plan(const ra_ring_desc *r, Plan *p) {
+  ra_status st = check_ring_desc(r);
   if (st != RA_OK) return st;
+  if (r->flags & ~(RA_RING_SERIALIZE | RA_RING_UNFUSED_MERGE))
+    return fail(RA_ERR_INVALID_ARG, "ring: unknown flag bits 0x%x", r->flags);
   p->c = r->S / r->N;
   p->esize = r->dtype == RA_BF16 ? 2 : 4;
   p->chunk_bytes = static_cast<size_t>(r->b) * p->c * r->n_kv * r->d * p->esize;
@@ -95,6 +110,8 @@ ra_status make_plan(const ra_ring_desc *r, Plan *p) {
   size_t off = 0;
   p->pos_off = off;
   off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
+  p->qlo_off = off;   // the rank's queries' document starts
+  off += align_up(static_cast<size_t>(p->c) * sizeof(int32_t));
   if (r->N > 1 || p->vt) {
     for (int i = 0; i < 2; ++i) {
       p->kv_off[i] = off;
@@ -149,6 +166,21 @@ hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   fill_zero_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
+__global__ void gather_i32_kernel(const int32_t *src, const int32_t *idx, int32_t *out, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    out[i] = src[idx[i]];
+}
+
+hipError_t launch_gather_i32(const int32_t *src, const int32_t *idx, int32_t *out, int64_t n,
+                             hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  gather_i32_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(src, idx, out, n);
   return hipGetLastError();
 }
 
@@ -219,6 +251,13 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
   int32_t *pos = reinterpret_cast<int32_t *>(ws + P.pos_off);
   st = hip_check(ra::launch_positions(r->kind, r->S, r->N, pos, sc), "ra_ring_fwd: positions");
   if (st != RA_OK) return st;
+  int32_t *qlo = reinterpret_cast<int32_t *>(ws + P.qlo_off);
+  if (r->doc_start) {
+    st = hip_check(ra::launch_gather_i32(r->doc_start, pos + static_cast<int64_t>(r->rank) * P.c,
+                                         qlo, P.c, sc),
+                   "ra_ring_fwd: document starts");
+    if (st != RA_OK) return st;
+  }
   if (ev) {
     // The copy stream reads k/v chunks the caller may have just written on `compute`.
     st = hip_check(hipEventRecord(ev->start, sc), "ra_ring_fwd: event record");
@@ -250,6 +289,7 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
   a.scale = r->scale > 0.f ? r->scale : 1.0f / std::sqrt(static_cast<float>(r->d));
   a.causal = r->causal;
   a.q_pos = pos + static_cast<int64_t>(rank) * P.c;
+  a.q_lo = r->doc_start ? qlo : nullptr;
 
   // Fill buffer half (step & 1) with the chunk of `step` (K copied, V copied
   // or transposed); step 0 needs only its V, and only when transposing.
@@ -347,6 +387,8 @@ ra_status make_bwd_plan(const ra_ring_desc *r, BwdPlan *p) {
   if (!r) return fail(RA_ERR_INVALID_ARG, "ring bwd: desc is NULL");
   if (r->flags & ~RA_RING_SERIALIZE)
     return fail(RA_ERR_INVALID_ARG, "ring bwd: only RA_RING_SERIALIZE may be set (0x%x)", r->flags);
+  if (r->doc_start)
+    return fail(RA_ERR_UNSUPPORTED, "ring bwd: no document mask in the backward");
   ra_ring_desc fwd = *r;
   fwd.flags = 0;
   Plan fp;

@@ -85,6 +85,54 @@ class RingCall:
         return [self.events[i].elapsed_time(self.events[i + 1]) for i in range(self.N)]
 
 
+def doc_start_positions(lengths):
+    """int32 host array [S]: for documents of these lengths packed from
+    position 0, the first position of every position's document (the
+    ``doc_start`` input of ra_ring_fwd / ra_allgather_fwd)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    first = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+    return np.repeat(first, lengths).astype(np.int32)
+
+
+class AllGatherCall:
+    """Buffers and descriptor of one rank's all-gather CP forward.
+
+    q: [b, c, n_q, d]; k_chunks, v_chunks: [N, b, c, n_kv, d]; doc_start:
+    optional int32 device tensor [S] (document mask).
+    """
+
+    def __init__(self, q, k_chunks, v_chunks, *, kind, S, N, rank, causal, scale=0.0,
+                 doc_start=None, stream=None):
+        self.q, self.k, self.v = q, k_chunks, v_chunks
+        b, c, n_q, d = q.shape
+        n_kv = k_chunks.shape[3]
+        dtype = _lib.RA_BF16 if q.dtype == torch.bfloat16 else _lib.RA_F32
+        dev = q.device
+        self.stream = stream if stream is not None else torch.cuda.current_stream(dev)
+        self.doc_start = doc_start
+        self.desc, _ = _lib.ring_desc(b=b, n_q=n_q, n_kv=n_kv, d=d, dtype=dtype, causal=causal,
+                                      kind=kind, S=S, N=N, rank=rank, scale=scale,
+                                      doc_start=doc_start)
+        ws = _lib.ra_allgather_workspace_bytes(self.desc)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        self.o = torch.empty((b, c, n_q, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((b, c, n_q), dtype=torch.float32, device=dev)
+
+    def __call__(self, events=None):
+        """Enqueue one all-gather forward; ``events``: optional 2 events recorded
+        around its attention launch."""
+        desc = self.desc
+        keep = None
+        if events is not None:
+            desc = _lib.RingDesc.from_buffer_copy(self.desc)
+            keep = (ctypes.c_void_p * 2)(*[e.cuda_event for e in events])
+            desc.step_events = ctypes.cast(keep, ctypes.c_void_p)
+        _lib.ra_allgather_fwd(desc, self.q, self.k, self.v, self.o, self.lse, self.workspace,
+                              stream=self.stream)
+        del keep
+        return self.o, self.lse
+
+
 def host_to_device(arr, dtype, device="cuda"):
     """Host array -> device tensor; bf16 arrays are given as uint16 bit patterns."""
     if dtype == "bf16":

@@ -14,6 +14,12 @@ Recipe (same for every workload):
 * values are float32 ``standard_normal``; for bfloat16 workloads they are
   rounded to nearest-even, and the oracle sees exactly those bf16 values
   widened to float64.
+
+Document-masked workloads (all-gather CP) also draw document lengths, from
+``Generator(PCG64(seed + 2000))``: log-uniform between S/256 and S/4 tokens,
+packed from position 0 until the sequence is full (the last one cut at S).
+The pages only say that a training sequence packs several documents; this
+mix of short and long documents is the stand-in.
 """
 
 from dataclasses import dataclass, replace
@@ -36,6 +42,7 @@ class Workload:
     causal: bool
     seed: int
     rank: int = 0
+    docs: bool = False  # document mask (all-gather CP workloads)
 
     @property
     def c(self):
@@ -65,6 +72,31 @@ WORKLOADS = {
     "long_1m_zigzag": Workload("long_1m_zigzag", 1, 1048576, 32, "zigzag",
                                8, 1, 128, "bf16", 4.0, True, 5),
 }
+
+# All-gather CP with a document mask: the Llama-3 shapes, zig-zag queries
+# (the 2 x CP chunking), K/V of the whole sequence, packed documents.
+ALLGATHER_WORKLOADS = {
+    "llama3_8b_32k_allgather_docs": Workload("llama3_8b_32k_allgather_docs", 1, 32768, 8,
+                                             "zigzag", 32, 8, 128, "bf16", 1.0, True, 7,
+                                             docs=True),
+    "llama3_70b_128k_allgather_docs": Workload("llama3_70b_128k_allgather_docs", 1, 131072, 8,
+                                               "zigzag", 64, 8, 128, "bf16", 1.0, True, 6,
+                                               docs=True),
+}
+
+
+def doc_lengths(S, seed, lo=None, hi=None):
+    """Seeded document lengths that pack [0, S) (see the module docstring)."""
+    lo = max(1, S // 256) if lo is None else lo
+    hi = max(lo, S // 4) if hi is None else hi
+    rng = np.random.Generator(np.random.PCG64(seed + 2000))
+    out, total = [], 0
+    while total < S:
+        L = int(np.exp(rng.uniform(np.log(lo), np.log(hi + 1))))
+        L = max(1, min(L, S - total))
+        out.append(L)
+        total += L
+    return np.array(out, dtype=np.int64)
 
 
 def bf16_bits(x):

@@ -36,12 +36,13 @@ def test_library_exports_every_declared_function():
 
 
 def test_struct_layouts_match_header():
-    # ra_attn_desc: 4 int32, 2 int64, 2 int32, float, int32, 2 pointers
-    assert ctypes.sizeof(_lib.AttnDesc) == 16 + 16 + 8 + 8 + 16
-    assert _lib.AttnDesc.q_pos.offset == 48
-    # ra_ring_desc: 8 x 4-byte fields, int64 S, 4 int32, pointer
+    # ra_attn_desc: 4 int32, 2 int64, 2 int32, float, int32, 3 pointers
+    assert ctypes.sizeof(_lib.AttnDesc) == 16 + 16 + 8 + 8 + 24
+    assert _lib.AttnDesc.q_pos.offset == 48 and _lib.AttnDesc.q_doc_start.offset == 64
+    # ra_ring_desc: 8 x 4-byte fields, int64 S, 4 int32, 2 pointers
     assert _lib.RingDesc.S.offset == 32 and _lib.RingDesc.step_events.offset == 56
-    assert ctypes.sizeof(_lib.RingDesc) == 64
+    assert _lib.RingDesc.doc_start.offset == 64
+    assert ctypes.sizeof(_lib.RingDesc) == 72
 
 
 @pytest.mark.parametrize("kind", opart.KINDS)
@@ -158,16 +159,18 @@ def test_ring_workspace_bytes():
         return (x + 255) // 256 * 256
     desc = _ring()
     chunk = 1 * 256 * 2 * 128 * 2
-    assert ra.ra_ring_workspace_bytes(desc) == align(1024 * 4) + 2 * 2 * align(chunk)
+    # positions of all ranks, the rank's document starts, the double buffer
+    assert ra.ra_ring_workspace_bytes(desc) == align(1024 * 4) + align(256 * 4) + 2 * 2 * align(chunk)
     unfused = _ring(flags=ra.RA_RING_UNFUSED_MERGE)
     rows = 256 * 8
     assert ra.ra_ring_workspace_bytes(unfused) == (ra.ra_ring_workspace_bytes(desc)
                                                    + align(rows * 128 * 4) + align(rows * 4))
     # N = 1 (one dense pass): bf16 still stages the transposed V chunk
     one_chunk = 1 * 1024 * 2 * 128 * 2
-    assert ra.ra_ring_workspace_bytes(_ring(N=1, rank=0)) == align(1024 * 4) + 2 * 2 * align(one_chunk)
+    assert ra.ra_ring_workspace_bytes(_ring(N=1, rank=0)) == (align(1024 * 4) + align(1024 * 4)
+                                                              + 2 * 2 * align(one_chunk))
     # ... float32 reads K and V in place: no double buffer
-    assert ra.ra_ring_workspace_bytes(_ring(N=1, rank=0, dtype=ra.RA_F32)) == align(1024 * 4)
+    assert ra.ra_ring_workspace_bytes(_ring(N=1, rank=0, dtype=ra.RA_F32)) == 2 * align(1024 * 4)
 
 
 @pytest.mark.parametrize("kw", [
@@ -235,3 +238,52 @@ def test_backward_argument_errors():
     def align(x):
         return (x + 255) // 256 * 256
     assert ra.ra_ring_bwd_workspace_bytes(_ring()) == align(1024 * 4) + align(256 * 8 * 4)
+
+
+def test_document_mask_argument_errors():
+    """The document mask needs the causal rule; the backward takes none."""
+    lib = ra.load_library()
+    desc = _attn_desc(causal=0)
+    desc.q_doc_start = FAKE.value
+    st = lib.ra_block_attn_fwd(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == ra.RA_ERR_UNSUPPORTED, ra.ra_last_error()
+    desc = _attn_desc(causal=1, q_pos=FAKE.value, kv_pos=FAKE.value)
+    desc.q_doc_start = FAKE.value
+    st = lib.ra_block_attn_bwd(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, None)
+    assert st == ra.RA_ERR_UNSUPPORTED
+    ring = _ring()
+    ring.doc_start = FAKE.value
+    ra.ra_ring_workspace_bytes(ring)            # the forward ring takes it
+    ra.ra_allgather_workspace_bytes(ring)
+    with pytest.raises(ra.RingAttnError):
+        ra.ra_ring_bwd_workspace_bytes(ring)
+    ring = _ring(causal=False)
+    ring.doc_start = FAKE.value
+    for fn in (ra.ra_ring_workspace_bytes, ra.ra_allgather_workspace_bytes):
+        with pytest.raises(ra.RingAttnError):
+            fn(ring)
+
+
+def test_allgather_workspace_and_errors():
+    def align(x):
+        return (x + 255) // 256 * 256
+    # S = 1024, N = 4, c = 256; bf16 K/V of the sequence 1024 x 2 x 128 x 2 bytes each
+    full = 1024 * 2 * 128 * 2
+    want = align(1024 * 4) * 2 + align(256 * 4) + 3 * align(full)   # K, V, V^T
+    assert ra.ra_allgather_workspace_bytes(_ring()) == want
+    # float32: no transposed copy
+    full32 = 1024 * 2 * 128 * 4
+    assert ra.ra_allgather_workspace_bytes(_ring(dtype=ra.RA_F32)) == (
+        align(1024 * 4) * 2 + align(256 * 4) + 2 * align(full32))
+    for kw in (dict(flags=ra.RA_RING_SERIALIZE), dict(S=1002), dict(rank=4), dict(d=64)):
+        with pytest.raises(ra.RingAttnError):
+            ra.ra_allgather_workspace_bytes(_ring(**kw))
+    lib = ra.load_library()
+    desc = _ring()
+    need = ra.ra_allgather_workspace_bytes(desc)
+    st = lib.ra_allgather_fwd(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                              None)
+    assert st == ra.RA_ERR_INVALID_ARG and "workspace" in ra.ra_last_error()
+    st = lib.ra_allgather_fwd(ctypes.byref(desc), FAKE, None, FAKE, FAKE, FAKE, FAKE, need, None)
+    assert st == ra.RA_ERR_INVALID_ARG

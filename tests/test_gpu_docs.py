@@ -1,0 +1,192 @@
+"""GPU parity of the document mask and of all-gather context parallelism
+("Context Parallelism and Ring Attention" §8) against the fp64 oracle
+(oracle/documents.py), through the C ABI: ra_block_attn_fwd with
+q_doc_start, ra_allgather_fwd, and ra_ring_fwd with doc_start.
+
+Tolerances are the forward's (tests/gpu_util.py): O max-abs <= 1e-2 (bf16)
+or 1e-5 (f32), lse <= 2e-3, -inf rows exactly -inf with o = 0."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import ring_attention_context_amd as ra
+import synth
+from gpu_util import compare, rand_inputs, require_gpu, to_device
+from oracle import documents as odoc
+from oracle import partition as opart
+from ring_attention_context_amd import runner
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _seed(case):
+    return zlib.crc32(str(case).encode())
+
+
+def _lengths(rng, span, mean):
+    out, tot = [], 0
+    while tot < span:
+        L = int(min(span - tot, max(1, rng.geometric(1.0 / mean))))
+        out.append(L)
+        tot += L
+    return np.array(out)
+
+
+BLOCK_CASES = [
+    # b, s_q, s_kv, n_q, n_kv, dtype, v_transposed, mean document length
+    (1, 128, 256, 8, 1, "bf16", False, 40),
+    (1, 200, 333, 8, 2, "bf16", False, 25),       # ragged query and key tails
+    (2, 160, 512, 8, 4, "bf16", True, 60),        # V^T layout, batch 2
+    (1, 96, 640, 4, 4, "bf16", True, 1),          # every token its own document
+    (1, 257, 704, 8, 8, "bf16", True, 5000),      # one document: plain causal
+    (1, 70, 190, 4, 2, "f32", False, 30),
+    (1, 33, 64, 2, 1, "f32", False, 1),
+]
+
+
+@pytest.mark.parametrize("case", BLOCK_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_block_doc_mask_matches_oracle(case):
+    b, s_q, s_kv, n_q, n_kv, dt, vt, mean = case
+    print(f"block doc mask {case}", flush=True)
+    rng = np.random.default_rng(_seed(case))
+    d = 128
+    span = 2 * (s_q + s_kv) + 8
+    lengths = _lengths(rng, span, mean)
+    ids = odoc.doc_ids_from_lengths(lengths)
+    starts = runner.doc_start_positions(lengths)
+    q_pos = np.sort(rng.choice(span, s_q, replace=False)).astype(np.int32)
+    kv_pos = np.sort(rng.choice(span, s_kv, replace=False)).astype(np.int32)
+    q, q64 = rand_inputs((b, s_q, n_q, d), dt, rng)
+    k, k64 = rand_inputs((b, s_kv, n_kv, d), dt, rng)
+    v, v64 = rand_inputs((b, s_kv, n_kv, d), dt, rng)
+    tq, tk, tv = to_device(q, dt), to_device(k, dt), to_device(v, dt)
+    if vt:
+        tvt = torch.empty((b, n_kv, d, s_kv), dtype=tv.dtype, device="cuda")
+        ra.ra_v_transpose(tv, tvt)
+        tv = tvt
+    o = torch.full((b, s_q, n_q, d), float("nan"), device="cuda")
+    lse = torch.full((b, s_q, n_q), float("nan"), device="cuda")
+    ra.ra_block_attn_fwd(tq, tk, tv, o, lse, causal=True, scale=0.0, v_transposed=vt,
+                         q_pos=torch.from_numpy(q_pos).cuda(),
+                         kv_pos=torch.from_numpy(kv_pos).cuda(),
+                         q_doc_start=torch.from_numpy(starts[q_pos]).cuda())
+    torch.cuda.synchronize()
+    vis = odoc.visible_docs(q_pos, kv_pos, ids, True)
+    ro, rl = odoc.masked_attention(q64, k64, v64, vis, np.float32(1 / np.sqrt(d)))
+    do, dl = compare(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, dt, str(case))
+    print(f"  max|dO| {do:.2e} max|dlse| {dl:.2e}; rows without keys: "
+          f"{int(np.isneginf(rl).sum())}", flush=True)
+
+
+def _allgather_case(kind, N, S, n_q, n_kv, dt, rank, mean, docs=True, seed=0):
+    rng = np.random.default_rng(seed)
+    d = 128
+    lengths = _lengths(rng, S, mean)
+    k, k64 = rand_inputs((1, S, n_kv, d), dt, rng)
+    v, v64 = rand_inputs((1, S, n_kv, d), dt, rng)
+    c = S // N
+    q, q64 = rand_inputs((1, c, n_q, d), dt, rng)
+    tq = to_device(q, dt)
+    kc = runner.chunk_kv(to_device(k, dt), kind, N)
+    vc = runner.chunk_kv(to_device(v, dt), kind, N)
+    ds = torch.from_numpy(runner.doc_start_positions(lengths)).cuda() if docs else None
+    ids = odoc.doc_ids_from_lengths(lengths if docs else [S])
+    return tq, kc, vc, ds, q64, k64, v64, ids
+
+
+AG_CASES = [
+    # kind, N, S, n_q, n_kv, dtype, rank, mean document length, docs
+    ("zigzag", 4, 1536, 8, 2, "bf16", 0, 90, True),
+    ("zigzag", 4, 1536, 8, 2, "bf16", 3, 90, True),
+    ("striped", 4, 1024, 8, 1, "bf16", 1, 50, True),
+    ("contiguous", 2, 768, 4, 4, "bf16", 1, 300, True),
+    ("zigzag", 8, 2048, 16, 2, "bf16", 5, 1, True),      # one token per document
+    ("zigzag", 4, 1024, 8, 2, "bf16", 2, 0, False),      # no documents: plain causal
+    ("zigzag", 2, 300, 4, 2, "bf16", 1, 40, True),       # c = 150: V kept row-major
+    ("zigzag", 4, 256, 2, 1, "f32", 3, 20, True),
+]
+
+
+@pytest.mark.parametrize("case", AG_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_allgather_matches_oracle(case):
+    kind, N, S, n_q, n_kv, dt, rank, mean, docs = case
+    print(f"all-gather {case}", flush=True)
+    tq, kc, vc, ds, q64, k64, v64, ids = _allgather_case(kind, N, S, n_q, n_kv, dt, rank,
+                                                         max(mean, 1), docs, _seed(case))
+    call = runner.AllGatherCall(tq, kc, vc, kind=kind, S=S, N=N, rank=rank, causal=True,
+                                doc_start=ds)
+    call.o.fill_(float("nan"))
+    call.workspace.fill_(0xFF)
+    o, lse = call()
+    torch.cuda.synchronize()
+    kc64 = np.stack([k64[:, opart.partition_map(kind, S, N, j)] for j in range(N)])
+    vc64 = np.stack([v64[:, opart.partition_map(kind, S, N, j)] for j in range(N)])
+    ro, rl = odoc.allgather_attention(q64, kc64, vc64, kind, S, N, rank, ids, True,
+                                      np.float32(1 / np.sqrt(128)))
+    do, dl = compare(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, dt, str(case))
+    print(f"  max|dO| {do:.2e} max|dlse| {dl:.2e}", flush=True)
+
+
+RING_DOC_CASES = [("zigzag", 4, 1536, 0), ("zigzag", 4, 1536, 2), ("striped", 4, 1024, 3),
+                  ("contiguous", 4, 1024, 3)]
+
+
+@pytest.mark.parametrize("case", RING_DOC_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_ring_with_doc_mask_matches_oracle(case):
+    """The ring applies the same per-query lower bound at every step; the
+    merged result must equal the document-masked definition."""
+    kind, N, S, rank = case
+    print(f"ring doc mask {case}", flush=True)
+    tq, kc, vc, ds, q64, k64, v64, ids = _allgather_case(kind, N, S, 8, 2, "bf16", rank, 70,
+                                                         True, _seed(case))
+    call = runner.RingCall(tq, kc, vc, kind=kind, S=S, N=N, rank=rank, causal=True)
+    desc, _ = ra.ring_desc(b=1, n_q=8, n_kv=2, d=128, dtype=ra.RA_BF16, causal=True, kind=kind,
+                           S=S, N=N, rank=rank, doc_start=ds)
+    ws = torch.empty(ra.ra_ring_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    ra.ra_ring_fwd(desc, tq, kc, vc, call.o, call.lse, ws, compute=call.compute, copy=call.copy)
+    torch.cuda.synchronize()
+    q_pos = opart.partition_map(kind, S, N, rank)
+    ro, rl = odoc.rows_attention_docs(q64, k64, v64, q_pos, ids, True,
+                                      np.float32(1 / np.sqrt(128)))
+    do, dl = compare(call.o.cpu().numpy(), call.lse.cpu().numpy(), ro, rl, "bf16", str(case))
+    print(f"  max|dO| {do:.2e} max|dlse| {dl:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", sorted(synth.ALLGATHER_WORKLOADS))
+def test_allgather_workload_sampled_rows(name):
+    """Full-size all-gather run (every row on the GPU); 128 sampled rows x all
+    heads compared element by element with the oracle."""
+    w = synth.ALLGATHER_WORKLOADS[name]
+    print(f"workload {w.name}", flush=True)
+    inp = synth.draw(w)
+    lengths = synth.doc_lengths(w.S, w.seed)
+    q, kc, vc = runner.ring_inputs(inp.q, inp.k, inp.v, w.dtype, w.kind, w.N, "cuda")
+    ds = torch.from_numpy(runner.doc_start_positions(lengths)).cuda()
+    call = runner.AllGatherCall(q, kc, vc, kind=w.kind, S=w.S, N=w.N, rank=w.rank,
+                                causal=True, scale=w.scale, doc_start=ds)
+    o, lse = call()
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    del call, q, kc, vc
+    torch.cuda.empty_cache()
+    c = w.c
+    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)
+    ids = odoc.doc_ids_from_lengths(lengths)
+    # rows at document starts inside the shard, the chunk boundaries, and seeded rows
+    firsts = np.searchsorted(q_pos, np.concatenate([[0], np.cumsum(lengths)[:-1]]))
+    rows = synth.sample_rows(c, 128, w.seed,
+                             must=[0, 1, c // 2 - 1, c // 2, c - 1, *firsts[:24].tolist()])
+    ro, rl = odoc.rows_attention_docs(inp.q64[:, rows], inp.k64, inp.v64, q_pos[rows], ids,
+                                      True, w.scale)
+    do, dl = compare(o[:, rows], lse[:, rows], ro, rl, w.dtype, w.name)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    print(f"  rows {len(rows)} max|dO| {do:.2e} max|dlse| {dl:.2e}", flush=True)
