@@ -12,6 +12,13 @@ the reason this form suits Llama 3: one training sequence packs several
 documents and no token may attend across a document boundary; with the whole
 K/V at hand the rank applies that mask directly on original positions.
 
+The backward of all-gather CP (§8: a reduce-scatter of dK, dV) follows the
+backward paragraph of §3 with the same mask: the gradients of L = sum(do * o)
+by the chain rule (as in :mod:`oracle.backward`), the rank's dK, dV of the
+whole sequence then cut back into the N chunks (this rank's share of the
+reduce-scatter's input; summing every rank's shares gives the sequence's
+dK, dV).
+
 Readings where the page stops:
 
 * documents are contiguous runs of positions that tile [0, S); a document id
@@ -138,3 +145,52 @@ def doc_visible_pairs(q_pos, doc_ids, causal=True):
         return int((q_pos - start[q_pos] + 1).sum())
     lengths = np.bincount(doc_ids)
     return int(lengths[doc_ids[q_pos]].sum())
+
+
+def masked_attention_bwd(q, k, v, do, vis, scale):
+    """Gradients of L = sum(do * o) for o = softmax(x) v over an explicit
+    visibility matrix vis [c, s] (x = scale q . k), by the chain rule:
+    p = softmax(x), D = rowsum(do * o), dv = p^T do, dp = do v^T,
+    dx = p * (dp - D), dq = scale dx k, dk = scale dx^T q. Query head h reads
+    key/value head h // (n_q // n_kv); a key/value head sums its group's
+    contributions. Rows with no visible key contribute nothing."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    b, c, n_q, d = q.shape
+    n_kv = k.shape[2]
+    g = n_q // n_kv
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    if c == 0 or k.shape[1] == 0:
+        return dq, dk, dv
+    has_key = vis.any(axis=1)
+    for bi in range(b):
+        for h in range(n_q):
+            kvh = h // g
+            x = np.where(vis, scale * (q[bi, :, h, :] @ k[bi, :, kvh, :].T), -np.inf)
+            m = np.where(has_key, x.max(axis=1), 0.0)
+            e = np.exp(x - m[:, None])
+            p = e / np.where(has_key, e.sum(axis=1), 1.0)[:, None]
+            o = p @ v[bi, :, kvh, :]
+            D = np.sum(do[bi, :, h, :] * o, axis=1)
+            dv[bi, :, kvh, :] += p.T @ do[bi, :, h, :]
+            dx = p * (do[bi, :, h, :] @ v[bi, :, kvh, :].T - D[:, None])
+            dq[bi, :, h, :] = scale * (dx @ k[bi, :, kvh, :])
+            dk[bi, :, kvh, :] += scale * (dx.T @ q[bi, :, h, :])
+    return dq, dk, dv
+
+
+def allgather_attention_bwd(q, k_chunks, v_chunks, do, kind, S, N, rank, doc_ids, causal,
+                            scale):
+    """Backward of one rank of all-gather CP (§8) under the document mask.
+
+    q, do: [b, c, n_q, d] (the rank's queries, local order); k_chunks,
+    v_chunks: [N, b, c, n_kv, d]. Returns dq [b, c, n_q, d] and dk_chunks,
+    dv_chunks [N, b, c, n_kv, d]: this rank's contribution to every chunk's
+    dK, dV, chunk j in rank j's local order (what the reduce-scatter sums)."""
+    k = allgather_kv(k_chunks, kind, S, N)
+    v = allgather_kv(v_chunks, kind, S, N)
+    q_pos = partition_map(kind, S, N, rank)
+    vis = visible_docs(q_pos, np.arange(S), doc_ids, causal)
+    dq, dk, dv = masked_attention_bwd(q, k, v, do, vis, scale)
+    dk_chunks = np.stack([dk[:, partition_map(kind, S, N, j)] for j in range(N)])
+    dv_chunks = np.stack([dv[:, partition_map(kind, S, N, j)] for j in range(N)])
+    return dq, dk_chunks, dv_chunks

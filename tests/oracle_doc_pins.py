@@ -25,7 +25,13 @@ What pins what ("Context Parallelism and Ring Attention", §8 all-gather CP):
   rank's all-gather result, put back at its positions, reassembles the
   whole sequence's document-masked attention;
 * pair counts: brute-force counts of the mask, and the closed form
-  sum_docs L (L + 1) / 2 over a whole sequence.
+  sum_docs L (L + 1) / 2 over a whole sequence;
+* backward: central finite differences of L = sum(do * o) through the
+  masked forward; per-document independence against the plain backward
+  oracle (oracle/backward.py, pinned on its own) run on each document
+  alone; and every rank's all-gather backward, its dq put back at its
+  positions and its chunk contributions summed, equals the whole sequence's
+  document-masked gradients.
 """
 
 import math
@@ -162,3 +168,84 @@ def pin_docs_pair_counts(A):
 DOC_PINS = [pin_docs_independent_documents, pin_docs_one_document, pin_docs_singletons,
             pin_docs_brute_force, pin_docs_allgather_inverse, pin_docs_ranks_reassemble,
             pin_docs_pair_counts]
+
+
+def pin_docs_bwd_finite_differences(A):
+    rng = np.random.default_rng(208)
+    lengths = [3, 1, 4]
+    S = sum(lengths)
+    ids = A.doc_ids_from_lengths(lengths)
+    q_pos = np.array([0, 2, 3, 5, 7])
+    q = rng.standard_normal((1, 5, 2, 3))
+    k = rng.standard_normal((1, S, 1, 3))
+    v = rng.standard_normal((1, S, 1, 3))
+    do = rng.standard_normal((1, 5, 2, 3))
+    vis = A.visible_docs(q_pos, np.arange(S), ids, True)
+    dq, dk, dv = A.masked_attention_bwd(q, k, v, do, vis, 0.8)
+
+    def loss(qq, kk, vv):
+        o, _ = A.masked_attention(qq, kk, vv, vis, 0.8)
+        return float(np.sum(do * o))
+
+    h = 1e-6
+    for which, (x, g) in enumerate(((q, dq), (k, dk), (v, dv))):
+        for idx in np.ndindex(x.shape):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += h
+            lp = loss(*args)
+            args[which][idx] -= 2 * h
+            lm = loss(*args)
+            assert abs((lp - lm) / (2 * h) - g[idx]) < 1e-6, (which, idx)
+
+
+def pin_docs_bwd_independent_documents(A):
+    rng = np.random.default_rng(209)
+    lengths = [6, 1, 9, 4]
+    S = sum(lengths)
+    ids = A.doc_ids_from_lengths(lengths)
+    q, k, v = _qkv(rng, 1, S, S, 4, 2, 5)
+    do = rng.standard_normal(q.shape)
+    pos = np.arange(S)
+    dq, dk, dv = A.masked_attention_bwd(q, k, v, do, A.visible_docs(pos, pos, ids, True), 0.35)
+    lo = 0
+    for L in lengths:
+        sl = slice(lo, lo + L)
+        rel = np.arange(L)
+        rq, rk, rv = A.naive_attention_bwd(q[:, sl], k[:, sl], v[:, sl], do[:, sl], rel, rel,
+                                           True, 0.35)
+        for got, want in ((dq[:, sl], rq), (dk[:, sl], rk), (dv[:, sl], rv)):
+            assert np.max(np.abs(got - want)) < 1e-12, f"document at {lo}"
+        lo += L
+
+
+def pin_docs_bwd_ranks_reassemble(A):
+    rng = np.random.default_rng(210)
+    lengths = [5, 11, 2, 14]
+    S = sum(lengths)            # 32 = 2 * 4 * 4
+    ids = A.doc_ids_from_lengths(lengths)
+    q_all, k, v = _qkv(rng, 1, S, S, 4, 2, 3)
+    do_all = rng.standard_normal(q_all.shape)
+    pos = np.arange(S)
+    want = A.masked_attention_bwd(q_all, k, v, do_all, A.visible_docs(pos, pos, ids, True), 0.5)
+    for kind in ("contiguous", "zigzag", "striped"):
+        N = 4
+        kc = np.stack([k[:, A.partition_map(kind, S, N, j)] for j in range(N)])
+        vc = np.stack([v[:, A.partition_map(kind, S, N, j)] for j in range(N)])
+        dq = np.zeros_like(q_all)
+        dk = np.zeros_like(k)
+        dv = np.zeros_like(v)
+        for rank in range(N):
+            qp = A.partition_map(kind, S, N, rank)
+            g_q, g_kc, g_vc = A.allgather_attention_bwd(q_all[:, qp], kc, vc, do_all[:, qp], kind,
+                                                        S, N, rank, ids, True, 0.5)
+            dq[:, qp] = g_q
+            for j in range(N):
+                pj = A.partition_map(kind, S, N, j)
+                dk[:, pj] += g_kc[j]
+                dv[:, pj] += g_vc[j]
+        for got, w, name in ((dq, want[0], "dq"), (dk, want[1], "dk"), (dv, want[2], "dv")):
+            assert np.max(np.abs(got - w)) < 1e-12, f"{kind} {name}"
+
+
+DOC_PINS += [pin_docs_bwd_finite_differences, pin_docs_bwd_independent_documents,
+             pin_docs_bwd_ranks_reassemble]

@@ -8,15 +8,17 @@ import numpy as np
 import pytest
 
 import oracle_doc_pins as pins
-from oracle import attention, documents, partition
+from oracle import attention, backward, documents, partition
 
 
 def namespace():
     """Late-bound view of the oracle: monkeypatched functions are seen."""
     names = ["doc_ids_from_lengths", "doc_start", "visible_docs", "masked_attention",
-             "allgather_kv", "allgather_attention", "doc_visible_pairs"]
+             "allgather_kv", "allgather_attention", "doc_visible_pairs",
+             "masked_attention_bwd", "allgather_attention_bwd"]
     ns = {n: (lambda n: lambda *a: getattr(documents, n)(*a))(n) for n in names}
     ns["naive_attention"] = lambda *a: attention.naive_attention(*a)
+    ns["naive_attention_bwd"] = lambda *a: backward.naive_attention_bwd(*a)
     ns["partition_map"] = lambda *a: partition.partition_map(*a)
     return types.SimpleNamespace(**ns)
 
@@ -64,7 +66,46 @@ def masked_no_scale(q, k, v, vis, scale):
     return real_masked(q, k, v, vis, 1.0)
 
 
+real_masked_bwd = documents.masked_attention_bwd
+
+
+def masked_bwd_no_delta(q, k, v, do, vis, scale):
+    """dx = p * dp (the - D term dropped)."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    n_q, n_kv = q.shape[2], k.shape[2]
+    g = n_q // n_kv
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for bi in range(q.shape[0]):
+        for h in range(n_q):
+            kvh = h // g
+            x = np.where(vis, scale * (q[bi, :, h] @ k[bi, :, kvh].T), -np.inf)
+            m = np.where(vis.any(axis=1), x.max(axis=1), 0.0)
+            e = np.exp(x - m[:, None])
+            p = e / np.maximum(e.sum(axis=1, keepdims=True), 1e-300)
+            dv[bi, :, kvh] += p.T @ do[bi, :, h]
+            dx = p * (do[bi, :, h] @ v[bi, :, kvh].T)
+            dq[bi, :, h] = scale * dx @ k[bi, :, kvh]
+            dk[bi, :, kvh] += scale * dx.T @ q[bi, :, h]
+    return dq, dk, dv
+
+
+def masked_bwd_dk_unscaled(q, k, v, do, vis, scale):
+    dq, dk, dv = real_masked_bwd(q, k, v, do, vis, scale)
+    return dq, dk / scale, dv
+
+
+real_ag_bwd = documents.allgather_attention_bwd
+
+
+def ag_bwd_chunks_rolled(*a):
+    dq, dkc, dvc = real_ag_bwd(*a)
+    return dq, np.roll(dkc, 1, axis=0), np.roll(dvc, 1, axis=0)
+
+
 MUTANTS = {
+    "masked_bwd_no_delta": ("masked_attention_bwd", masked_bwd_no_delta),
+    "masked_bwd_dk_unscaled": ("masked_attention_bwd", masked_bwd_dk_unscaled),
+    "ag_bwd_chunks_rolled": ("allgather_attention_bwd", ag_bwd_chunks_rolled),
     "visible_earlier_docs": ("visible_docs", visible_earlier_docs),
     "visible_no_docs": ("visible_docs", visible_no_docs),
     "visible_no_causal": ("visible_docs", visible_no_causal),
