@@ -20,7 +20,8 @@ With --allgather the step is one ``ra_allgather_fwd`` call (all-gather
 context parallelism: K/V of every rank gathered into the sequence, one pass
 of the rank's queries over it) under a document mask, on the Llama-3-70B
 shape at 128K with packed documents; visible pairs are those inside the
-query's document and at or before it.
+query's document and at or before it. --allgather --backward times
+``ra_allgather_bwd`` on the same workload (10 * d flop per visible pair).
 
 Prints progress on stderr and ONE JSON line on stdout.
 """
@@ -43,6 +44,8 @@ METRIC_BWD = ("causal-adjusted attention backward TFLOP/s per rank shard (10*d f
               "pair and head) + % of bf16 MFMA peak")
 METRIC_AG = ("document-masked causal attention TFLOP/s per rank shard, all-gather CP "
              "(4*d flop per visible pair and head) + % of bf16 MFMA peak")
+METRIC_AG_BWD = ("document-masked causal attention backward TFLOP/s per rank shard, all-gather "
+                 "CP (10*d flop per visible pair and head) + % of bf16 MFMA peak")
 
 
 def log(msg):
@@ -156,9 +159,10 @@ def doc_pairs(q_pos, doc_start):
     return int((q_pos - doc_start[q_pos] + 1).sum())
 
 
-def cpu_baseline_docs(w, lengths, seconds_hint=15.0):
+def cpu_baseline_docs(w, lengths, seconds_hint=15.0, backward=False):
     """Time the fp64 document-mask oracle (as it stands) on a bounded sample of
-    query rows x all heads against the whole sequence."""
+    query rows x all heads against the whole sequence (the backward oracle
+    with ``backward``: the sampled rows' gradients)."""
     import numpy as np
     import synth
     from oracle import documents as odoc
@@ -168,7 +172,7 @@ def cpu_baseline_docs(w, lengths, seconds_hint=15.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    per_row = 4 * w.d * w.n_q * w.S          # the oracle scores every key, then masks
+    per_row = (10 if backward else 4) * w.d * w.n_q * w.S   # every key scored, then masked
     rows_n = int(max(8, min(512, seconds_hint * 2.5e10 / per_row)))
     rows = synth.sample_rows(w.c, rows_n, w.seed)
     inp = synth.draw(w, q_rows=rows)
@@ -176,13 +180,22 @@ def cpu_baseline_docs(w, lengths, seconds_hint=15.0):
     ids = odoc.doc_ids_from_lengths(lengths)
     k64, v64, q64 = inp.k64, inp.v64, inp.q64
     t0 = time.perf_counter()
-    odoc.rows_attention_docs(q64, k64, v64, q_pos, ids, True, w.scale)
+    if backward:
+        rng = np.random.default_rng(w.seed + 1000)
+        do64 = synth.bf16_to_f32(synth.bf16_bits(
+            rng.standard_normal(q64.shape, dtype=np.float32))).astype(np.float64)
+        vis = odoc.visible_docs(q_pos, np.arange(w.S), ids, True)
+        odoc.masked_attention_bwd(q64, k64, v64, do64, vis, w.scale)
+    else:
+        odoc.rows_attention_docs(q64, k64, v64, q_pos, ids, True, w.scale)
     t = time.perf_counter() - t0
     pairs = odoc.doc_visible_pairs(q_pos, ids, True)
-    flops = 4 * w.b * w.n_q * w.d * pairs
+    flops = (10 if backward else 4) * w.b * w.n_q * w.d * pairs
+    what = "backward by the chain rule" if backward else "softmax attention"
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {w.c} query rows x {w.n_q} heads vs all {w.S} keys "
-                      f"under the document mask (fp64 NumPy, {t:.1f} s, {pairs} visible pairs)",
+                      f"under the document mask (fp64 NumPy {what}, {t:.1f} s, "
+                      f"{pairs} visible pairs)",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -206,6 +219,9 @@ def run_allgather(args, w, dev, props):
     call = runner.AllGatherCall(q, kc, vc, kind=w.kind, S=w.S, N=w.N, rank=w.rank,
                                 causal=True, scale=w.scale, doc_start=ds, stream=stream)
     pairs = doc_pairs(ra_partition(w.kind, w.S, w.N, w.rank), starts)
+    if args.backward:
+        run_allgather_backward(args, w, q, kc, vc, ds, call, stream, pairs, lengths, props)
+        return
     total_flops = 4 * w.b * w.n_q * w.d * pairs
     for _ in range(args.warmup):
         call()
@@ -252,6 +268,79 @@ def run_allgather(args, w, dev, props):
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "kernel": "attn_bf16_kernel (one launch per call)",
                      "avg_launch_ms": round(float(kern.mean()), 4), "launches": len(kern),
+                     "flops_per_launch_avg": total_flops},
+        "cpu_baseline": cpu,
+        "device": props.name,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_allgather_backward(args, w, q, kc, vc, ds, call, stream, pairs, lengths, props):
+    """Time ra_allgather_bwd (one rank's all-gather CP backward, document mask)."""
+    import numpy as np
+    import torch
+    import synth
+    import ring_attention_context_amd as ra
+    from ring_attention_context_amd import runner
+    dev = q.device
+    o, lse = call()                      # the rank's o and lse (forward, untimed)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed + 1000)
+    do = runner.host_to_device(synth.bf16_bits(rng.standard_normal(tuple(q.shape),
+                                                                   dtype=np.float32)),
+                               "bf16", dev)
+    dq = torch.empty(tuple(q.shape), dtype=torch.float32, device=dev)
+    dkc = torch.zeros(tuple(kc.shape), dtype=torch.float32, device=dev)
+    dvc = torch.zeros_like(dkc)
+    desc, _ = ra.ring_desc(b=w.b, n_q=w.n_q, n_kv=w.n_kv, d=w.d, dtype=ra.RA_BF16, causal=True,
+                           kind=w.kind, S=w.S, N=w.N, rank=w.rank, scale=w.scale, doc_start=ds)
+    ws = torch.empty(ra.ra_allgather_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    total_flops = 10 * w.b * w.n_q * w.d * pairs
+    for _ in range(args.warmup):
+        ra.ra_allgather_bwd(desc, q, kc, vc, o, lse, do, dq, dkc, dvc, ws, stream)
+    torch.cuda.synchronize()
+    log(f"[bench-ag-bwd] warmup {args.warmup} done")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        ra.ra_allgather_bwd(desc, q, kc, vc, o, lse, do, dq, dkc, dvc, ws, stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    ev_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    log(f"[bench-ag-bwd] {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s "
+        f"(events {ev_ms:.3f} ms per call)")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_docs(w, lengths, args.cpu_seconds,
+                                                              backward=True)
+    out = {
+        "metric": METRIC_AG_BWD,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), bf16 round-to-nearest-even; seeded document lengths)",
+        "config": {"workload": w.name, "pass": "backward, all-gather CP", "b": w.b, "S": w.S,
+                   "N": w.N, "rank": w.rank, "map": w.kind, "n_q": w.n_q, "n_kv": w.n_kv,
+                   "d": w.d, "causal": True, "documents": len(lengths), "scale": w.scale,
+                   "queries_per_rank": w.c, "visible_pairs": pairs},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(total_flops / (ev_ms * 1e-3) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(total_flops / (ev_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "whole ra_allgather_bwd call (gathers, dq and dK/dV kernels, "
+                               "scatter)",
+                     "avg_launch_ms": round(ev_ms, 4), "launches": len(evs),
                      "flops_per_launch_avg": total_flops},
         "cpu_baseline": cpu,
         "device": props.name,

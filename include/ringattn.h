@@ -176,8 +176,9 @@ typedef struct ra_ring_desc {
                                of p's document (0 <= doc_start[p] <= p,
                                non-decreasing: documents are runs of
                                consecutive positions). A key is visible only
-                               within the query's document. Needs causal = 1;
-                               ra_ring_fwd and ra_allgather_fwd only.       */
+                               within the query's document. Needs causal = 1.
+                               Taken by the ring and all-gather calls, both
+                               passes.                                       */
 } ra_ring_desc;
 
 /* Workspace bytes ra_ring_fwd needs for *desc (same validation as the call). */
@@ -263,13 +264,14 @@ ra_status ra_block_attn_bwd(const ra_attn_desc *desc, const void *q, const void 
                             const void *v, const void *dout, const float *lse,
                             const float *delta, float *dq, float *dk, float *dv, void *stream);
 
-/* Workspace bytes ra_ring_bwd needs: positions (S int32) and D (b*c*n_q floats). */
+/* Workspace bytes ra_ring_bwd needs: positions (S int32), D (b*c*n_q floats)
+ * and the queries' document starts (c int32). */
 ra_status ra_ring_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
 
 /*
  * ra_ring_bwd -- the ring backward for rank `rank`, replayed on one GPU.
  * desc: as for ra_ring_fwd (bf16, d = 128; flags 0 or RA_RING_SERIALIZE,
- * which changes nothing here: one stream; doc_start must be NULL).
+ * which changes nothing here: one stream; doc_start optional).
  * q, dout: device [b, c, n_q, d] bf16, the rank's tokens in its local order;
  * o, lse: device float32 [b, c, n_q, d] and [b, c, n_q], the rank's forward
  * outputs (global o and lse); k_chunks, v_chunks: device [N, b, c, n_kv, d]
@@ -286,6 +288,28 @@ ra_status ra_ring_bwd(const ra_ring_desc *desc, const void *q, const void *k_chu
                       const void *v_chunks, const float *o, const float *lse, const void *dout,
                       float *dq, float *dk_chunks, float *dv_chunks, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/* Workspace bytes ra_allgather_bwd needs for *desc (same validation as the call). */
+ra_status ra_allgather_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
+
+/*
+ * ra_allgather_bwd -- the backward of all-gather context parallelism
+ * ("Context Parallelism and Ring Attention" §8: K/V all-gathered before
+ * attention, dK/dV reduce-scattered after) for rank `rank`, replayed on one
+ * GPU, with the optional document mask of desc->doc_start.
+ * desc: as for ra_allgather_fwd (bf16, d = 128). Arguments as for
+ * ra_ring_bwd: dq is overwritten with the rank's dQ; this rank's
+ * contribution to chunk j's dK, dV is ADDED to slot j of dk_chunks /
+ * dv_chunks (the reduce-scatter's input: summing every rank's calls on the
+ * same slots gives each chunk's dK, dV). workspace: >=
+ * ra_allgather_bwd_workspace_bytes(): positions, D, document starts, the
+ * gathered K and V of the sequence (bf16) and its dK, dV (float32). One
+ * stream; step_events unused.
+ */
+ra_status ra_allgather_bwd(const ra_ring_desc *desc, const void *q, const void *k_chunks,
+                           const void *v_chunks, const float *o, const float *lse,
+                           const void *dout, float *dq, float *dk_chunks, float *dv_chunks,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static text of a status code. */
 const char *ra_status_str(int32_t status);

@@ -25,6 +25,8 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     RingAttnError,
     load_library,
+    ra_allgather_bwd,
+    ra_allgather_bwd_workspace_bytes,
     ra_allgather_fwd,
     ra_allgather_workspace_bytes,
     ra_attn_bwd_delta,

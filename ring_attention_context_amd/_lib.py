@@ -25,7 +25,8 @@ KINDS = {"contiguous": RA_PART_CONTIGUOUS, "zigzag": RA_PART_ZIGZAG, "striped": 
 EXPORTED = ("ra_partition", "ra_block_attn_fwd", "ra_v_transpose", "ra_lse_merge",
             "ra_ring_workspace_bytes", "ra_ring_fwd", "ra_attn_bwd_delta", "ra_block_attn_bwd",
             "ra_ring_bwd_workspace_bytes", "ra_ring_bwd", "ra_allgather_workspace_bytes",
-            "ra_allgather_fwd", "ra_status_str", "ra_last_error")
+            "ra_allgather_fwd", "ra_allgather_bwd_workspace_bytes", "ra_allgather_bwd",
+            "ra_status_str", "ra_last_error")
 
 
 class RingAttnError(RuntimeError):
@@ -83,10 +84,15 @@ def load_library(path=None):
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.ra_allgather_fwd.argtypes = [ctypes.POINTER(RingDesc), vp, vp, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
+    lib.ra_allgather_bwd_workspace_bytes.argtypes = [ctypes.POINTER(RingDesc),
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.ra_allgather_bwd.argtypes = [ctypes.POINTER(RingDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, vp, ctypes.c_size_t, vp]
     for name in ("ra_partition", "ra_block_attn_fwd", "ra_v_transpose", "ra_lse_merge",
                  "ra_ring_workspace_bytes", "ra_ring_fwd", "ra_attn_bwd_delta",
                  "ra_block_attn_bwd", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd",
-                 "ra_allgather_workspace_bytes", "ra_allgather_fwd"):
+                 "ra_allgather_workspace_bytes", "ra_allgather_fwd",
+                 "ra_allgather_bwd_workspace_bytes", "ra_allgather_bwd"):
         getattr(lib, name).restype = i32
     lib.ra_status_str.argtypes = [i32]
     lib.ra_status_str.restype = ctypes.c_char_p
@@ -200,15 +206,17 @@ def ra_attn_bwd_delta(dout, o, delta, stream=None):
 
 
 def ra_block_attn_bwd(q, k, v, dout, lse, delta, dq, dk, dv, *, causal, scale=0.0, q_pos=None,
-                      kv_pos=None, stream=None):
+                      kv_pos=None, q_doc_start=None, stream=None):
     """dq, dk, dv (float32) += the gradient contributions of key block (k, v)
-    for queries q with upstream gradient dout, global lse and delta = dout . o."""
-    _need_contiguous(q, k, v, dout, lse, delta, dq, dk, dv, q_pos, kv_pos)
+    for queries q with upstream gradient dout, global lse and delta = dout . o
+    (q_doc_start: the document mask, as for :func:`ra_block_attn_fwd`)."""
+    _need_contiguous(q, k, v, dout, lse, delta, dq, dk, dv, q_pos, kv_pos, q_doc_start)
     desc = AttnDesc(b=q.shape[0], n_q=q.shape[2], n_kv=k.shape[2], d=q.shape[3],
                     s_q=q.shape[1], s_kv=k.shape[1], dtype=_dtype_code(q), causal=int(causal),
                     scale=scale, v_layout=RA_V_ROWS,
                     q_pos=None if q_pos is None else q_pos.data_ptr(),
-                    kv_pos=None if kv_pos is None else kv_pos.data_ptr())
+                    kv_pos=None if kv_pos is None else kv_pos.data_ptr(),
+                    q_doc_start=None if q_doc_start is None else q_doc_start.data_ptr())
     _check(load_library().ra_block_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                             _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
                                             _ptr(dk), _ptr(dv), _stream(stream)))
@@ -275,3 +283,20 @@ def ra_allgather_fwd(desc, q, k_chunks, v_chunks, o, lse, workspace, stream=None
     _check(load_library().ra_allgather_fwd(ctypes.byref(desc), _ptr(q), _ptr(k_chunks),
                                            _ptr(v_chunks), _ptr(o), _ptr(lse), _ptr(workspace),
                                            ws_bytes, _stream(stream)))
+
+
+def ra_allgather_bwd_workspace_bytes(desc):
+    out = ctypes.c_size_t(0)
+    _check(load_library().ra_allgather_bwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
+
+
+def ra_allgather_bwd(desc, q, k_chunks, v_chunks, o, lse, dout, dq, dk_chunks, dv_chunks,
+                     workspace, stream=None):
+    """All-gather CP backward of one rank; see ringattn.h. dk_chunks / dv_chunks are added to."""
+    _need_contiguous(q, k_chunks, v_chunks, o, lse, dout, dq, dk_chunks, dv_chunks, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().ra_allgather_bwd(ctypes.byref(desc), _ptr(q), _ptr(k_chunks),
+                                           _ptr(v_chunks), _ptr(o), _ptr(lse), _ptr(dout),
+                                           _ptr(dq), _ptr(dk_chunks), _ptr(dv_chunks),
+                                           _ptr(workspace), ws_bytes, _stream(stream)))

@@ -14,6 +14,13 @@
 // transposed into the layout the attention kernel reads fastest. Everything
 // runs on one stream: positions, the queries' document starts, the gathers,
 // the transpose, one attention launch.
+//
+// ra_allgather_bwd is the backward of the same scheme (§8: the all-gather's
+// backward is a reduce-scatter of dK, dV): the block backward of the rank's
+// queries against the gathered sequence (the kernels of the ring backward,
+// with K/V of all S keys), then the sequence's dK, dV cut back into the N
+// chunks and added to the caller's slots -- this rank's share of the
+// reduce-scatter.
 #include <cmath>
 
 #include "ra_internal.h"
@@ -60,6 +67,47 @@ hipError_t launch_kv_gather(const void *chunks, void *full, const int32_t *pos, 
   return hipGetLastError();
 }
 
+// chunks[j, bi, a, :] += full[bi, pos[j*c + a], :] for float32 rows of
+// `row16` 16-byte units: the inverse of kv_gather_kernel, accumulating.
+__global__ __launch_bounds__(256) void kv_scatter_add_kernel(const float4 *__restrict__ full,
+                                                             float4 *__restrict__ chunks,
+                                                             const int32_t *__restrict__ pos,
+                                                             int64_t c, int32_t b, int64_t S,
+                                                             int64_t row16, int64_t total) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += stride) {
+    const int64_t u = i % row16;
+    const int64_t row = i / row16;         // (j * b + bi) * c + a
+    const int64_t a = row % c;
+    const int64_t jb = row / c;
+    const int64_t bi = jb % b;
+    const int64_t j = jb / b;
+    const int64_t p = pos[j * c + a];
+    const float4 x = full[(bi * S + p) * row16 + u];
+    float4 y = chunks[i];
+    y.x += x.x;
+    y.y += x.y;
+    y.z += x.z;
+    y.w += x.w;
+    chunks[i] = y;
+  }
+}
+
+hipError_t launch_kv_scatter_add(const float *full, float *chunks, const int32_t *pos, int64_t c,
+                                 int32_t N, int32_t b, int64_t S, size_t row_bytes,
+                                 hipStream_t stream) {
+  const int64_t row16 = static_cast<int64_t>(row_bytes / 16);
+  const int64_t total = static_cast<int64_t>(N) * b * c * row16;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  kv_scatter_add_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(
+      reinterpret_cast<const float4 *>(full), reinterpret_cast<float4 *>(chunks), pos, c, b, S,
+      row16, total);
+  return hipGetLastError();
+}
+
 struct AgPlan {
   int64_t c = 0;
   size_t full_bytes = 0;    // K (or V) of the whole sequence [b, S, n_kv, d]
@@ -94,6 +142,45 @@ ra_status make_ag_plan(const ra_ring_desc *r, AgPlan *p) {
     p->vt_off = off;
     off += align_up(p->full_bytes);
   }
+  p->total = off;
+  return RA_OK;
+}
+
+struct AgBwdPlan {
+  int64_t c = 0;
+  size_t kv_bytes = 0;      // K (or V) of the sequence, bf16 [b, S, n_kv, d]
+  size_t g_bytes = 0;       // dK (or dV) of the sequence, float32
+  size_t pos_off = 0, kvpos_off = 0, qlo_off = 0, delta_off = 0, k_off = 0, v_off = 0,
+         dk_off = 0, dv_off = 0, total = 0;
+};
+
+ra_status make_ag_bwd_plan(const ra_ring_desc *r, AgBwdPlan *p) {
+  ra_status st = check_ring_desc(r);
+  if (st != RA_OK) return st;
+  if (r->flags != 0) return fail(RA_ERR_INVALID_ARG, "all-gather bwd: flags must be 0 (0x%x)", r->flags);
+  if (r->dtype != RA_BF16 || r->d != 128)
+    return fail(RA_ERR_UNSUPPORTED, "all-gather bwd: bf16 with d = 128 only");
+  p->c = r->S / r->N;
+  const size_t elems = static_cast<size_t>(r->b) * r->S * r->n_kv * r->d;
+  p->kv_bytes = elems * 2;
+  p->g_bytes = elems * 4;
+  size_t off = 0;
+  p->pos_off = off;
+  off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
+  p->kvpos_off = off;
+  off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
+  p->qlo_off = off;
+  off += align_up(static_cast<size_t>(p->c) * sizeof(int32_t));
+  p->delta_off = off;
+  off += align_up(static_cast<size_t>(r->b) * p->c * r->n_q * sizeof(float));
+  p->k_off = off;
+  off += align_up(p->kv_bytes);
+  p->v_off = off;
+  off += align_up(p->kv_bytes);
+  p->dk_off = off;
+  off += align_up(p->g_bytes);
+  p->dv_off = off;
+  off += align_up(p->g_bytes);
   p->total = off;
   return RA_OK;
 }
@@ -193,5 +280,110 @@ extern "C" ra_status ra_allgather_fwd(const ra_ring_desc *r, const void *q, cons
   hipError_t err = r->dtype == RA_BF16 ? ra::launch_attn_bf16(a, s) : ra::launch_attn_f32(a, s);
   st = hip_check(err, "ra_allgather_fwd: attention launch");
   if (st == RA_OK && ev) st = hip_check(hipEventRecord(ev[1], s), "ra_allgather_fwd: event");
+  return st;
+}
+
+extern "C" ra_status ra_allgather_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *bytes) {
+  ra::clear_error();
+  if (!bytes) return ra::fail(RA_ERR_INVALID_ARG, "ra_allgather_bwd_workspace_bytes: bytes is NULL");
+  ra::AgBwdPlan p;
+  ra_status st = ra::make_ag_bwd_plan(desc, &p);
+  if (st != RA_OK) return st;
+  *bytes = p.total;
+  return RA_OK;
+}
+
+extern "C" ra_status ra_allgather_bwd(const ra_ring_desc *r, const void *q, const void *k_chunks,
+                                      const void *v_chunks, const float *o, const float *lse,
+                                      const void *dout, float *dq, float *dk_chunks,
+                                      float *dv_chunks, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+  using ra::fail;
+  using ra::hip_check;
+  ra::clear_error();
+  ra::AgBwdPlan P;
+  ra_status st = ra::make_ag_bwd_plan(r, &P);
+  if (st != RA_OK) return st;
+  if (r->b == 0 || P.c == 0) return RA_OK;
+  if (!q || !k_chunks || !v_chunks || !o || !lse || !dout || !dq || !dk_chunks || !dv_chunks)
+    return fail(RA_ERR_INVALID_ARG, "ra_allgather_bwd: NULL input or output");
+  const void *ptrs[] = {q, k_chunks, v_chunks, o, dout, dq, dk_chunks, dv_chunks};
+  for (const void *p : ptrs)
+    if (!ra::aligned16(p)) return fail(RA_ERR_INVALID_ARG, "ra_allgather_bwd: pointer not 16-byte aligned");
+  if (!workspace || !ra::aligned16(workspace))
+    return fail(RA_ERR_INVALID_ARG, "ra_allgather_bwd: workspace NULL or not 16-byte aligned");
+  if (workspace_bytes < P.total)
+    return fail(RA_ERR_INVALID_ARG, "ra_allgather_bwd: workspace has %zu bytes, needs %zu",
+                workspace_bytes, P.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  int32_t *pos = reinterpret_cast<int32_t *>(ws + P.pos_off);
+  int32_t *kv_pos = reinterpret_cast<int32_t *>(ws + P.kvpos_off);
+  int32_t *qlo = reinterpret_cast<int32_t *>(ws + P.qlo_off);
+  float *delta = reinterpret_cast<float *>(ws + P.delta_off);
+  unsigned char *kfull = ws + P.k_off;
+  unsigned char *vfull = ws + P.v_off;
+  float *dkfull = reinterpret_cast<float *>(ws + P.dk_off);
+  float *dvfull = reinterpret_cast<float *>(ws + P.dv_off);
+  const int32_t *q_pos = pos + static_cast<int64_t>(r->rank) * P.c;
+  const size_t row_bytes = static_cast<size_t>(r->n_kv) * r->d * 2;
+  const int64_t rows = static_cast<int64_t>(r->b) * P.c * r->n_q;
+  const int64_t g_elems = static_cast<int64_t>(r->b) * r->S * r->n_kv * r->d;
+
+  st = hip_check(ra::launch_positions(r->kind, r->S, r->N, pos, s), "ra_allgather_bwd: positions");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_positions(RA_PART_CONTIGUOUS, r->S, 1, kv_pos, s),
+                   "ra_allgather_bwd: key positions");
+  if (st == RA_OK && r->doc_start)
+    st = hip_check(ra::launch_gather_i32(r->doc_start, q_pos, qlo, P.c, s),
+                   "ra_allgather_bwd: document starts");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_bwd_delta(rows, r->d, 2, dout, o, delta, s), "ra_allgather_bwd: delta");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_fill_zero(dq, rows * r->d, s), "ra_allgather_bwd: zero dq");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_fill_zero(dkfull, g_elems, s), "ra_allgather_bwd: zero dK");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_fill_zero(dvfull, g_elems, s), "ra_allgather_bwd: zero dV");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_kv_gather(k_chunks, kfull, pos, P.c, r->N, r->b, r->S, row_bytes, s),
+                   "ra_allgather_bwd: K gather");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_kv_gather(v_chunks, vfull, pos, P.c, r->N, r->b, r->S, row_bytes, s),
+                   "ra_allgather_bwd: V gather");
+  if (st != RA_OK) return st;
+
+  ra::BwdArgs a{};
+  a.q = q;
+  a.k = kfull;
+  a.v = vfull;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dkfull;
+  a.dv = dvfull;
+  a.q_pos = q_pos;
+  a.kv_pos = kv_pos;
+  a.q_lo = r->doc_start ? qlo : nullptr;
+  a.s_q = P.c;
+  a.s_kv = r->S;
+  a.b = r->b;
+  a.n_q = r->n_q;
+  a.n_kv = r->n_kv;
+  a.d = r->d;
+  a.scale = r->scale > 0.f ? r->scale : 1.0f / std::sqrt(static_cast<float>(r->d));
+  a.causal = r->causal;
+  st = hip_check(ra::launch_attn_bwd_bf16(a, s), "ra_allgather_bwd: backward launch");
+  const size_t g_row_bytes = static_cast<size_t>(r->n_kv) * r->d * 4;
+  if (st == RA_OK)
+    st = hip_check(ra::launch_kv_scatter_add(dkfull, dk_chunks, pos, P.c, r->N, r->b, r->S,
+                                             g_row_bytes, s),
+                   "ra_allgather_bwd: dK scatter");
+  if (st == RA_OK)
+    st = hip_check(ra::launch_kv_scatter_add(dvfull, dv_chunks, pos, P.c, r->N, r->b, r->S,
+                                             g_row_bytes, s),
+                   "ra_allgather_bwd: dV scatter");
   return st;
 }

@@ -148,7 +148,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 // counters are left alone). A barrier after it publishes the data to all waves.
 __device__ __forceinline__ void wait_own_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int HW, bool VT>
+// DOC: a document mask is given (a.q_lo); without it the mask code compiles away.
+template <int HW, bool VT, bool DOC>
 __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // One LDS object per stage and operand: the compiler then sees that the
   // asynchronous loads into one stage never alias the reads of the others and
@@ -213,11 +214,11 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   int32_t w_lomax = INT_MIN;  // latest document start among the wave's queries
   if (a.causal) {
     nkeys = count_le(a.kv_pos, a.s_kv, a.q_pos[wg_tok_last]);
-    if (a.q_lo) kbeg = count_lt(a.kv_pos, a.s_kv, a.q_lo[wg_tok0]) / BK * BK;
+    if (DOC) kbeg = count_lt(a.kv_pos, a.s_kv, a.q_lo[wg_tok0]) / BK * BK;
     if (wave_has_rows) {
       w_qmin = a.q_pos[w_tok0];
       w_qmax = a.q_pos[w_tok_last];
-      if (a.q_lo) w_lomax = a.q_lo[w_tok_last];
+      if (DOC) w_lomax = a.q_lo[w_tok_last];
     }
   }
   const int nt = nkeys > kbeg ? static_cast<int>((nkeys - kbeg + BK - 1) / BK) : 0;
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     }
   }
   const int32_t qpos = !a.causal ? INT_MAX - 1 : (tok_ok ? a.q_pos[tok] : INT_MIN);
-  const int32_t qlo = a.q_lo && tok_ok ? a.q_lo[tok] : INT_MIN;  // first visible key position
+  const int32_t qlo = DOC && tok_ok ? a.q_lo[tok] : INT_MIN;  // first visible key position
   const float sl2 = a.scale * LOG2E;
 
   // ---- per-lane LDS offsets of the MFMA operands (within one stage) ----
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     const int64_t key0 = kbeg + static_cast<int64_t>(t) * BK;
     const bool ragged = key0 + BK > a.s_kv;
     if (ragged || (a.causal && tile_pos(stage, BK - 1) > w_qmin) ||
-        (a.q_lo && tile_pos(stage, 0) < w_lomax)) {
+        (DOC && tile_pos(stage, 0) < w_lomax)) {
       // Branch-free selects: key index past the block, position after the
       // query, or before the query's document.
       const int lim = ragged ? static_cast<int>(a.s_kv - key0) : BK;
@@ -635,7 +636,10 @@ hipError_t launch_hw(const AttnArgs &a, hipStream_t stream) {
   const int64_t blocks = ntb * a.b * a.n_kv * ((a.n_q / a.n_kv) / HW);
   if (blocks == 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  attn_bf16_kernel<HW, VT><<<static_cast<unsigned>(blocks), THREADS, 0, stream>>>(a);
+  if (a.q_lo)
+    attn_bf16_kernel<HW, VT, true><<<static_cast<unsigned>(blocks), THREADS, 0, stream>>>(a);
+  else
+    attn_bf16_kernel<HW, VT, false><<<static_cast<unsigned>(blocks), THREADS, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -154,7 +154,8 @@ constexpr int Q_BK = 64;
 constexpr int Q_TILE_B = Q_BK * ROW_B;
 constexpr int Q_LOADS = Q_TILE_B / (1024 * Q_WAVES);
 
-template <int HW>
+// DOC: a document mask is given (a.q_lo); without it the mask code compiles away.
+template <int HW, bool DOC>
 __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char k_lds0[Q_TILE_B], k_lds1[Q_TILE_B],
       k_lds2[Q_TILE_B];
@@ -203,16 +204,22 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
   const int64_t tok = w_tok0 + col;
   const bool tok_ok = tok < a.s_q;
 
+  // Keys up to the workgroup's last position; with a document mask, from the
+  // tile holding the first query's document start.
   int64_t nkeys = a.s_kv;
+  int64_t kbeg = 0;
   int32_t w_qmin = INT_MAX - 1, w_qmax = INT_MAX - 1;
+  int32_t w_lomax = INT_MIN;
   if (a.causal) {
     nkeys = count_le(a.kv_pos, a.s_kv, a.q_pos[wg_tok_last]);
+    if (DOC) kbeg = count_lt(a.kv_pos, a.s_kv, a.q_lo[wg_tok0]) / Q_BK * Q_BK;
     if (wave_has_rows) {
       w_qmin = a.q_pos[w_tok0];
       w_qmax = a.q_pos[w_tok_last];
+      if (DOC) w_lomax = a.q_lo[w_tok_last];
     }
   }
-  const int nt = static_cast<int>((nkeys + Q_BK - 1) / Q_BK);
+  const int nt = nkeys > kbeg ? static_cast<int>((nkeys - kbeg + Q_BK - 1) / Q_BK) : 0;
 
   // This lane's query and upstream gradient: the B operands of S^T and dP^T.
   const uint16_t *qg = static_cast<const uint16_t *>(a.q);
@@ -229,6 +236,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     dreg[ds] = __builtin_bit_cast(bf16x8, rd);
   }
   const int32_t qpos = !a.causal ? INT_MAX - 1 : (tok_ok ? a.q_pos[tok] : INT_MIN);
+  const int32_t qlo = DOC && tok_ok ? a.q_lo[tok] : INT_MIN;  // document start
   const float lse2 = tok_ok ? lse_log2(a.lse[row]) : INFINITY;
   const float dlt = tok_ok ? a.delta[row] : 0.f;
   const float sl2 = a.scale * LOG2E;
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     goff[i] = static_cast<uint32_t>(r * kv_row_bytes + (((lane & 15) ^ swz(r & 15)) << 4));
   }
   auto issue_tile = [&](int t, auto stage) INLINE {
-    const int64_t key0 = static_cast<int64_t>(t) * Q_BK;
+    const int64_t key0 = kbeg + static_cast<int64_t>(t) * Q_BK;
     const int64_t left = a.s_kv - key0;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + kv_base + key0 * kv_row_bytes,
                                                 (left - 1) * kv_row_bytes + D * 2);
@@ -275,6 +283,9 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
   bool done = !wave_has_rows || nt == 0;
+  // With a document mask many waves see no key at all: they skip the dq
+  // update (adding zeros). Without one the flag compiles away.
+  bool any = false;
 
   auto process = [&](int t, auto stage) INLINE {
     const unsigned char *kb = k_stage(stage);
@@ -295,9 +306,10 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
         dp[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dreg[ds], dp[j], 0, 0, 0);
       }
     // Element e4*4 + j of key block kb holds key kb*32 + e4*8 + hi*4 + j.
-    const int64_t key0 = static_cast<int64_t>(t) * Q_BK;
+    const int64_t key0 = kbeg + static_cast<int64_t>(t) * Q_BK;
     const bool ragged = key0 + Q_BK > a.s_kv;
-    if (ragged || (a.causal && p_stage(stage)[Q_BK - 1] > w_qmin)) {
+    if (ragged || (a.causal && p_stage(stage)[Q_BK - 1] > w_qmin) ||
+        (DOC && p_stage(stage)[0] < w_lomax)) {
       const int lim = ragged ? static_cast<int>(a.s_kv - key0) : Q_BK;
       const int32_t *pp = p_stage(stage);
       const int32_t qp = a.causal ? qpos : INT_MAX;
@@ -308,7 +320,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
           const int kk = j * 32 + e4 * 8 + hi * 4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool out = (kk + i >= lim) | (pp[kk + i] > qp);
+            const bool out = (kk + i >= lim) | (pp[kk + i] > qp) | (pp[kk + i] < qlo);
             s[j][e4 * 4 + i] = out ? -INFINITY : s[j][e4 * 4 + i];
           }
         }
@@ -344,10 +356,12 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();   // ... and in everyone's; every wave is done with tile t-1
     if (t + 2 < nt) issue_tile(t + 2, SL{});
     if (!done) {
-      if (a.causal && p_stage(SC{})[0] > w_qmax)
+      if (a.causal && p_stage(SC{})[0] > w_qmax) {
         done = true;  // this and every later tile is after the wave's last query
-      else
+      } else {
         process(t, SC{});
+        if (DOC) any = true;
+      }
     }
   };
   for (int t = 0; t < nt; t += 3) {
@@ -356,7 +370,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     if (t + 2 < nt) step(St2{}, t + 2);
   }
 
-  if (!tok_ok) return;
+  if (!tok_ok || (DOC && !any)) return;
   // Accumulator element e4*4 + j of block db holds d = db*32 + e4*8 + hi*4 + j.
   float *drow = a.dq + row * D + hi * 4;
 #pragma unroll
@@ -384,6 +398,7 @@ constexpr int KV_SUB = 32;
 constexpr int KV_TILE_B = KV_QB * ROW_B;     // 16 KiB (q or do)
 constexpr int KV_LOADS = KV_TILE_B / (1024 * KV_WAVES);
 
+template <bool DOC>
 __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char q_lds0[KV_TILE_B], q_lds1[KV_TILE_B],
       q_lds2[KV_TILE_B];
@@ -393,6 +408,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float l_lds0[64], l_lds1[64], l_lds2[64];
   __shared__ __attribute__((aligned(16))) float e_lds0[64], e_lds1[64], e_lds2[64];
   __shared__ __attribute__((aligned(16))) int32_t p_lds0[64], p_lds1[64], p_lds2[64];
+  // ... and the rows' document starts (document mask)
+  __shared__ __attribute__((aligned(16))) int32_t o_lds0[64], o_lds1[64], o_lds2[64];
   auto q_stage = [&](auto s) INLINE -> unsigned char * {
     constexpr int v = decltype(s)::value;
     return v == 0 ? q_lds0 : v == 1 ? q_lds1 : q_lds2;
@@ -412,6 +429,10 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   auto p_stage = [&](auto s) INLINE -> int32_t * {
     constexpr int v = decltype(s)::value;
     return v == 0 ? p_lds0 : v == 1 ? p_lds1 : p_lds2;
+  };
+  auto lo_stage = [&](auto s) INLINE -> int32_t * {
+    constexpr int v = decltype(s)::value;
+    return v == 0 ? o_lds0 : v == 1 ? o_lds1 : o_lds2;
   };
 
   const int tid = threadIdx.x;
@@ -443,11 +464,15 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // ---- query range that can see any key of the workgroup ----
-  int64_t q_first = 0;
+  // Causal: from the first query at or after its first key. With a document
+  // mask, up to the last query whose document starts at or before its last
+  // key (document starts are non-decreasing).
+  int64_t q_first = 0, q_end = a.s_q;
   if (a.causal) q_first = count_lt(a.q_pos, a.s_q, a.kv_pos[wg_key0]);
+  if (DOC) q_end = count_le(a.q_lo, a.s_q, a.kv_pos[min(wg_key0 + KV_KT, a.s_kv) - 1]);
   const int64_t qb0 = q_first / KV_QB;
-  const int64_t nqb = (a.s_q + KV_QB - 1) / KV_QB;
-  const int64_t n_blk = nqb - qb0;         // query blocks per head
+  const int64_t nqb = (q_end + KV_QB - 1) / KV_QB;
+  const int64_t n_blk = nqb > qb0 ? nqb - qb0 : 0;   // query blocks per head
   const int n_it = static_cast<int>(n_blk * g);
 
   // ---- this lane's key: B operands of S = Q K^T and dP = dO V^T ----
@@ -525,9 +550,17 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.q_pos + q0, left * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (LDS_AS void *)p_stage(stage), 4, lane * 4,
                                                0, 0, 0);
+    } else if (DOC && wave == 3) {
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_lo + q0, left * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (LDS_AS void *)lo_stage(stage), 4, lane * 4,
+                                               0, 0, 0);
     }
   };
 
+  // With a document mask most workgroups of a long sequence see few queries:
+  // a wave that processed nothing skips the dk, dv update (adding zeros).
+  // Without one the flag compiles away.
+  bool any = false;
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
@@ -542,8 +575,13 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int32_t *pp = p_stage(stage) + rb;
     const int64_t qlim = a.s_q - q0 - rb;     // rows past the sequence are masked
     if (qlim <= 0) return;
-    // Whole sub-block before the wave's first key (causal): nothing visible.
-    if (a.causal && pp[min<int64_t>(KV_SUB, qlim) - 1] < w_kmin) return;
+    const int32_t *lp = lo_stage(stage) + rb;
+    const int64_t last = min<int64_t>(KV_SUB, qlim) - 1;
+    // Whole sub-block before the wave's first key (causal), or every query's
+    // document starting after the wave's last key: nothing visible.
+    if (a.causal && pp[last] < w_kmin) return;
+    if (DOC && lp[0] > w_kmax) return;
+    if (DOC) any = true;
     const unsigned char *qb = q_stage(stage);
     const unsigned char *db = d_stage(stage);
     // Every LDS operand of the sub-block is read up front (one wave per SIMD:
@@ -571,7 +609,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const float *ll = l_stage(stage) + rb;
     const float *ee = e_stage(stage) + rb;
     const bool ragged = qlim < KV_SUB;
-    const bool diag = a.causal && pp[0] < w_kmax;  // some query sees only part of the keys
+    // some query sees only part of the keys (diagonal, or a document start inside them)
+    const bool diag = (a.causal && pp[0] < w_kmax) || (DOC && lp[last] > w_kmin);
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
@@ -581,15 +620,21 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
       const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
       int32_t qp[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+      int32_t ql[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
       if (diag) {
         const int4 p4 = *reinterpret_cast<const int4 *>(pp + r0);
         qp[0] = p4.x; qp[1] = p4.y; qp[2] = p4.z; qp[3] = p4.w;
+        if (DOC) {
+          const int4 o4 = *reinterpret_cast<const int4 *>(lp + r0);
+          ql[0] = o4.x; ql[1] = o4.y; ql[2] = o4.z; ql[3] = o4.w;
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int el = e4 * 4 + j;
         float x = s[el];
-        const bool out = ((ragged | diag) & ((r0 + j >= qlim) | (kpos > qp[j]))) | !key_ok;
+        const bool out =
+            ((ragged | diag) & ((r0 + j >= qlim) | (kpos > qp[j]) | (kpos < ql[j]))) | !key_ok;
         x = out ? -INFINITY : x;
         const float p = exp2_fast(fmaf(x, sl2, -lse_log2(lv[j])));
         const float dsv = p * (dp[el] - dv4[j]);
@@ -636,7 +681,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (it + 2 < n_it) step(St2{}, it + 2);
   }
 
-  if (!key_ok) return;
+  if (!key_ok || (DOC && !any)) return;
   // Accumulator element e4*4 + j of block dblk holds d = dblk*32 + e4*8 + hi*4 + j.
   float *krow_out = a.dk + krow * D + hi * 4;
   float *vrow_out = a.dv + krow * D + hi * 4;
@@ -667,7 +712,10 @@ hipError_t launch_dq(const BwdArgs &a, hipStream_t stream) {
   const int64_t blocks = ntb * a.b * a.n_kv * ((a.n_q / a.n_kv) / HW);
   if (blocks == 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  bwd_dq_kernel<HW><<<static_cast<unsigned>(blocks), Q_THREADS, 0, stream>>>(a);
+  if (a.q_lo)
+    bwd_dq_kernel<HW, true><<<static_cast<unsigned>(blocks), Q_THREADS, 0, stream>>>(a);
+  else
+    bwd_dq_kernel<HW, false><<<static_cast<unsigned>(blocks), Q_THREADS, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -707,7 +755,10 @@ hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t stream) {
   const int64_t nkt = (a.s_kv + KV_KT - 1) / KV_KT;
   const int64_t blocks = nkt * a.b * a.n_kv;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  bwd_dkdv_kernel<<<static_cast<unsigned>(blocks), KV_THREADS, 0, stream>>>(a);
+  if (a.q_lo)
+    bwd_dkdv_kernel<true><<<static_cast<unsigned>(blocks), KV_THREADS, 0, stream>>>(a);
+  else
+    bwd_dkdv_kernel<false><<<static_cast<unsigned>(blocks), KV_THREADS, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -742,8 +793,6 @@ extern "C" ra_status ra_block_attn_bwd(const ra_attn_desc *desc, const void *q, 
     return fail(RA_ERR_UNSUPPORTED, "ra_block_attn_bwd: bf16 with d = 128 only");
   if (desc->v_layout != RA_V_ROWS)
     return fail(RA_ERR_UNSUPPORTED, "ra_block_attn_bwd: v must be row-major (RA_V_ROWS)");
-  if (desc->q_doc_start)
-    return fail(RA_ERR_UNSUPPORTED, "ra_block_attn_bwd: no document mask in the backward");
   if (desc->b == 0 || desc->s_q == 0 || desc->s_kv == 0) return RA_OK;
   if (!dout || !delta || !dk || !dv)
     return fail(RA_ERR_INVALID_ARG, "ra_block_attn_bwd: NULL dout / delta / dk / dv");
@@ -761,6 +810,7 @@ extern "C" ra_status ra_block_attn_bwd(const ra_attn_desc *desc, const void *q, 
   a.dv = dv;
   a.q_pos = desc->q_pos;
   a.kv_pos = desc->kv_pos;
+  a.q_lo = desc->q_doc_start;
   a.s_q = desc->s_q;
   a.s_kv = desc->s_kv;
   a.b = desc->b;

@@ -21,7 +21,6 @@ struct AttnArgs {
   float *lse;
   const int32_t *q_pos;
   const int32_t *kv_pos;
-  const int32_t *q_lo;  // optional [s_q]: first visible key position (document start)
   int64_t s_q;
   int64_t s_kv;
   int32_t b;
@@ -32,6 +31,7 @@ struct AttnArgs {
   int32_t causal;
   int32_t merge;
   int32_t v_layout;  // ra_v_layout of v (RA_V_TRANSPOSED: [b, n_kv, d, s_kv], bf16 only)
+  const int32_t *q_lo;  // optional [s_q]: first visible key position (document start)
 };
 
 // Arguments of one backward launch (one key block against a query shard):
@@ -50,6 +50,7 @@ struct BwdArgs {
   float *dv;
   const int32_t *q_pos;
   const int32_t *kv_pos;
+  const int32_t *q_lo;  // optional [s_q]: first visible key position (document start)
   int64_t s_q;
   int64_t s_kv;
   int32_t b;
@@ -84,6 +85,8 @@ hipError_t launch_bwd_delta(int64_t rows, int32_t d, int32_t esize, const void *
                             const float *o, float *delta, hipStream_t stream);
 // dq, dk, dv += the gradient contributions of one key block (bf16, d = 128).
 hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t stream);
+// p[0 .. n) = 0 (a kernel, so that callers may capture it in a graph).
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
 // v [b, s, n_kv, d] -> vt [b, n_kv, d, s]; esize = 2 or 4 bytes per element.
 // out[i] = src[idx[i]], i < n.
 hipError_t launch_gather_i32(const int32_t *src, const int32_t *idx, int32_t *out, int64_t n,

@@ -110,8 +110,6 @@ ra_status make_plan(const ra_ring_desc *r, Plan *p) {
   size_t off = 0;
   p->pos_off = off;
   off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
-  p->qlo_off = off;   // the rank's queries' document starts
-  off += align_up(static_cast<size_t>(p->c) * sizeof(int32_t));
   if (r->N > 1 || p->vt) {
     for (int i = 0; i < 2; ++i) {
       p->kv_off[i] = off;
@@ -125,6 +123,8 @@ ra_status make_plan(const ra_ring_desc *r, Plan *p) {
     p->lseb_off = off;
     off += align_up(rows * sizeof(float));
   }
+  p->qlo_off = off;   // the rank's queries' document starts
+  off += align_up(static_cast<size_t>(p->c) * sizeof(int32_t));
   p->total = off;
   return RA_OK;
 }
@@ -380,15 +380,13 @@ namespace {
 struct BwdPlan {
   int64_t c = 0;
   size_t chunk_elems = 0;  // one K (or V) chunk [b, c, n_kv, d]
-  size_t pos_off = 0, delta_off = 0, total = 0;
+  size_t pos_off = 0, delta_off = 0, qlo_off = 0, total = 0;
 };
 
 ra_status make_bwd_plan(const ra_ring_desc *r, BwdPlan *p) {
   if (!r) return fail(RA_ERR_INVALID_ARG, "ring bwd: desc is NULL");
   if (r->flags & ~RA_RING_SERIALIZE)
     return fail(RA_ERR_INVALID_ARG, "ring bwd: only RA_RING_SERIALIZE may be set (0x%x)", r->flags);
-  if (r->doc_start)
-    return fail(RA_ERR_UNSUPPORTED, "ring bwd: no document mask in the backward");
   ra_ring_desc fwd = *r;
   fwd.flags = 0;
   Plan fp;
@@ -403,6 +401,8 @@ ra_status make_bwd_plan(const ra_ring_desc *r, BwdPlan *p) {
   off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
   p->delta_off = off;
   off += align_up(static_cast<size_t>(r->b) * fp.c * r->n_q * sizeof(float));
+  p->qlo_off = off;   // the rank's queries' document starts
+  off += align_up(static_cast<size_t>(fp.c) * sizeof(int32_t));
   p->total = off;
   return RA_OK;
 }
@@ -463,6 +463,11 @@ extern "C" ra_status ra_ring_bwd(const ra_ring_desc *r, const void *q, const voi
     st = hip_check(ra::launch_bwd_delta(rows, r->d, 2, dout, o, delta, sc), "ra_ring_bwd: delta");
   if (st == RA_OK)
     st = hip_check(ra::launch_fill_zero(dq, rows * r->d, sc), "ra_ring_bwd: zero dq");
+  int32_t *qlo = reinterpret_cast<int32_t *>(ws + P.qlo_off);
+  if (st == RA_OK && r->doc_start)
+    st = hip_check(ra::launch_gather_i32(r->doc_start, pos + static_cast<int64_t>(r->rank) * P.c,
+                                         qlo, P.c, sc),
+                   "ra_ring_bwd: document starts");
   if (st == RA_OK && step_ev) st = hip_check(hipEventRecord(step_ev[0], sc), "ra_ring_bwd: step event");
   if (st != RA_OK) return st;
 
@@ -481,6 +486,7 @@ extern "C" ra_status ra_ring_bwd(const ra_ring_desc *r, const void *q, const voi
   a.scale = r->scale > 0.f ? r->scale : 1.0f / std::sqrt(static_cast<float>(r->d));
   a.causal = r->causal;
   a.q_pos = pos + static_cast<int64_t>(r->rank) * P.c;
+  a.q_lo = r->doc_start ? qlo : nullptr;
   const unsigned char *kc = static_cast<const unsigned char *>(k_chunks);
   const unsigned char *vc = static_cast<const unsigned char *>(v_chunks);
   const int N = r->N;

@@ -237,30 +237,29 @@ def test_backward_argument_errors():
         ra.ra_ring_bwd_workspace_bytes(_ring(flags=ra.RA_RING_UNFUSED_MERGE))
     def align(x):
         return (x + 255) // 256 * 256
-    assert ra.ra_ring_bwd_workspace_bytes(_ring()) == align(1024 * 4) + align(256 * 8 * 4)
+    assert ra.ra_ring_bwd_workspace_bytes(_ring()) == (align(1024 * 4) + align(256 * 8 * 4)
+                                                       + align(256 * 4))
 
 
 def test_document_mask_argument_errors():
-    """The document mask needs the causal rule; the backward takes none."""
+    """The document mask needs the causal rule."""
     lib = ra.load_library()
-    desc = _attn_desc(causal=0)
-    desc.q_doc_start = FAKE.value
-    st = lib.ra_block_attn_fwd(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, None)
-    assert st == ra.RA_ERR_UNSUPPORTED, ra.ra_last_error()
-    desc = _attn_desc(causal=1, q_pos=FAKE.value, kv_pos=FAKE.value)
-    desc.q_doc_start = FAKE.value
-    st = lib.ra_block_attn_bwd(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                               FAKE, FAKE, None)
-    assert st == ra.RA_ERR_UNSUPPORTED
+    for fn in (lambda d: lib.ra_block_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                               None),
+               lambda d: lib.ra_block_attn_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                               FAKE, FAKE, FAKE, FAKE, None)):
+        desc = _attn_desc(causal=0)
+        desc.q_doc_start = FAKE.value
+        assert fn(desc) == ra.RA_ERR_UNSUPPORTED, ra.ra_last_error()
     ring = _ring()
     ring.doc_start = FAKE.value
-    ra.ra_ring_workspace_bytes(ring)            # the forward ring takes it
-    ra.ra_allgather_workspace_bytes(ring)
-    with pytest.raises(ra.RingAttnError):
-        ra.ra_ring_bwd_workspace_bytes(ring)
+    for fn in (ra.ra_ring_workspace_bytes, ra.ra_allgather_workspace_bytes,
+               ra.ra_ring_bwd_workspace_bytes, ra.ra_allgather_bwd_workspace_bytes):
+        fn(ring)                                  # every ring / all-gather call takes it
     ring = _ring(causal=False)
     ring.doc_start = FAKE.value
-    for fn in (ra.ra_ring_workspace_bytes, ra.ra_allgather_workspace_bytes):
+    for fn in (ra.ra_ring_workspace_bytes, ra.ra_allgather_workspace_bytes,
+               ra.ra_ring_bwd_workspace_bytes, ra.ra_allgather_bwd_workspace_bytes):
         with pytest.raises(ra.RingAttnError):
             fn(ring)
 
@@ -286,4 +285,25 @@ def test_allgather_workspace_and_errors():
                               None)
     assert st == ra.RA_ERR_INVALID_ARG and "workspace" in ra.ra_last_error()
     st = lib.ra_allgather_fwd(ctypes.byref(desc), FAKE, None, FAKE, FAKE, FAKE, FAKE, need, None)
+    assert st == ra.RA_ERR_INVALID_ARG
+
+
+def test_allgather_bwd_workspace_and_errors():
+    def align(x):
+        return (x + 255) // 256 * 256
+    elems = 1024 * 2 * 128
+    want = (2 * align(1024 * 4) + align(256 * 4) + align(256 * 8 * 4)
+            + 2 * align(elems * 2) + 2 * align(elems * 4))
+    assert ra.ra_allgather_bwd_workspace_bytes(_ring()) == want
+    for kw in (dict(dtype=ra.RA_F32), dict(flags=ra.RA_RING_SERIALIZE), dict(S=1002)):
+        with pytest.raises(ra.RingAttnError):
+            ra.ra_allgather_bwd_workspace_bytes(_ring(**kw))
+    lib = ra.load_library()
+    desc = _ring()
+    need = ra.ra_allgather_bwd_workspace_bytes(desc)
+    args = [FAKE] * 9
+    st = lib.ra_allgather_bwd(ctypes.byref(desc), *args, FAKE, need - 1, None)
+    assert st == ra.RA_ERR_INVALID_ARG and "workspace" in ra.ra_last_error()
+    args[6] = None       # dq
+    st = lib.ra_allgather_bwd(ctypes.byref(desc), *args, FAKE, need, None)
     assert st == ra.RA_ERR_INVALID_ARG

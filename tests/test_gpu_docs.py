@@ -1,10 +1,12 @@
 """GPU parity of the document mask and of all-gather context parallelism
 ("Context Parallelism and Ring Attention" §8) against the fp64 oracle
-(oracle/documents.py), through the C ABI: ra_block_attn_fwd with
-q_doc_start, ra_allgather_fwd, and ra_ring_fwd with doc_start.
+(oracle/documents.py), through the C ABI: ra_block_attn_fwd and
+ra_block_attn_bwd with q_doc_start, ra_allgather_fwd / ra_allgather_bwd, and
+ra_ring_fwd / ra_ring_bwd with doc_start.
 
-Tolerances are the forward's (tests/gpu_util.py): O max-abs <= 1e-2 (bf16)
-or 1e-5 (f32), lse <= 2e-3, -inf rows exactly -inf with o = 0."""
+Tolerances: the forward's (tests/gpu_util.py: O max-abs <= 1e-2 for bf16 or
+1e-5 for f32, lse <= 2e-3, -inf rows exactly -inf with o = 0) and the
+backward's (tests/test_gpu_bwd.py: max |g - g_ref| <= 1e-2 max |g_ref| + 1e-4)."""
 
 import zlib
 
@@ -190,3 +192,191 @@ def test_allgather_workload_sampled_rows(name):
     do, dl = compare(o[:, rows], lse[:, rows], ro, rl, w.dtype, w.name)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     print(f"  rows {len(rows)} max|dO| {do:.2e} max|dlse| {dl:.2e}", flush=True)
+
+
+# ------------------------------------------------------------------ backward
+# Tolerance as in tests/test_gpu_bwd.py: max |g - g_ref| <= 1e-2 max |g_ref| + 1e-4.
+
+def _grad_close(got, want, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert not np.isnan(got).any(), f"{what}: NaN"
+    err = float(np.max(np.abs(got - want))) if want.size else 0.0
+    scale = float(np.max(np.abs(want))) if want.size else 0.0
+    assert err <= 1e-2 * scale + 1e-4, f"{what}: max err {err:.3g} vs max |ref| {scale:.3g}"
+    return err, scale
+
+
+BWD_BLOCK_CASES = [
+    # b, s_q, s_kv, n_q, n_kv, mean document length
+    (1, 128, 256, 8, 1, 40),
+    (1, 200, 333, 8, 2, 25),     # ragged
+    (2, 77, 130, 8, 4, 1),       # one token per document
+    (1, 257, 640, 8, 8, 5000),   # one document
+]
+
+
+@pytest.mark.parametrize("case", BWD_BLOCK_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_block_bwd_doc_mask_matches_oracle(case):
+    b, s_q, s_kv, n_q, n_kv, mean = case
+    print(f"block bwd doc mask {case}", flush=True)
+    rng = np.random.default_rng(_seed(case))
+    d = 128
+    span = 2 * (s_q + s_kv) + 8
+    lengths = _lengths(rng, span, mean)
+    ids = odoc.doc_ids_from_lengths(lengths)
+    starts = runner.doc_start_positions(lengths)
+    q_pos = np.sort(rng.choice(span, s_q, replace=False)).astype(np.int32)
+    kv_pos = np.sort(rng.choice(span, s_kv, replace=False)).astype(np.int32)
+    q, q64 = rand_inputs((b, s_q, n_q, d), "bf16", rng)
+    k, k64 = rand_inputs((b, s_kv, n_kv, d), "bf16", rng)
+    v, v64 = rand_inputs((b, s_kv, n_kv, d), "bf16", rng)
+    do, do64 = rand_inputs((b, s_q, n_q, d), "bf16", rng)
+    scale = np.float32(1 / np.sqrt(d))
+    vis = odoc.visible_docs(q_pos, kv_pos, ids, True)
+    o, lse = odoc.masked_attention(q64, k64, v64, vis, scale)
+    tq, tk, tv, tdo = (to_device(x, "bf16") for x in (q, k, v, do))
+    delta = torch.empty((b, s_q, n_q), device="cuda")
+    ra.ra_attn_bwd_delta(tdo, torch.from_numpy(o.astype(np.float32)).cuda(), delta)
+    dq = torch.zeros((b, s_q, n_q, d), device="cuda")
+    dk = torch.zeros((b, s_kv, n_kv, d), device="cuda")
+    dv = torch.zeros_like(dk)
+    ra.ra_block_attn_bwd(tq, tk, tv, tdo, torch.from_numpy(lse.astype(np.float32)).cuda(), delta,
+                         dq, dk, dv, causal=True, q_pos=torch.from_numpy(q_pos).cuda(),
+                         kv_pos=torch.from_numpy(kv_pos).cuda(),
+                         q_doc_start=torch.from_numpy(starts[q_pos]).cuda())
+    torch.cuda.synchronize()
+    rq, rk, rv = odoc.masked_attention_bwd(q64, k64, v64, do64, vis, scale)
+    for got, want, name in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        err, mag = _grad_close(got.cpu().numpy(), want, f"{case} {name}")
+        print(f"  {name}: max err {err:.2e} (max |ref| {mag:.2e})", flush=True)
+
+
+AG_BWD_CASES = [
+    # kind, N, S, n_q, n_kv, rank, mean document length (0: no documents)
+    ("zigzag", 4, 1536, 8, 2, 0, 90),
+    ("zigzag", 4, 1536, 8, 2, 3, 90),
+    ("striped", 4, 1024, 8, 1, 1, 50),
+    ("contiguous", 2, 768, 4, 4, 1, 300),
+    ("zigzag", 4, 1024, 8, 2, 2, 0),
+    ("zigzag", 2, 300, 4, 2, 1, 40),
+]
+
+
+@pytest.mark.parametrize("case", AG_BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_allgather_bwd_matches_oracle(case):
+    kind, N, S, n_q, n_kv, rank, mean = case
+    print(f"all-gather bwd {case}", flush=True)
+    docs = mean > 0
+    tq, kc, vc, ds, q64, k64, v64, ids = _allgather_case(kind, N, S, n_q, n_kv, "bf16", rank,
+                                                         max(mean, 1), docs, _seed(case))
+    rng = np.random.default_rng(_seed(case) + 1)
+    c = S // N
+    do, do64 = rand_inputs((1, c, n_q, 128), "bf16", rng)
+    scale = np.float32(1 / np.sqrt(128))
+    kc64 = np.stack([k64[:, opart.partition_map(kind, S, N, j)] for j in range(N)])
+    vc64 = np.stack([v64[:, opart.partition_map(kind, S, N, j)] for j in range(N)])
+    o, lse = odoc.allgather_attention(q64, kc64, vc64, kind, S, N, rank, ids, True, scale)
+    desc, _ = ra.ring_desc(b=1, n_q=n_q, n_kv=n_kv, d=128, dtype=ra.RA_BF16, causal=True,
+                           kind=kind, S=S, N=N, rank=rank, doc_start=ds)
+    ws = torch.empty(ra.ra_allgather_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    dq = torch.full(tuple(tq.shape), float("nan"), device="cuda")
+    dkc = torch.zeros((N, 1, c, n_kv, 128), device="cuda")
+    dvc = torch.zeros_like(dkc)
+    ra.ra_allgather_bwd(desc, tq, kc, vc, torch.from_numpy(o.astype(np.float32)).cuda(),
+                        torch.from_numpy(lse.astype(np.float32)).cuda(), to_device(do, "bf16"),
+                        dq, dkc, dvc, ws)
+    torch.cuda.synchronize()
+    rq, rkc, rvc = odoc.allgather_attention_bwd(q64, kc64, vc64, do64, kind, S, N, rank, ids,
+                                                True, scale)
+    for got, want, name in ((dq, rq, "dq"), (dkc, rkc, "dk"), (dvc, rvc, "dv")):
+        err, mag = _grad_close(got.cpu().numpy(), want, f"{case} {name}")
+        print(f"  {name}: max err {err:.2e} (max |ref| {mag:.2e})", flush=True)
+
+
+def test_ring_bwd_with_doc_mask_reassembles_sequence_gradients():
+    """Every rank's ring backward under the document mask: dq of each rank and
+    the summed dK, dV slots against the whole sequence's masked gradients."""
+    kind, N, S = "zigzag", 4, 1536
+    rng = np.random.default_rng(77)
+    lengths = _lengths(rng, S, 120)
+    ids = odoc.doc_ids_from_lengths(lengths)
+    ds = torch.from_numpy(runner.doc_start_positions(lengths)).cuda()
+    q_all, q64 = rand_inputs((1, S, 8, 128), "bf16", rng)
+    k, k64 = rand_inputs((1, S, 2, 128), "bf16", rng)
+    v, v64 = rand_inputs((1, S, 2, 128), "bf16", rng)
+    do_all, do64 = rand_inputs((1, S, 8, 128), "bf16", rng)
+    scale = np.float32(1 / np.sqrt(128))
+    pos = np.arange(S)
+    vis = odoc.visible_docs(pos, pos, ids, True)
+    want = odoc.masked_attention_bwd(q64, k64, v64, do64, vis, scale)
+    o_all, lse_all = odoc.masked_attention(q64, k64, v64, vis, scale)
+    kc = runner.chunk_kv(to_device(k, "bf16"), kind, N)
+    vc = runner.chunk_kv(to_device(v, "bf16"), kind, N)
+    dkc = torch.zeros((N, 1, S // N, 2, 128), device="cuda")
+    dvc = torch.zeros_like(dkc)
+    dq_all = np.zeros_like(q64)
+    for rank in range(N):
+        qp = opart.partition_map(kind, S, N, rank)
+        desc, _ = ra.ring_desc(b=1, n_q=8, n_kv=2, d=128, dtype=ra.RA_BF16, causal=True,
+                               kind=kind, S=S, N=N, rank=rank, doc_start=ds)
+        ws = torch.empty(ra.ra_ring_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        dq = torch.empty((1, S // N, 8, 128), device="cuda")
+        ra.ra_ring_bwd(desc, to_device(q_all[:, qp], "bf16"), kc, vc,
+                       torch.from_numpy(o_all[:, qp].astype(np.float32)).cuda(),
+                       torch.from_numpy(lse_all[:, qp].astype(np.float32)).cuda(),
+                       to_device(do_all[:, qp], "bf16"), dq, dkc, dvc, ws)
+        torch.cuda.synchronize()
+        dq_all[:, qp] = dq.cpu().numpy()
+    dk = np.zeros_like(k64)
+    dv = np.zeros_like(v64)
+    for j in range(N):
+        pj = opart.partition_map(kind, S, N, j)
+        dk[:, pj] = dkc[j].cpu().numpy()
+        dv[:, pj] = dvc[j].cpu().numpy()
+    for got, w, name in ((dq_all, want[0], "dq"), (dk, want[1], "dk"), (dv, want[2], "dv")):
+        err, mag = _grad_close(got, w, name)
+        print(f"  {name}: max err {err:.2e} (max |ref| {mag:.2e})", flush=True)
+
+
+def test_allgather_bwd_workload_sampled_rows_and_invariant():
+    """Full-size all-gather backward (32K, 14 documents): dq on 64 sampled rows
+    x all heads against the oracle (dq of a row depends on that row only), and
+    the invariant sum_j dk_j = 0 (each query's dx sums to zero over its keys)
+    over the rank's whole contribution."""
+    w = synth.ALLGATHER_WORKLOADS["llama3_8b_32k_allgather_docs"]
+    print(f"workload {w.name} backward", flush=True)
+    inp = synth.draw(w)
+    lengths = synth.doc_lengths(w.S, w.seed)
+    q, kc, vc = runner.ring_inputs(inp.q, inp.k, inp.v, w.dtype, w.kind, w.N, "cuda")
+    ds = torch.from_numpy(runner.doc_start_positions(lengths)).cuda()
+    call = runner.AllGatherCall(q, kc, vc, kind=w.kind, S=w.S, N=w.N, rank=w.rank, causal=True,
+                                scale=w.scale, doc_start=ds)
+    o, lse = call()
+    rng = np.random.default_rng(w.seed + 1000)
+    do_bits = synth.bf16_bits(rng.standard_normal(tuple(q.shape), dtype=np.float32))
+    desc, _ = ra.ring_desc(b=1, n_q=w.n_q, n_kv=w.n_kv, d=w.d, dtype=ra.RA_BF16, causal=True,
+                           kind=w.kind, S=w.S, N=w.N, rank=w.rank, scale=w.scale, doc_start=ds)
+    ws = torch.empty(ra.ra_allgather_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    dq = torch.empty(tuple(q.shape), device="cuda")
+    dkc = torch.zeros(tuple(kc.shape), device="cuda")
+    dvc = torch.zeros_like(dkc)
+    ra.ra_allgather_bwd(desc, q, kc, vc, o, lse, to_device(do_bits, "bf16"), dq, dkc, dvc, ws)
+    torch.cuda.synchronize()
+    dq, dk = dq.cpu().numpy(), dkc.cpu().numpy().astype(np.float64)
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and torch.isfinite(dvc).all()
+    # invariant: sum over every key of dk (per batch, kv head and channel) is 0
+    tot = dk.sum(axis=(0, 2))
+    mag = np.abs(dk).sum(axis=(0, 2))
+    assert np.max(np.abs(tot) / mag) < 1e-3, np.max(np.abs(tot) / mag)
+    c = w.c
+    rows = synth.sample_rows(c, 64, w.seed, must=[0, c // 2, c - 1])
+    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)
+    ids = odoc.doc_ids_from_lengths(lengths)
+    do64 = synth.bf16_to_f32(do_bits).astype(np.float64)
+    vis = odoc.visible_docs(q_pos[rows], np.arange(w.S), ids, True)
+    rq, _, _ = odoc.masked_attention_bwd(inp.q64[:, rows], inp.k64, inp.v64, do64[:, rows], vis,
+                                         w.scale)
+    err, m = _grad_close(dq[:, rows], rq, "dq rows")
+    print(f"  dq rows {len(rows)}: max err {err:.2e} (max |ref| {m:.2e}); "
+          f"max |sum dk| / sum |dk| {np.max(np.abs(tot) / mag):.2e}", flush=True)
