@@ -151,3 +151,34 @@ def ring_attention_bwd(q, k, v, do, o, lse, kind, S, N, rank, causal, scale):
         dk_chunks[src] += dk_b
         dv_chunks[src] += dv_b
     return dq, dk_chunks, dv_chunks
+
+
+def rows_dq(q_rows, k, v, do_rows, q_pos_rows, kv_pos, causal, scale):
+    """dq of chosen query rows only, by the same chain rule as
+    :func:`naive_attention_bwd` (a row's dq depends on that row alone:
+    dq = scale * sum_j p_j (dp_j - D) k_j with p its softmax over the visible
+    keys, dp_j = do . v_j, D = do . o). For full-size spot checks: each key /
+    value head is copied once into contiguous memory for its query heads.
+    Returns [b, r, n_q, d] float64."""
+    q_rows, do_rows = _as64(q_rows, do_rows)
+    b, r, n_q, d = q_rows.shape
+    n_kv = k.shape[2]
+    g = n_q // n_kv
+    dq = np.zeros_like(q_rows)
+    if r == 0 or k.shape[1] == 0:
+        return dq
+    vis = visible(q_pos_rows, kv_pos, causal)
+    has_key = vis.any(axis=1)
+    for bi in range(b):
+        for kvh in range(n_kv):
+            kk = np.ascontiguousarray(k[bi, :, kvh, :], dtype=np.float64)
+            vv = np.ascontiguousarray(v[bi, :, kvh, :], dtype=np.float64)
+            for h in range(kvh * g, (kvh + 1) * g):
+                x = np.where(vis, scale * (q_rows[bi, :, h, :] @ kk.T), -np.inf)
+                m = np.where(has_key, x.max(axis=1), 0.0)
+                e = np.exp(x - m[:, None])
+                p = e / np.where(has_key, e.sum(axis=1), 1.0)[:, None]
+                D = np.sum(do_rows[bi, :, h, :] * (p @ vv), axis=1)
+                dx = p * (do_rows[bi, :, h, :] @ vv.T - D[:, None])
+                dq[bi, :, h, :] = scale * (dx @ kk)
+    return dq

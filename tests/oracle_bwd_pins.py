@@ -196,5 +196,20 @@ def pin_bwd_single_key(B):
         assert 0 < p_last <= 1
 
 
+def pin_bwd_rows_dq(B):
+    """The row-subset dq equals the full backward's dq on those rows."""
+    rng = np.random.default_rng(107)
+    for causal in (True, False):
+        c, s, n_q, n_kv, d = 9, 14, 6, 2, 5
+        q, k, v, do = _inputs(rng, 2, c, s, n_q, n_kv, d)
+        qp = np.sort(rng.choice(30, c, replace=False))
+        kp = np.sort(rng.choice(30, s, replace=False))
+        want = B.naive_attention_bwd(q, k, v, do, qp, kp, causal, 0.4)[0]
+        rows = np.array([0, 3, 4, 8])
+        got = B.rows_dq(q[:, rows], k, v, do[:, rows], qp[rows], kp, causal, 0.4)
+        assert np.max(np.abs(got - want[:, rows])) < 1e-12, f"rows_dq causal={causal}"
+
+
 BACKWARD_PINS = [pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_invariants,
-                 pin_bwd_blocks_sum_to_naive, pin_bwd_ring_all_ranks, pin_bwd_single_key]
+                 pin_bwd_blocks_sum_to_naive, pin_bwd_ring_all_ranks, pin_bwd_single_key,
+                 pin_bwd_rows_dq]

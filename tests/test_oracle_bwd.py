@@ -19,6 +19,7 @@ def namespace():
         block_attention_bwd=lambda *a: backward.block_attention_bwd(*a),
         delta=lambda *a: backward.delta(*a),
         ring_attention_bwd=lambda *a: backward.ring_attention_bwd(*a),
+        rows_dq=lambda *a: backward.rows_dq(*a),
         partition_map=lambda *a: partition.partition_map(*a),
     )
 
@@ -92,7 +93,15 @@ def ring_bwd_wrong_chunk(q, k, v, do, o, lse, kind, S, N, rank, causal, scale):
     return dq, np.roll(dkc, 1, axis=0), np.roll(dvc, 1, axis=0)
 
 
+real_rows_dq = backward.rows_dq
+
+
+def rows_dq_no_scale(q, k, v, do, qp, kp, causal, scale):
+    return real_rows_dq(q, k, v, do, qp, kp, causal, scale) / scale
+
+
 MUTANTS = {
+    "rows_dq_no_scale": ("rows_dq", rows_dq_no_scale),
     "naive_bwd_no_delta": ("naive_attention_bwd", naive_bwd_no_delta),
     "naive_bwd_sign": ("naive_attention_bwd", naive_bwd_sign),
     "naive_bwd_dk_unscaled": ("naive_attention_bwd", naive_bwd_dk_unscaled),
