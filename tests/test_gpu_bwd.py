@@ -184,3 +184,47 @@ def test_ring_bwd_all_ranks_reassemble_sequence_gradients(case):
         dv[:, pj] = dvh[j]
     grad_close(dk, want[1], f"{case} dk")
     grad_close(dv, want[2], f"{case} dv")
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_32k_zigzag", "llama3_70b_128k_zigzag"])
+def test_full_workload_bwd_sampled_rows_and_invariant(name):
+    """The ring backward at full size in the benchmark's configuration: dq on 32
+    sampled rows x all heads against the oracle (a row's dq depends on that row
+    only), and sum_j dk_j = 0 over the rank's whole contribution to every block
+    (each query's dx sums to zero over its visible keys)."""
+    w = synth.WORKLOADS[name]
+    print(f"workload {w.name} backward", flush=True)
+    inp = synth.draw(w)
+    q, kc, vc = runner.ring_inputs(inp.q, inp.k, inp.v, w.dtype, w.kind, w.N, "cuda")
+    call = runner.RingCall(q, kc, vc, kind=w.kind, S=w.S, N=w.N, rank=w.rank, causal=w.causal,
+                           scale=w.scale)
+    o, lse = call()
+    rng = np.random.default_rng(w.seed + 1000)
+    do_bits = synth.bf16_bits(rng.standard_normal(tuple(q.shape), dtype=np.float32))
+    desc, _ = ra.ring_desc(b=w.b, n_q=w.n_q, n_kv=w.n_kv, d=w.d, dtype=ra.RA_BF16,
+                           causal=w.causal, kind=w.kind, S=w.S, N=w.N, rank=w.rank,
+                           scale=w.scale)
+    ws = torch.empty(ra.ra_ring_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    dq = torch.empty(tuple(q.shape), device="cuda")
+    dkc = torch.zeros(tuple(kc.shape), device="cuda")
+    dvc = torch.zeros_like(dkc)
+    ra.ra_ring_bwd(desc, q, kc, vc, o, lse, runner.host_to_device(do_bits, "bf16", "cuda"), dq,
+                   dkc, dvc, ws)
+    torch.cuda.synchronize()
+    dq = dq.cpu().numpy()
+    dk = dkc.cpu().numpy().astype(np.float64)
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and torch.isfinite(dvc).all()
+    del call, q, kc, vc, dkc, dvc, ws
+    torch.cuda.empty_cache()
+    tot = dk.sum(axis=(0, 1, 2))          # [n_kv, d]: every block, batch and key
+    mag = np.abs(dk).sum(axis=(0, 1, 2))
+    assert np.max(np.abs(tot) / mag) < 1e-3, np.max(np.abs(tot) / mag)
+    c = w.c
+    rows = synth.sample_rows(c, 32, w.seed, must=[0, c // 2 - 1, c // 2, c - 1])
+    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)
+    do64 = synth.bf16_to_f32(do_bits).astype(np.float64)
+    rq = obwd.rows_dq(inp.q64[:, rows], inp.k64, inp.v64, do64[:, rows], q_pos[rows],
+                      np.arange(w.S), w.causal, w.scale)
+    err, m = grad_close(dq[:, rows], rq, f"{name} dq rows")
+    print(f"  dq rows {len(rows)}: max err {err:.2e} (max |ref| {m:.2e}); "
+          f"max |sum dk| / sum |dk| {np.max(np.abs(tot) / mag):.2e}", flush=True)
