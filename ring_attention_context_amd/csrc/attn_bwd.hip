@@ -568,112 +568,148 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
 
-  // One 32-row sub-block (rows rb .. rb+31 of the staged block). S
-  // accumulator: lane holds key `col`; element a holds sub-block row
+  // Software pipeline over 32-row sub-blocks (rows rb .. rb+31 of a staged
+  // block). One wave per SIMD, so the wave itself must overlap its LDS
+  // traffic with its MFMAs:
+  //   A: S = Q K^T and dP = dO V^T from Q, dO rows read during the previous
+  //      sub-block's C; then the transposing reads of Q^T, dO^T and the
+  //      rows' lse, D, which land while the MFMAs run;
+  //   B: P and dS on the VALU;
+  //   C: dV^T += dO^T P and dK^T += Q^T dS; then the next sub-block's Q, dO
+  //      rows are read, landing while these MFMAs run.
+  // The block barrier sits between B and C of a block's second sub-block:
+  // no wave reads that block's stage any more, so block it+3 streams into
+  // it, and the next block (landed) feeds the rows read after C.
+  // S accumulator: lane holds key `col`; element a holds sub-block row
   // (a/4)*8 + hi*4 + a%4.
-  auto process_sub = [&](int64_t q0, int rb, auto stage) INLINE {
+  bf16x8 qa[D / 16], da[D / 16];
+  auto read_rows = [&](auto stage, int rb) INLINE {
+    const unsigned char *qb = q_stage(stage) + rb * ROW_B;
+    const unsigned char *db = d_stage(stage) + rb * ROW_B;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      qa[ds] = *reinterpret_cast<const bf16x8 *>(qb + qoff[ds]);
+      da[ds] = *reinterpret_cast<const bf16x8 *>(db + qoff[ds]);
+    }
+  };
+  auto sub = [&](int it, int64_t q0, int rb, auto stage, bool last_in_blk) INLINE {
     const int32_t *pp = p_stage(stage) + rb;
-    const int64_t qlim = a.s_q - q0 - rb;     // rows past the sequence are masked
-    if (qlim <= 0) return;
     const int32_t *lp = lo_stage(stage) + rb;
+    const int64_t qlim = a.s_q - q0 - rb;     // rows past the sequence are masked
     const int64_t last = min<int64_t>(KV_SUB, qlim) - 1;
-    // Whole sub-block before the wave's first key (causal), or every query's
-    // document starting after the wave's last key: nothing visible.
-    if (a.causal && pp[last] < w_kmin) return;
-    if (DOC && lp[0] > w_kmax) return;
-    if (DOC) any = true;
-    const unsigned char *qb = q_stage(stage);
-    const unsigned char *db = d_stage(stage);
-    // Every LDS operand of the sub-block is read up front (one wave per SIMD:
-    // a read issued just before its MFMA would expose the whole LDS latency).
-    bf16x8 qa[D / 16], da[D / 16], qt[2][D / 32], dt[2][D / 32];
+    // Nothing to do: no keys, no rows, the whole sub-block before the wave's
+    // first key (causal), or every query's document starting after the
+    // wave's last key.
+    bool skip = !wave_has_keys || qlim <= 0;
+    if (!skip && a.causal && pp[last] < w_kmin) skip = true;
+    if (!skip && DOC && lp[0] > w_kmax) skip = true;
+    // some query sees only part of the keys (diagonal, or a document start
+    // inside them); decided before the reads below, whose wait it would share
+    const bool diag = !skip && ((a.causal && pp[0] < w_kmax) || (DOC && lp[last] > w_kmin));
+    bf16x8 qt[2][D / 32], dt[2][D / 32], pb[2], dsb[2];
+    if (!skip) {
+      if (DOC) any = true;
+      // ---- A ----
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      qa[ds] = *reinterpret_cast<const bf16x8 *>(qb + rb * ROW_B + qoff[ds]);
-      da[ds] = *reinterpret_cast<const bf16x8 *>(db + rb * ROW_B + qoff[ds]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int dblk = 0; dblk < D / 32; ++dblk) {
-        dt[ks][dblk] = tr_read(db, toff, dblk, rb + ks * 16);
-        qt[ks][dblk] = tr_read(qb, toff, dblk, rb + ks * 16);
+      for (int ds = 0; ds < D / 16; ++ds) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ds], kreg[ds], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ds], vreg[ds], dp, 0, 0, 0);
       }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 s = f32x16{}, dp = f32x16{};
+      __builtin_amdgcn_sched_barrier(0);
+      const unsigned char *qb = q_stage(stage);
+      const unsigned char *db = d_stage(stage);
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ds], kreg[ds], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ds], vreg[ds], dp, 0, 0, 0);
-    }
-    const float *ll = l_stage(stage) + rb;
-    const float *ee = e_stage(stage) + rb;
-    const bool ragged = qlim < KV_SUB;
-    // some query sees only part of the keys (diagonal, or a document start inside them)
-    const bool diag = (a.causal && pp[0] < w_kmax) || (DOC && lp[last] > w_kmin);
-    bf16x8 pb[2], dsb[2];
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int r0 = e4 * 8 + hi * 4;
-      const float4 l4 = *reinterpret_cast<const float4 *>(ll + r0);
-      const float4 d4 = *reinterpret_cast<const float4 *>(ee + r0);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-      int32_t qp[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-      int32_t ql[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
-      if (diag) {
-        const int4 p4 = *reinterpret_cast<const int4 *>(pp + r0);
-        qp[0] = p4.x; qp[1] = p4.y; qp[2] = p4.z; qp[3] = p4.w;
-        if (DOC) {
-          const int4 o4 = *reinterpret_cast<const int4 *>(lp + r0);
-          ql[0] = o4.x; ql[1] = o4.y; ql[2] = o4.z; ql[3] = o4.w;
+        for (int dblk = 0; dblk < D / 32; ++dblk) {
+          dt[ks][dblk] = tr_read(db, toff, dblk, rb + ks * 16);
+          qt[ks][dblk] = tr_read(qb, toff, dblk, rb + ks * 16);
+        }
+      const float *ll = l_stage(stage) + rb;
+      const float *ee = e_stage(stage) + rb;
+      float4 l4[4], d4[4];
+      int4 p4[4], o4[4];
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int r0 = e4 * 8 + hi * 4;
+        l4[e4] = *reinterpret_cast<const float4 *>(ll + r0);
+        d4[e4] = *reinterpret_cast<const float4 *>(ee + r0);
+        p4[e4] = int4{INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+        o4[e4] = int4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+        if (diag) {
+          p4[e4] = *reinterpret_cast<const int4 *>(pp + r0);
+          if (DOC) o4[e4] = *reinterpret_cast<const int4 *>(lp + r0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- B ----
+      const bool ragged = qlim < KV_SUB;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int el = e4 * 4 + j;
-        float x = s[el];
-        const bool out =
-            ((ragged | diag) & ((r0 + j >= qlim) | (kpos > qp[j]) | (kpos < ql[j]))) | !key_ok;
-        x = out ? -INFINITY : x;
-        const float p = exp2_fast(fmaf(x, sl2, -lse_log2(lv[j])));
-        const float dsv = p * (dp[el] - dv4[j]);
-        pb[el >> 3][el & 7] = static_cast<__bf16>(p);
-        dsb[el >> 3][el & 7] = static_cast<__bf16>(dsv);
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int r0 = e4 * 8 + hi * 4;
+        const float lv[4] = {l4[e4].x, l4[e4].y, l4[e4].z, l4[e4].w};
+        const float dv4[4] = {d4[e4].x, d4[e4].y, d4[e4].z, d4[e4].w};
+        const int32_t qp[4] = {p4[e4].x, p4[e4].y, p4[e4].z, p4[e4].w};
+        const int32_t ql[4] = {o4[e4].x, o4[e4].y, o4[e4].z, o4[e4].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int el = e4 * 4 + j;
+          float x = s[el];
+          const bool out =
+              ((ragged | diag) & ((r0 + j >= qlim) | (kpos > qp[j]) | (kpos < ql[j]))) | !key_ok;
+          x = out ? -INFINITY : x;
+          const float p = exp2_fast(fmaf(x, sl2, -lse_log2(lv[j])));
+          const float dsv = p * (dp[el] - dv4[j]);
+          pb[el >> 3][el & 7] = static_cast<__bf16>(p);
+          dsb[el >> 3][el & 7] = static_cast<__bf16>(dsv);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS: A = dO^T / Q^T by the transposing read,
-    // B = P / dS (k-slots = queries of the sub-block's 16-row steps).
+    if (last_in_blk) {
+      // Block it+1 has landed everywhere; every wave is done with block it.
+      wait_own_loads();
+      __syncthreads();
+      if (it + 3 < n_it) issue_blk(it + 3, stage);
+    }
+    if (!skip) {
+      // ---- C ---- dV^T += dO^T P and dK^T += Q^T dS: A = dO^T / Q^T by the
+      // transposing read, B = P / dS (k-slots = queries of 16-row steps).
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int dblk = 0; dblk < D / 32; ++dblk) {
-        dv[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[ks][dblk], pb[ks], dv[dblk], 0, 0, 0);
-        dk[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[ks][dblk], dsb[ks], dk[dblk], 0, 0, 0);
-      }
-  };
-  auto process = [&](int it, auto stage) INLINE {
-    int64_t q0;
-    int h;
-    blk_of(it, &q0, &h);
-    (void)h;
-    process_sub(q0, 0, stage);
-    process_sub(q0, KV_SUB, stage);
+        for (int dblk = 0; dblk < D / 32; ++dblk) {
+          dv[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[ks][dblk], pb[ks], dv[dblk], 0, 0, 0);
+          dk[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[ks][dblk], dsb[ks], dk[dblk], 0, 0, 0);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   using St0 = std::integral_constant<int, 0>;
   using St1 = std::integral_constant<int, 1>;
   using St2 = std::integral_constant<int, 2>;
+  // Block it lives in stage it % 3. Blocks 0..2 start streaming now; block
+  // it+3 is issued at block it's barrier.
   if (n_it > 0) issue_blk(0, St0{});
   if (n_it > 1) issue_blk(1, St1{});
+  if (n_it > 2) issue_blk(2, St2{});
+  wait_own_loads();
+  __syncthreads();
+  if (n_it > 0) read_rows(St0{}, 0);
   auto step = [&](auto stage_c, int it) INLINE {
     constexpr int S = decltype(stage_c)::value;
     using SC = std::integral_constant<int, S>;
-    using SL = std::integral_constant<int, (S + 2) % 3>;
-    wait_own_loads();
-    __syncthreads();
-    if (it + 2 < n_it) issue_blk(it + 2, SL{});
-    if (wave_has_keys) process(it, SC{});
+    using SN = std::integral_constant<int, (S + 1) % 3>;
+    int64_t q0;
+    int h;
+    blk_of(it, &q0, &h);
+    (void)h;
+    sub(it, q0, 0, SC{}, false);
+    read_rows(SC{}, KV_SUB);
+    sub(it, q0, KV_SUB, SC{}, true);
+    if (it + 1 < n_it) read_rows(SN{}, 0);
   };
   for (int it = 0; it < n_it; it += 3) {
     step(St0{}, it);
