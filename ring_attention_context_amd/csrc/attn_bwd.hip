@@ -582,7 +582,11 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // it, and the next block (landed) feeds the rows read after C.
   // S accumulator: lane holds key `col`; element a holds sub-block row
   // (a/4)*8 + hi*4 + a%4.
+  // Rows qa, da and the rows' lse and D (element e4*4 + j of the S
+  // accumulator is row e4*8 + hi*4 + j) of the next sub-block.
   bf16x8 qa[D / 16], da[D / 16];
+  float4 l4[4], d4[4];
+  const bool w_ragged = w_key0 + KV_KW > a.s_kv;   // some key of the wave past the block
   auto read_rows = [&](auto stage, int rb) INLINE {
     const unsigned char *qb = q_stage(stage) + rb * ROW_B;
     const unsigned char *db = d_stage(stage) + rb * ROW_B;
@@ -590,6 +594,13 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for (int ds = 0; ds < D / 16; ++ds) {
       qa[ds] = *reinterpret_cast<const bf16x8 *>(qb + qoff[ds]);
       da[ds] = *reinterpret_cast<const bf16x8 *>(db + qoff[ds]);
+    }
+    const float *ll = l_stage(stage) + rb;
+    const float *ee = e_stage(stage) + rb;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      l4[e4] = *reinterpret_cast<const float4 *>(ll + e4 * 8 + hi * 4);
+      d4[e4] = *reinterpret_cast<const float4 *>(ee + e4 * 8 + hi * 4);
     }
   };
   auto sub = [&](int it, int64_t q0, int rb, auto stage, bool last_in_blk) INLINE {
@@ -609,8 +620,15 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     bf16x8 qt[2][D / 32], dt[2][D / 32], pb[2], dsb[2];
     if (!skip) {
       if (DOC) any = true;
-      // ---- A ----
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // ---- A ---- (dP starts from -D, so it comes out as dP - D)
+      f32x16 s = f32x16{}, dp;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        dp[e4 * 4 + 0] = -d4[e4].x;
+        dp[e4 * 4 + 1] = -d4[e4].y;
+        dp[e4 * 4 + 2] = -d4[e4].z;
+        dp[e4 * 4 + 3] = -d4[e4].w;
+      }
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ds], kreg[ds], s, 0, 0, 0);
@@ -626,15 +644,10 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
           dt[ks][dblk] = tr_read(db, toff, dblk, rb + ks * 16);
           qt[ks][dblk] = tr_read(qb, toff, dblk, rb + ks * 16);
         }
-      const float *ll = l_stage(stage) + rb;
-      const float *ee = e_stage(stage) + rb;
-      float4 l4[4], d4[4];
       int4 p4[4], o4[4];
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int r0 = e4 * 8 + hi * 4;
-        l4[e4] = *reinterpret_cast<const float4 *>(ll + r0);
-        d4[e4] = *reinterpret_cast<const float4 *>(ee + r0);
         p4[e4] = int4{INT_MAX, INT_MAX, INT_MAX, INT_MAX};
         o4[e4] = int4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
         if (diag) {
@@ -643,28 +656,36 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      // ---- B ----
+      // ---- B ---- the element mask only where some element can be out
+      // (ragged rows or keys, the diagonal, a document start): a uniform branch.
       const bool ragged = qlim < KV_SUB;
+      auto softmax = [&](auto masked_c) INLINE {
+        constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int r0 = e4 * 8 + hi * 4;
-        const float lv[4] = {l4[e4].x, l4[e4].y, l4[e4].z, l4[e4].w};
-        const float dv4[4] = {d4[e4].x, d4[e4].y, d4[e4].z, d4[e4].w};
-        const int32_t qp[4] = {p4[e4].x, p4[e4].y, p4[e4].z, p4[e4].w};
-        const int32_t ql[4] = {o4[e4].x, o4[e4].y, o4[e4].z, o4[e4].w};
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int r0 = e4 * 8 + hi * 4;
+          const float lv[4] = {l4[e4].x, l4[e4].y, l4[e4].z, l4[e4].w};
+          const int32_t qp[4] = {p4[e4].x, p4[e4].y, p4[e4].z, p4[e4].w};
+          const int32_t ql[4] = {o4[e4].x, o4[e4].y, o4[e4].z, o4[e4].w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int el = e4 * 4 + j;
-          float x = s[el];
-          const bool out =
-              ((ragged | diag) & ((r0 + j >= qlim) | (kpos > qp[j]) | (kpos < ql[j]))) | !key_ok;
-          x = out ? -INFINITY : x;
-          const float p = exp2_fast(fmaf(x, sl2, -lse_log2(lv[j])));
-          const float dsv = p * (dp[el] - dv4[j]);
-          pb[el >> 3][el & 7] = static_cast<__bf16>(p);
-          dsb[el >> 3][el & 7] = static_cast<__bf16>(dsv);
+          for (int j = 0; j < 4; ++j) {
+            const int el = e4 * 4 + j;
+            float x = s[el];
+            if constexpr (MASKED) {
+              const bool out =
+                  (r0 + j >= qlim) | (kpos > qp[j]) | (kpos < ql[j]) | !key_ok;
+              x = out ? -INFINITY : x;
+            }
+            const float p = exp2_fast(fmaf(x, sl2, -lse_log2(lv[j])));
+            pb[el >> 3][el & 7] = static_cast<__bf16>(p);
+            dsb[el >> 3][el & 7] = static_cast<__bf16>(p * dp[el]);
+          }
         }
-      }
+      };
+      if (ragged | diag | w_ragged)
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
     }
     if (last_in_blk) {
