@@ -676,7 +676,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
                   (r0 + j >= qlim) | (kpos > qp[j]) | (kpos < ql[j]) | !key_ok;
               x = out ? -INFINITY : x;
             }
-            const float p = exp2_fast(fmaf(x, sl2, -lse_log2(lv[j])));
+            const float p = exp2_fast(fmaf(x, sl2, -lv[j]));   // lse already in log2 units
             pb[el >> 3][el & 7] = static_cast<__bf16>(p);
             dsb[el >> 3][el & 7] = static_cast<__bf16>(p * dp[el]);
           }
@@ -708,6 +708,18 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
+  // Wave 0 loads every block's lse and converts it in place to log2 units
+  // (-inf, a query with no key, to +inf so that its probabilities are 0)
+  // once its own load has landed and before any wave reads it: block 0 before
+  // the first barrier, block it+1 at the start of block it (it landed at
+  // block it-1's barrier, and the other waves read it after block it's).
+  auto prescale_lse = [&](auto stage) INLINE {
+    if (wave == 0) {
+      float *l = l_stage(stage);
+      l[lane] = lse_log2(l[lane]);
+    }
+  };
+
   using St0 = std::integral_constant<int, 0>;
   using St1 = std::integral_constant<int, 1>;
   using St2 = std::integral_constant<int, 2>;
@@ -717,6 +729,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   if (n_it > 1) issue_blk(1, St1{});
   if (n_it > 2) issue_blk(2, St2{});
   wait_own_loads();
+  if (n_it > 0) prescale_lse(St0{});
   __syncthreads();
   if (n_it > 0) read_rows(St0{}, 0);
   auto step = [&](auto stage_c, int it) INLINE {
@@ -727,6 +740,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     int h;
     blk_of(it, &q0, &h);
     (void)h;
+    if (it + 1 < n_it) prescale_lse(SN{});
     sub(it, q0, 0, SC{}, false);
     read_rows(SC{}, KV_SUB);
     sub(it, q0, KV_SUB, SC{}, true);
