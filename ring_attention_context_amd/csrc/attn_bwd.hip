@@ -620,15 +620,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     bf16x8 qt[2][D / 32], dt[2][D / 32], pb[2], dsb[2];
     if (!skip) {
       if (DOC) any = true;
-      // ---- A ---- (dP starts from -D, so it comes out as dP - D)
-      f32x16 s = f32x16{}, dp;
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        dp[e4 * 4 + 0] = -d4[e4].x;
-        dp[e4 * 4 + 1] = -d4[e4].y;
-        dp[e4 * 4 + 2] = -d4[e4].z;
-        dp[e4 * 4 + 3] = -d4[e4].w;
-      }
+      // ---- A ----
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ds], kreg[ds], s, 0, 0, 0);
@@ -665,6 +658,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
         for (int e4 = 0; e4 < 4; ++e4) {
           const int r0 = e4 * 8 + hi * 4;
           const float lv[4] = {l4[e4].x, l4[e4].y, l4[e4].z, l4[e4].w};
+          const float dv4[4] = {d4[e4].x, d4[e4].y, d4[e4].z, d4[e4].w};
           const int32_t qp[4] = {p4[e4].x, p4[e4].y, p4[e4].z, p4[e4].w};
           const int32_t ql[4] = {o4[e4].x, o4[e4].y, o4[e4].z, o4[e4].w};
 #pragma unroll
@@ -678,7 +672,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
             }
             const float p = exp2_fast(fmaf(x, sl2, -lv[j]));   // lse already in log2 units
             pb[el >> 3][el & 7] = static_cast<__bf16>(p);
-            dsb[el >> 3][el & 7] = static_cast<__bf16>(p * dp[el]);
+            dsb[el >> 3][el & 7] = static_cast<__bf16>(p * (dp[el] - dv4[j]));
           }
         }
       };
