@@ -478,25 +478,34 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     lht = lh[0] + lh[1];
   };
 
-  // O^T += V^T P^T with the V tile in `stage`.
+  // O^T += V^T P^T with the V tile in `stage`. The V operand of MFMA i is read
+  // two MFMAs ahead behind scheduling fences; left to itself the compiler
+  // waits for each read right before its MFMA.
   auto pv = [&](auto stage) INLINE {
     const unsigned char *vb = v_stage(stage);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        bf16x8 va;
-        if constexpr (VT) {
-          va = *reinterpret_cast<const bf16x8 *>(vb + voff[0][ks] + db * 32 * VT_ROW_B);
-        } else {
-          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LDS_AS bf16x4 *)(vb + voff[0][db] + ks * 16 * ROW_B));
-          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LDS_AS bf16x4 *)(vb + voff[1][db] + ks * 16 * ROW_B));
-          va = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        }
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], acc[db], 0, 0, 0);
+    constexpr int NDB = D / 32;  // d blocks per k-step
+    auto rd = [&](int i) INLINE -> bf16x8 {
+      const int ks = i / NDB, db = i % NDB;
+      if constexpr (VT) {
+        return *reinterpret_cast<const bf16x8 *>(vb + voff[0][ks] + db * 32 * VT_ROW_B);
+      } else {
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(vb + voff[0][db] + ks * 16 * ROW_B));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(vb + voff[1][db] + ks * 16 * ROW_B));
+        return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       }
+    };
+    bf16x8 va[3];
+    va[0] = rd(0);
+    va[1] = rd(1);
+#pragma unroll
+    for (int i = 0; i < 4 * NDB; ++i) {
+      if (i + 2 < 4 * NDB) va[(i + 2) % 3] = rd(i + 2);
+      acc[i % NDB] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], pb[i / NDB], acc[i % NDB], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // Phase 1 of tile t: scores of tile t+1 (K in stage `sn`) on the matrix
