@@ -20,9 +20,12 @@
 //     key/value head (GQA), so every K/V tile staged in LDS serves all eight
 //     waves (two per SIMD);
 //   * K/V tiles of 64 keys go from HBM straight into LDS (buffer loads with
-//     the LDS destination, no register staging) through a ring of four
-//     stages, one barrier per tile; out-of-range keys come back as zeros from
-//     the buffer descriptor's bounds check;
+//     the LDS destination, no register staging), K and V each through a ring
+//     of four stages, one barrier per tile; out-of-range keys come back as
+//     zeros from the buffer descriptor's bounds check. K is consumed a step
+//     before V, so K is issued three tiles ahead and V two, and every load
+//     has two steps to land: the barrier waits only for loads older than the
+//     previous step's (a fence-free barrier; __syncthreads would drain all);
 //   * K rows are row-major in LDS with the 16-byte chunks of each 256-byte row
 //     XOR-swizzled by the row index, so the operand reads (ds_read_b128) are
 //     bank-conflict free. V comes either row-major (read with the gfx950
@@ -41,8 +44,8 @@
 //     t+1 interleaved, k-step by k-step, with the exponentials of tile t;
 //     phase 2 issues the P V MFMAs of tile t. Waves w and w+4 share a SIMD; the second group runs the two phases
 //     in the opposite order (P V of tile t-1 first), so the pair overlaps one
-//     wave's exponentials with the other's MFMAs. The fourth LDS stage keeps
-//     tile t-1 resident for that group while tile t+2 streams in;
+//     wave's exponentials with the other's MFMAs. V of tile t-1 therefore
+//     stays resident for that group while V of tile t+2 streams in;
 //   * exponentials run in base 2 (v_exp_f32) with the scale folded into one
 //     FMA. The reference of the exponentials is updated lazily from the tile
 //     sum instead of a per-tile max: probabilities are formed against the
@@ -144,21 +147,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                            BUF_DWORD3);
 }
 
-// Waits until this wave's own HBM->LDS loads have landed (vmcnt = 0; the other
-// counters are left alone). A barrier after it publishes the data to all waves.
-__device__ __forceinline__ void wait_own_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Waits until at most n (0..5) of this wave's HBM->LDS loads are still in
+// flight: the n most recent ones (loads complete in order). Only vmcnt is
+// waited on. A barrier after it publishes the older loads to all waves.
+__device__ __forceinline__ void wait_loads_upto(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+  }
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for every load still in flight). The empty asm statements keep
+// the compiler from moving LDS accesses across it; LDS reads issued before it
+// have been consumed, so they are complete.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // DOC: a document mask is given (a.q_lo); without it the mask code compiles away.
 template <int HW, bool VT, bool DOC>
 __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
-  // One LDS object per stage and operand: the compiler then sees that the
-  // asynchronous loads into one stage never alias the reads of the others and
-  // does not drain them before every LDS read.
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE_B], k_lds1[TILE_B],
-      k_lds2[TILE_B], k_lds3[TILE_B];
+  // One LDS object per stage and operand (the key positions of a tile sit
+  // after its K rows): the compiler then sees that the asynchronous loads into
+  // one stage never alias the reads of the others and waits for exactly the
+  // loads a read depends on. It tells at most eight such objects apart.
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE_B + BK * 4],
+      k_lds1[TILE_B + BK * 4], k_lds2[TILE_B + BK * 4], k_lds3[TILE_B + BK * 4];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE_B], v_lds1[TILE_B],
       v_lds2[TILE_B], v_lds3[TILE_B];
-  __shared__ __attribute__((aligned(16))) int32_t p_lds0[BK], p_lds1[BK], p_lds2[BK], p_lds3[BK];
   auto k_stage = [&](auto s) INLINE -> unsigned char * {
     constexpr int v = decltype(s)::value;
     return v == 0 ? k_lds0 : v == 1 ? k_lds1 : v == 2 ? k_lds2 : k_lds3;
@@ -168,13 +191,12 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     return v == 0 ? v_lds0 : v == 1 ? v_lds1 : v == 2 ? v_lds2 : v_lds3;
   };
   auto p_stage = [&](auto s) INLINE -> int32_t * {
-    constexpr int v = decltype(s)::value;
-    return v == 0 ? p_lds0 : v == 1 ? p_lds1 : v == 2 ? p_lds2 : p_lds3;
+    return reinterpret_cast<int32_t *>(k_stage(s) + TILE_B);
   };
 
   constexpr int TB = WAVES / HW;  // 32-token blocks per workgroup
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int lane = tid & 63;
   const int col = lane & 31;  // query within the wave
   const int hi = lane >> 5;   // which half of the MFMA k-slots this lane holds
@@ -288,11 +310,27 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     const int vrow = 8 * (wave + WAVES * i) + (lane >> 3);
     vgoff[i] = static_cast<uint32_t>(vrow * vt_stride + (((lane & 7) ^ swz_vt(vrow)) << 4));
   }
-  auto issue_tile = [&](int t, auto stage) INLINE {
+  // K rows (and key positions) of tile t into K stage `stage`: LOADS_PER_WAVE
+  // loads per wave, plus one for wave 0 when causal.
+  auto issue_k = [&](int t, auto stage) INLINE {
     const int64_t key0 = kbeg + static_cast<int64_t>(t) * BK;
     const int64_t left = a.s_kv - key0;  // rows before the end of the block
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + kv_base + key0 * kv_row_bytes,
                                                 (left - 1) * kv_row_bytes + D * 2);
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (LDS_AS void *)(k_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16, goff[i], 0, 0, 0);
+    if (a.causal && wave == 0) {
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.kv_pos + key0, left * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (LDS_AS void *)p_stage(stage), 4, lane * 4,
+                                               0, 0, 0);
+    }
+  };
+  // V (or V^T) of tile t into V stage `stage`: LOADS_PER_WAVE loads per wave.
+  auto issue_v = [&](int t, auto stage) INLINE {
+    const int64_t key0 = kbeg + static_cast<int64_t>(t) * BK;
+    const int64_t left = a.s_kv - key0;
     // V^T: keys past the block in a d-row read the next d-row's first keys
     // (finite values that meet a zero probability) or, for the last row,
     // zeros from the bounds check.
@@ -301,8 +339,6 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
            : make_rsrc(vg + kv_base + key0 * kv_row_bytes, (left - 1) * kv_row_bytes + D * 2);
 #pragma unroll
     for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (LDS_AS void *)(k_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16, goff[i], 0, 0, 0);
       if constexpr (VT)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rv, (LDS_AS void *)(v_stage(stage) + (wave + WAVES * i) * 1024), 16, vgoff[i], 0, 0, 0);
@@ -310,12 +346,9 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rv, (LDS_AS void *)(v_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16, goff[i], 0, 0, 0);
     }
-    if (a.causal && wave == 0) {
-      const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.kv_pos + key0, left * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (LDS_AS void *)p_stage(stage), 4, lane * 4,
-                                               0, 0, 0);
-    }
   };
+  const int nk = LOADS_PER_WAVE + (a.causal && wave == 0 ? 1 : 0);  // loads per issue_k
+  constexpr int nv = LOADS_PER_WAVE;                                  // loads per issue_v
 
   // ---- running state: one query per lane ----
   f32x16 acc[D / 32];
@@ -549,10 +582,20 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   using St1 = std::integral_constant<int, 1>;
   using St2 = std::integral_constant<int, 2>;
   using St3 = std::integral_constant<int, 3>;
-  if (nt > 0) issue_tile(0, St0{});
-  if (nt > 1) issue_tile(1, St1{});
-  wait_own_loads();
-  __syncthreads();
+  // Step t issues K of tile t+3 and V of tile t+2 and needs everything issued
+  // up to step t-2, so each load has two steps to land. The prologue issues
+  // what steps -3 .. -1 would have: K0; K1, V0; K2, V1. Loads are issued
+  // unconditionally (a tile past the range reads zeros, or keys that are
+  // never used, into a free stage): the compiler's own waits before LDS reads
+  // then count the loads that follow exactly instead of assuming none did.
+  const int n_step = nk + nv;  // loads this wave issues per step
+  issue_k(0, St0{});
+  issue_k(1, St1{});
+  issue_v(0, St0{});
+  wait_loads_upto(n_step);  // K0 has landed
+  barrier_keep_loads();
+  issue_k(2, St2{});
+  issue_v(1, St1{});
   if (!done && tile_skip(St0{})) done = true;
   if (!done) {
     qk(St0{}, sA);
@@ -562,7 +605,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   static_assert(TAU == 8.f, "phase2 compares against 2^TAU");
 
   // ---- main loop: step t = 0 .. nt (step nt only finishes the second group's
-  // last P V). Tile t lives in stage t % 4; its scores are in sA (t even) or sB.
+  // last P V). Tile t lives in K and V stage t % 4; its scores are in sA (t
+  // even) or sB.
   auto step = [&](auto stage_c, int t) INLINE {
     constexpr int S = decltype(stage_c)::value;
     using SC = std::integral_constant<int, S>;
@@ -571,9 +615,13 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     using SL = std::integral_constant<int, (S + 2) % NSTAGE>;
     f32x16 *cur = (S & 1) == 0 ? sA : sB;
     f32x16 *nxt = (S & 1) == 0 ? sB : sA;
-    wait_own_loads();  // this wave's part of tile t+1 has landed ...
-    __syncthreads();   // ... and everyone's; every wave is done with tile t-2
-    if (t + 2 < nt) issue_tile(t + 2, SL{});
+    // This wave's loads up to step t-2 (K and positions of tile t+1, V of
+    // tile t) have landed, and after the barrier everyone's; every wave is done
+    // with step t-1, so K stage t-1 and V stage t-2 are free.
+    wait_loads_upto(n_step);
+    barrier_keep_loads();
+    issue_k(t + 3, SP{});
+    issue_v(t + 2, SL{});
     if (grp_b && pend) {
       phase2(t - 1, SP{}, SC{}, cur);  // scores of tile t are in `cur`
       pend = false;
@@ -586,12 +634,16 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
         phase2(t, SC{}, SN{}, nxt);
     }
   };
+  // The body always runs all four steps (steps past nt only wait, synchronise
+  // and issue loads past the range), so the loads issued between two LDS reads
+  // are the same on every path through the loop.
   for (int t = 0; t <= nt; t += NSTAGE) {
     step(St0{}, t);
-    if (t + 1 <= nt) step(St1{}, t + 1);
-    if (t + 2 <= nt) step(St2{}, t + 2);
-    if (t + 3 <= nt) step(St3{}, t + 3);
+    step(St1{}, t + 1);
+    step(St2{}, t + 2);
+    step(St3{}, t + 3);
   }
+  wait_loads_upto(0);  // the loads past the range have landed before the wave ends
   apply_rescale();
 
   // ---- epilogue: o_b = acc / l^, lse_b = (ref + log2 l) ln 2; optional merge ----
