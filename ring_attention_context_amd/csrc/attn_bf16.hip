@@ -22,10 +22,10 @@
 //   * K/V tiles of 64 keys go from HBM straight into LDS (buffer loads with
 //     the LDS destination, no register staging), K and V each through a ring
 //     of four stages, one barrier per tile; out-of-range keys come back as
-//     zeros from the buffer descriptor's bounds check. K is consumed a step
-//     before V, so K is issued three tiles ahead and V two, and every load
-//     has two steps to land: the barrier waits only for loads older than the
-//     previous step's (a fence-free barrier; __syncthreads would drain all);
+//     zeros from the buffer descriptor's bounds check. Step t loads tile t+3
+//     into the stages tile t-1 left, so every load has two steps to land:
+//     the barrier waits only for loads older than the previous step's (a
+//     fence-free barrier; __syncthreads would drain all of them);
 //   * K rows are row-major in LDS with the 16-byte chunks of each 256-byte row
 //     XOR-swizzled by the row index, so the operand reads (ds_read_b128) are
 //     bank-conflict free. V comes either row-major (read with the gfx950
@@ -40,12 +40,14 @@
 //     With V^T the K rows are read in a permuted order (bits 2 and 3 of the
 //     row swapped) so that each lane's probabilities are 8 consecutive keys,
 //     the k-slots of one 16-byte V^T read;
-//   * each tile runs in two phases: phase 1 issues the score MFMAs of tile
-//     t+1 interleaved, k-step by k-step, with the exponentials of tile t;
-//     phase 2 issues the P V MFMAs of tile t. Waves w and w+4 share a SIMD; the second group runs the two phases
-//     in the opposite order (P V of tile t-1 first), so the pair overlaps one
-//     wave's exponentials with the other's MFMAs. V of tile t-1 therefore
-//     stays resident for that group while V of tile t+2 streams in;
+//   * each step has a matrix phase, the score MFMAs of tile t+1 interleaved
+//     with the P V MFMAs of tile t (operands read a few MFMAs ahead), and a
+//     vector phase, the probabilities of the tile whose scores are at hand.
+//     Waves w and w+4 share a SIMD and run the phases in opposite orders
+//     (matrix then vector, vector then matrix), so one wave's exponentials
+//     overlap the other's MFMAs; the matrix phase runs at raised priority.
+//     The per-wave tile counts come from the key positions up front (64-lane
+//     searches), so no LDS read decides a branch;
 //   * exponentials run in base 2 (v_exp_f32) with the scale folded into one
 //     FMA. The reference of the exponentials is updated lazily from the tile
 //     sum instead of a per-tile max: probabilities are formed against the
@@ -89,6 +91,7 @@ constexpr int ROW_B = D * 2;                 // bytes per key row
 constexpr int VT_ROW_B = BK * 2;             // bytes per d-row of a V^T tile
 constexpr int TILE_B = BK * ROW_B;           // 16 KiB
 constexpr int NSTAGE = 4;
+constexpr int NDB = D / 32;                  // 32-wide d blocks of the output
 constexpr int LOADS_PER_WAVE = TILE_B / (1024 * WAVES);  // 1 KiB per wave instruction
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -116,27 +119,27 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Number of keys with position <= p in the non-decreasing kv_pos[0, n).
-__device__ __forceinline__ int64_t count_le(const int32_t *kv_pos, int64_t n, int32_t p) {
-  int64_t lo = 0, hi = n;
+// Number of keys with position <= p (LE) or < p in the non-decreasing
+// kv_pos[0, n), found by the 64 lanes of a wave together: each round probes 64
+// evenly spaced keys of the remaining range and keeps the gap between the
+// last probe that counts and the first that does not, so a range of n keys
+// takes about log64(n) dependent loads instead of the log2(n) of a binary
+// search. Call with all lanes active; the result is uniform.
+template <bool LE>
+__device__ __forceinline__ int64_t wave_count(const int32_t *kv_pos, int64_t n, int32_t p, int lane) {
+  int64_t lo = 0, hi = n;  // the count lies in [lo, hi]
   while (lo < hi) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (kv_pos[mid] <= p)
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  return lo;
-}
-// Number of keys with position < p.
-__device__ __forceinline__ int64_t count_lt(const int32_t *kv_pos, int64_t n, int32_t p) {
-  int64_t lo = 0, hi = n;
-  while (lo < hi) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (kv_pos[mid] < p)
-      lo = mid + 1;
-    else
-      hi = mid;
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t idx = lo + lane * step;
+    bool in = false;
+    if (idx < hi) {
+      const int32_t v = kv_pos[idx];
+      in = LE ? v <= p : v < p;
+    }
+    const int cnt = __popcll(__ballot(in));  // the probes that count form a prefix
+    const int64_t new_hi = min(hi, lo + cnt * step);
+    lo = cnt == 0 ? lo : lo + (cnt - 1) * step + 1;
+    hi = new_hi;
   }
   return lo;
 }
@@ -147,7 +150,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                            BUF_DWORD3);
 }
 
-// Waits until at most n (0..5) of this wave's HBM->LDS loads are still in
+// Waits until at most n (0..7) of this wave's HBM->LDS loads are still in
 // flight: the n most recent ones (loads complete in order). Only vmcnt is
 // waited on. A barrier after it publishes the older loads to all waves.
 __device__ __forceinline__ void wait_loads_upto(int n) {
@@ -157,7 +160,9 @@ __device__ __forceinline__ void wait_loads_upto(int n) {
     case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
     case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
     case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F77); break;
   }
 }
 
@@ -235,8 +240,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   int32_t w_qmin = INT_MAX - 1, w_qmax = INT_MAX - 1;
   int32_t w_lomax = INT_MIN;  // latest document start among the wave's queries
   if (a.causal) {
-    nkeys = count_le(a.kv_pos, a.s_kv, a.q_pos[wg_tok_last]);
-    if (DOC) kbeg = count_lt(a.kv_pos, a.s_kv, a.q_lo[wg_tok0]) / BK * BK;
+    nkeys = wave_count<true>(a.kv_pos, a.s_kv, a.q_pos[wg_tok_last], lane);
+    if (DOC) kbeg = wave_count<false>(a.kv_pos, a.s_kv, a.q_lo[wg_tok0], lane) / BK * BK;
     if (wave_has_rows) {
       w_qmin = a.q_pos[w_tok0];
       w_qmax = a.q_pos[w_tok_last];
@@ -244,6 +249,22 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     }
   }
   const int nt = nkeys > kbeg ? static_cast<int>((nkeys - kbeg + BK - 1) / BK) : 0;
+  // Tiles of this wave, from the same counts (positions are non-decreasing):
+  // w_nt tiles hold a key not after its last query; tiles from j_diag on hold
+  // a key after its first query, and tiles before j_doc a key before its
+  // latest document start. Those (and a ragged last tile) take the element
+  // mask.
+  int w_nt = nt, j_diag = INT_MAX, j_doc = 0;
+  if (a.causal && wave_has_rows) {
+    const int64_t c_hi = wave_count<true>(a.kv_pos, a.s_kv, w_qmax, lane);
+    w_nt = c_hi > kbeg ? min(nt, static_cast<int>((c_hi - kbeg + BK - 1) / BK)) : 0;
+    const int64_t c_lo = wave_count<true>(a.kv_pos, a.s_kv, w_qmin, lane);
+    j_diag = c_lo > kbeg ? static_cast<int>((c_lo - kbeg) / BK) : 0;
+    if (DOC) {
+      const int64_t c_d = wave_count<false>(a.kv_pos, a.s_kv, w_lomax, lane);
+      j_doc = c_d > kbeg ? static_cast<int>((c_d - kbeg + BK - 1) / BK) : 0;
+    }
+  }
 
   // ---- this lane's query: B operand of S^T = K Q^T (8 bf16 per k-step) ----
   const uint16_t *qg = static_cast<const uint16_t *>(a.q);
@@ -263,21 +284,26 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // ---- per-lane LDS offsets of the MFMA operands (within one stage) ----
   // K: lane (col, hi) reads key row krow (+32 for the second key block),
   // logical chunk 2*ds + hi.
+  // The swizzle is an XOR of the chunk index, so the offset of k-step ds is
+  // that of k-step 0 with bits 5..7 XORed by ds: one register instead of
+  // eight (kept live through the loop by `pin`, which stops the compiler from
+  // hoisting the eight XORs back out).
   const int krow = VT ? kperm(col) : col;
-  uint32_t koff[D / 16];
-#pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds)
-    koff[ds] = krow * ROW_B + ((((2 * ds + hi) ^ swz(krow & 15))) << 4);
+  uint32_t koff0 = krow * ROW_B + (((hi ^ swz(krow & 15))) << 4);
+  auto koff = [&](int ds) INLINE -> uint32_t { return koff0 ^ (static_cast<uint32_t>(ds) << 5); };
   // V^T operand of k-step ks: with V^T staged, lane (col, hi) reads d-row col
   // (+32 per d block), keys ks*16 + hi*8 .. +7. With V row-major, the
   // transposing read: in each 16-lane group gq, lane s reads 8 bytes of key
   // row r (4 rows per group) so that lane j of the group receives
   // V[k0 + 0..3][d0 + j]; call c covers keys {0..3, 8..11} + 4*(gq>>1) of a
   // 16-key step, matching the k-slots of P in the B operand.
+  // With V^T the offset of k-step ks is that of k-step 0 with bits 5..6
+  // XORed by ks, as for K.
   uint32_t voff[2][D / 32];
+  uint32_t voff0 = col * VT_ROW_B + ((hi ^ swz_vt(col)) << 4);
+  auto voff_vt = [&](int ks) INLINE -> uint32_t { return voff0 ^ (static_cast<uint32_t>(ks) << 5); };
   if constexpr (VT) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) voff[0][ks] = col * VT_ROW_B + (((2 * ks + hi) ^ swz_vt(col)) << 4);
+    (void)voff;
   } else {
     const int gq = lane >> 4, s = lane & 15;
 #pragma unroll
@@ -360,36 +386,29 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   float lt = 0.f;           // this lane's half of the current tile's sum
   float lht = 0.f;          // ... and of its bf16-rounded probabilities
   float alpha = 1.f;        // rescale factor pending for acc / l_run
-  bool done = !wave_has_rows || nt == 0;
-  bool pend = false;        // second group: P V of the previous tile still to do
-  bool have_next = false;   // tile t+1 exists and is not entirely in the future
+  bool done = !wave_has_rows || w_nt == 0;
   bf16x8 pb[4];             // probabilities of the tile whose P V is next
-  f32x16 sA[2], sB[2];      // scores of two consecutive tiles (roles alternate)
-
-  auto tile_pos = [&](auto stage, int i) INLINE -> int32_t { return p_stage(stage)[i]; };
-  // Whole tile after this wave's last query (causal): nothing visible here or later.
-  auto tile_skip = [&](auto stage) INLINE -> bool { return a.causal && tile_pos(stage, 0) > w_qmax; };
+  f32x16 s[2];              // scores of the tile whose probabilities are next
 
   // Scores S^T = K Q^T of the K tile in `stage`.
-  auto qk = [&](auto stage, f32x16 *s) INLINE {
+  auto qk = [&](auto stage) INLINE {
     const unsigned char *kb_base = k_stage(stage);
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kb_base + koff[ds] + kb * 32 * ROW_B);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kb_base + koff(ds) + kb * 32 * ROW_B);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ds], ds == 0 ? f32x16{} : s[kb], 0, 0, 0);
       }
   };
 
-  // Element mask of a diagonal or ragged tile t held in `stage` (or one that
-  // starts before a query's document). Accumulator element e4*4 + j of key
-  // block kb holds key kk + j.
-  auto mask = [&](int t, auto stage, f32x16 *s) INLINE {
+  // Element mask of tile t (positions in `stage`) when it straddles the
+  // wave's diagonal, starts before a query's document, or is the ragged last
+  // tile. Accumulator element e4*4 + j of key block kb holds key kk + j.
+  auto mask = [&](int t, auto stage) INLINE {
     const int64_t key0 = kbeg + static_cast<int64_t>(t) * BK;
     const bool ragged = key0 + BK > a.s_kv;
-    if (ragged || (a.causal && tile_pos(stage, BK - 1) > w_qmin) ||
-        (DOC && tile_pos(stage, 0) < w_lomax)) {
+    if (ragged || t >= j_diag || (DOC && t < j_doc)) {
       // Branch-free selects: key index past the block, position after the
       // query, or before the query's document.
       const int lim = ragged ? static_cast<int>(a.s_kv - key0) : BK;
@@ -410,8 +429,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  // Row max of a tile (both key halves) in log2 units.
-  auto rowmax = [&](const f32x16 *s) INLINE -> float {
+  // Row max of the scores (both key halves) in log2 units.
+  auto rowmax = [&]() INLINE -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -435,7 +454,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // (ks%2)*8 .. +7 of block ks/2. The tile sum uses the fp32 probabilities
   // (before bf16 rounding), so lse carries no bf16 error; four partial sums
   // keep the dependency chains short.
-  auto softmax = [&](const f32x16 *s) INLINE {
+  auto softmax = [&]() INLINE {
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float lp[4];
 #pragma unroll
@@ -449,6 +468,10 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
           lp[e & 3] += p;
         pb[ks][e] = static_cast<__bf16>(p);
       }
+      // Convert each k-step's probabilities as they are made, so that at most
+      // one k-step of fp32 probabilities is live (the compiler would
+      // otherwise compute all 32 first).
+      asm volatile("" : "+v"(pb[ks]));
     }
     lt = (lp[0] + lp[1]) + (lp[2] + lp[3]);
     const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
@@ -460,67 +483,30 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
         lh[e >> 2] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ks][e], pb[ks][e + 1]}, one,
                                                      lh[e >> 2], false);
     lht = lh[0] + lh[1];
+    asm volatile("" : "+v"(lt), "+v"(lht));
   };
 
-  // Phase-1 body: the score MFMAs of the next tile interleaved with the
-  // probabilities of the current one, one k-step at a time behind hard
-  // scheduling fences (left to itself the compiler clusters the MFMAs and the
-  // VALU work apart). Each k-step issues the K reads two steps ahead, the two
-  // score MFMAs, then a quarter of one key block's probabilities (4 per
-  // lane), which the VALU works through while the MFMAs run.
-  auto qk_softmax = [&](auto stage, f32x16 *s, const f32x16 *cur) INLINE {
-    const unsigned char *kb_base = k_stage(stage);
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    bf16x8 ka[3][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        ka[j][kb] = *reinterpret_cast<const bf16x8 *>(kb_base + koff[j] + kb * 32 * ROW_B);
-    float lp[4] = {0.f, 0.f, 0.f, 0.f};
-    float lh[2] = {0.f, 0.f};
-    const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      if (ds + 2 < D / 16) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          ka[(ds + 2) % 3][kb] =
-              *reinterpret_cast<const bf16x8 *>(kb_base + koff[ds + 2] + kb * 32 * ROW_B);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds % 3][kb], qreg[ds],
-                                                        ds == 0 ? f32x16{} : s[kb], 0, 0, 0);
-      // probabilities of k-slots ks = ds / 2, e = (ds % 2) * 4 .. +3
-      const int ks = ds >> 1, e0 = (ds & 1) * 4;
-      float pf[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pf[j] = exp2_fast(fmaf(cur[ks >> 1][(ks & 1) * 8 + e0 + j], sl2, -m_use));
-        lp[j] += pf[j];
-        pb[ks][e0 + j] = static_cast<__bf16>(pf[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; j += 2)
-        lh[j >> 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ks][e0 + j], pb[ks][e0 + j + 1]},
-                                                     one, lh[j >> 1], false);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    lt = (lp[0] + lp[1]) + (lp[2] + lp[3]);
-    lht = lh[0] + lh[1];
-  };
-
-  // O^T += V^T P^T with the V tile in `stage`. The V operand of MFMA i is read
-  // two MFMAs ahead behind scheduling fences; left to itself the compiler
-  // waits for each read right before its MFMA.
-  auto pv = [&](auto stage) INLINE {
-    const unsigned char *vb = v_stage(stage);
-    constexpr int NDB = D / 32;  // d blocks per k-step
+  // Matrix phase of step t: the score MFMAs of tile t+1 (K in stage `sn`)
+  // interleaved with the P V MFMAs of tile t (V in stage `sc`). Operands are
+  // read DIST MFMAs ahead behind scheduling fences; left to itself the
+  // compiler waits for each read right before its MFMA.
+  auto xphase = [&](auto sn, auto sc) INLINE {
+    constexpr int NPV = 4 * NDB;          // P V MFMAs: 4 k-steps x NDB d blocks
+    constexpr int N = 2 * NPV;            // the score MFMAs are as many
+    constexpr int DIST = 4;
+    const unsigned char *kbase = k_stage(sn);
+    const unsigned char *vb = v_stage(sc);
+    // Sequence slot i: even slots are score MFMA i/2 (k-step i/4, key block
+    // (i/2)%2), odd slots P V MFMA i/2 (k-step i/2/NDB, d block i/2%NDB).
     auto rd = [&](int i) INLINE -> bf16x8 {
-      const int ks = i / NDB, db = i % NDB;
+      if ((i & 1) == 0) {
+        const int it = i >> 1;
+        return *reinterpret_cast<const bf16x8 *>(kbase + koff(it >> 1) + (it & 1) * 32 * ROW_B);
+      }
+      const int pi = i >> 1;
+      const int ks = pi / NDB, db = pi % NDB;
       if constexpr (VT) {
-        return *reinterpret_cast<const bf16x8 *>(vb + voff[0][ks] + db * 32 * VT_ROW_B);
+        return *reinterpret_cast<const bf16x8 *>(vb + voff_vt(ks) + db * 32 * VT_ROW_B);
       } else {
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (LDS_AS bf16x4 *)(vb + voff[0][db] + ks * 16 * ROW_B));
@@ -529,115 +515,123 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
         return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       }
     };
-    bf16x8 va[3];
-    va[0] = rd(0);
-    va[1] = rd(1);
+    bf16x8 op[DIST + 1];
 #pragma unroll
-    for (int i = 0; i < 4 * NDB; ++i) {
-      if (i + 2 < 4 * NDB) va[(i + 2) % 3] = rd(i + 2);
-      acc[i % NDB] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], pb[i / NDB], acc[i % NDB], 0, 0, 0);
+    for (int i = 0; i < DIST; ++i) op[i] = rd(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + DIST < N) op[(i + DIST) % (DIST + 1)] = rd(i + DIST);
+      const bf16x8 o = op[i % (DIST + 1)];
+      if ((i & 1) == 0) {
+        const int it = i >> 1, ds = it >> 1, kb = it & 1;
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, qreg[ds], ds == 0 ? f32x16{} : s[kb], 0, 0, 0);
+      } else {
+        const int pi = i >> 1;
+        acc[pi % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, pb[pi / NDB], acc[pi % NDB], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Phase 1 of tile t: scores of tile t+1 (K in stage `sn`) on the matrix
-  // cores, probabilities of tile t (scores in `cur`) on the VALU.
-  auto phase1 = [&](int t, auto sn, const f32x16 *cur, f32x16 *nxt) INLINE {
+  // Vector phase for the tile whose (masked) scores are in `s`: probabilities
+  // and sums. The reference of the exponentials is updated
+  // lazily from the tile sum: when a row's sum exceeds 2^TAU the reference
+  // moves up by log2 of it, and the rescale of acc and the sums waits until
+  // the P V of this tile has been added (the next vector phase). A tile is
+  // redone against its true row max when a row has no reference yet or its
+  // sum leaves [0, 2^32].
+  auto yphase = [&]() INLINE {
     apply_rescale();
-    have_next = t + 1 < nt && !tile_skip(sn);
-    qk_softmax(sn, nxt, cur);
-    const float lt_row = pair_sum(lt);
+    softmax();
+    float lt_row = pair_sum(lt);
     if (__any((m_run == -INFINITY) | !(lt_row <= 0x1p32f))) {
-      // No reference yet, or a score far above it: redo the tile against its
-      // true row max (rescaling what is accumulated so far).
-      const float m_new = fmaxf(m_run, rowmax(cur));
+      const float m_new = fmaxf(m_run, rowmax());
       const float al = (m_run == -INFINITY || m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) acc[i] *= al;
       l_run *= al;
       lh_run *= al;
       m_run = m_new;
-      softmax(cur);
+      softmax();
+      lt_row = pair_sum(lt);
     }
     l_run += lt;
     lh_run += lht;
-  };
-
-  // Phase 2 of tile t: P V with V in stage `sc`; mask of tile t+1 (positions in
-  // stage `sn`); lazy reference update from tile t's sum.
-  auto phase2 = [&](int t, auto sc, auto sn, f32x16 *nxt) INLINE {
-    if (have_next) mask(t + 1, sn, nxt);
-    pv(sc);
-    const float lt_row = pair_sum(lt);
     const bool need = lt_row > 0x1p8f;  // 2^TAU
     const float lg = __builtin_amdgcn_logf(lt_row);  // log2
     alpha = need ? exp2_fast(-lg) : 1.f;
     m_run = need ? m_run + lg : m_run;
-    done = !have_next;
   };
+  static_assert(TAU == 8.f, "yphase compares against 2^TAU");
 
-  // ---- prologue: tiles 0 and 1 in flight; reference from tile 0's row max ----
+  // ---- prologue ----
   using St0 = std::integral_constant<int, 0>;
   using St1 = std::integral_constant<int, 1>;
   using St2 = std::integral_constant<int, 2>;
   using St3 = std::integral_constant<int, 3>;
-  // Step t issues K of tile t+3 and V of tile t+2 and needs everything issued
-  // up to step t-2, so each load has two steps to land. The prologue issues
-  // what steps -3 .. -1 would have: K0; K1, V0; K2, V1. Loads are issued
-  // unconditionally (a tile past the range reads zeros, or keys that are
-  // never used, into a free stage): the compiler's own waits before LDS reads
-  // then count the loads that follow exactly instead of assuming none did.
+  // Step t issues K (with positions) and V of tile t+3 into the stages tile
+  // t-1 left, and needs everything issued up to step t-2: K of tile t+1 has
+  // two steps to land, V of tile t three. The loads are issued
+  // unconditionally (a tile past the range reads zeros, or keys that are never
+  // used, into a free stage): the compiler's own waits before LDS reads then
+  // count the loads that follow exactly instead of assuming none did. The
+  // prologue issues what steps -3 .. -1 would have.
   const int n_step = nk + nv;  // loads this wave issues per step
   issue_k(0, St0{});
-  issue_k(1, St1{});
   issue_v(0, St0{});
-  wait_loads_upto(n_step);  // K0 has landed
+  issue_k(1, St1{});
+  issue_v(1, St1{});
+  wait_loads_upto(nv + nk + nv);  // K (and positions) of tile 0 have landed
   barrier_keep_loads();
   issue_k(2, St2{});
-  issue_v(1, St1{});
-  if (!done && tile_skip(St0{})) done = true;
+  issue_v(2, St2{});
   if (!done) {
-    qk(St0{}, sA);
-    mask(0, St0{}, sA);
-    m_run = rowmax(sA);
+    qk(St0{});
+    mask(0, St0{});
+    m_run = rowmax();
   }
-  static_assert(TAU == 8.f, "phase2 compares against 2^TAU");
 
-  // ---- main loop: step t = 0 .. nt (step nt only finishes the second group's
-  // last P V). Tile t lives in K and V stage t % 4; its scores are in sA (t
-  // even) or sB.
+  // ---- main loop: step t = 0 .. nt-1 ----
+  // Tile t lives in K and V stage t % 4. Each step has a matrix phase (scores
+  // of tile t+1 and P V of tile t) and a vector phase (probabilities of the
+  // tile whose scores are at hand). The two waves on a SIMD run them in
+  // opposite orders: the first group matrix then vector (tile t+1), the
+  // second vector (tile t) then matrix, so one wave's exponentials overlap the
+  // other's MFMAs. The matrix phase runs at raised priority so that its MFMAs
+  // go first.
+  if (!grp_b && !done) yphase();
   auto step = [&](auto stage_c, int t) INLINE {
     constexpr int S = decltype(stage_c)::value;
     using SC = std::integral_constant<int, S>;
     using SN = std::integral_constant<int, (S + 1) % NSTAGE>;
     using SP = std::integral_constant<int, (S + NSTAGE - 1) % NSTAGE>;
-    using SL = std::integral_constant<int, (S + 2) % NSTAGE>;
-    f32x16 *cur = (S & 1) == 0 ? sA : sB;
-    f32x16 *nxt = (S & 1) == 0 ? sB : sA;
-    // This wave's loads up to step t-2 (K and positions of tile t+1, V of
-    // tile t) have landed, and after the barrier everyone's; every wave is done
-    // with step t-1, so K stage t-1 and V stage t-2 are free.
+    // This wave's loads up to step t-2 have landed, and after the barrier
+    // everyone's; every wave is done with step t-1, so stage t-1 is free.
     wait_loads_upto(n_step);
     barrier_keep_loads();
+    asm volatile("" : "+v"(koff0), "+v"(voff0));  // pin: see koff
     issue_k(t + 3, SP{});
-    issue_v(t + 2, SL{});
-    if (grp_b && pend) {
-      phase2(t - 1, SP{}, SC{}, cur);  // scores of tile t are in `cur`
-      pend = false;
-    }
-    if (!done && t < nt) {
-      phase1(t, SN{}, cur, nxt);
-      if (grp_b)
-        pend = true;
-      else
-        phase2(t, SC{}, SN{}, nxt);
+    issue_v(t + 3, SP{});
+    if (!done) {
+      if (grp_b) yphase();
+      // After the wave's last tile the scores computed here are of a stage
+      // holding no tile of its range and are dropped: one code path keeps the
+      // accumulators in place.
+      __builtin_amdgcn_s_setprio(1);
+      xphase(SN{}, SC{});
+      __builtin_amdgcn_s_setprio(0);
+      if (t + 1 < w_nt) {
+        mask(t + 1, SN{});
+        if (!grp_b) yphase();
+      } else {
+        done = true;
+      }
     }
   };
   // The body always runs all four steps (steps past nt only wait, synchronise
   // and issue loads past the range), so the loads issued between two LDS reads
   // are the same on every path through the loop.
-  for (int t = 0; t <= nt; t += NSTAGE) {
+  for (int t = 0; t < nt; t += NSTAGE) {
     step(St0{}, t);
     step(St1{}, t + 1);
     step(St2{}, t + 2);
