@@ -76,6 +76,30 @@ __device__ __forceinline__ int64_t count_le(const int32_t *pos, int64_t n, int32
   return lo;
 }
 
+// The same counts found by the 64 lanes of a wave together: each round probes
+// 64 evenly spaced entries of the remaining range and keeps the gap between
+// the last probe that counts and the first that does not (about log64(n)
+// dependent loads). LE: entries <= p, else < p. Call with all lanes active;
+// the result is uniform.
+template <bool LE>
+__device__ __forceinline__ int64_t wave_count(const int32_t *pos, int64_t n, int32_t p, int lane) {
+  int64_t lo = 0, hi = n;  // the count lies in [lo, hi]
+  while (lo < hi) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t idx = lo + lane * step;
+    bool in = false;
+    if (idx < hi) {
+      const int32_t v = pos[idx];
+      in = LE ? v <= p : v < p;
+    }
+    const int cnt = __popcll(__ballot(in));  // the probes that count form a prefix
+    const int64_t new_hi = min(hi, lo + cnt * step);
+    lo = cnt == 0 ? lo : lo + (cnt - 1) * step + 1;
+    hi = new_hi;
+  }
+  return lo;
+}
+
 // lse in log2 units; a query with no visible key (lse = -inf) gets +inf so
 // that every probability 2^(x - lse) of it is 0.
 __device__ __forceinline__ float lse_log2(float lse) {
@@ -491,13 +515,28 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
   const float sl2 = a.scale * LOG2E;
 
-  // Q / dO rows by ds_read_b128 (row = query col), chunk 2*ds + hi.
-  uint32_t qoff[D / 16];
-#pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds)
-    qoff[ds] = col * ROW_B + ((((2 * ds + hi) ^ swz(col & 15))) << 4);
-  uint32_t toff[2][D / 32];
-  tr_offsets(lane, toff);
+  // Q / dO rows by ds_read_b128 (row = query col), chunk 2*ds + hi: the
+  // swizzle is an XOR of the chunk index, so k-step ds reads at qoff0 with
+  // bits 5..7 XORed by ds. Likewise the transposing reads of d block db are at
+  // toff0 with bits 6..7 XORed by db. (`pin` keeps the compiler from hoisting
+  // the XORs back into eight registers each.)
+  uint32_t qoff0 = col * ROW_B + (((hi ^ swz(col & 15))) << 4);
+  auto qoff = [&](int ds) INLINE -> uint32_t { return qoff0 ^ (static_cast<uint32_t>(ds) << 5); };
+  uint32_t toff0[2];
+  {
+    uint32_t toff[2][D / 32];
+    tr_offsets(lane, toff);
+    toff0[0] = toff[0][0];
+    toff0[1] = toff[1][0];
+  }
+  auto tread = [&](const unsigned char *base, int db, int row0) INLINE -> bf16x8 {
+    const uint32_t x = static_cast<uint32_t>(db) << 6;
+    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (LDS_AS bf16x4 *)(base + (toff0[0] ^ x) + row0 * ROW_B));
+    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (LDS_AS bf16x4 *)(base + (toff0[1] ^ x) + row0 * ROW_B));
+    return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+  };
 
   // ---- staging of one query block (iteration it -> head, block) ----
   const unsigned char *qbytes = static_cast<const unsigned char *>(a.q);
@@ -557,10 +596,6 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  // With a document mask most workgroups of a long sequence see few queries:
-  // a wave that processed nothing skips the dk, dv update (adding zeros).
-  // Without one the flag compiles away.
-  bool any = false;
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
@@ -568,33 +603,70 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
 
-  // Software pipeline over 32-row sub-blocks (rows rb .. rb+31 of a staged
-  // block). One wave per SIMD, so the wave itself must overlap its LDS
-  // traffic with its MFMAs:
-  //   A: S = Q K^T and dP = dO V^T from Q, dO rows read during the previous
-  //      sub-block's C; then the transposing reads of Q^T, dO^T and the
-  //      rows' lse, D, which land while the MFMAs run;
-  //   B: P and dS on the VALU;
-  //   C: dV^T += dO^T P and dK^T += Q^T dS; then the next sub-block's Q, dO
-  //      rows are read, landing while these MFMAs run.
-  // The block barrier sits between B and C of a block's second sub-block:
-  // no wave reads that block's stage any more, so block it+3 streams into
-  // it, and the next block (landed) feeds the rows read after C.
+  // ---- the wave's sub-blocks ----
+  // Sub-block n = 2 it + h holds rows 32h .. 32h+31 of the block of iteration
+  // it. A sub-block whose rows are all before the wave's first key (causal),
+  // or all start their document after its last key, or lie past the
+  // sequence, sees none of the wave's keys. In row terms the useful first rows
+  // r (multiples of 32) satisfy c_vis - 31 <= r < r_end; they form one range
+  // of blocks in the walk, whose first and last blocks may have one useless
+  // half per head (those run fully masked and add nothing). n_lo .. n_hi is
+  // that range in the walk. c_kmax / c_dmin decide which sub-blocks need the
+  // element mask.
+  int64_t c_vis = 0, c_kmax = 0, r_end = a.s_q, c_dmin = a.s_q;
+  if (a.causal && wave_has_keys) {
+    c_vis = wave_count<false>(a.q_pos, a.s_q, w_kmin, lane);
+    c_kmax = wave_count<false>(a.q_pos, a.s_q, w_kmax, lane);
+  }
+  if (DOC && wave_has_keys) {
+    r_end = min(r_end, wave_count<true>(a.q_lo, a.s_q, w_kmax, lane));
+    c_dmin = wave_count<true>(a.q_lo, a.s_q, w_kmin, lane);
+  }
+  const int64_t qb_last = qb0 + n_blk - 1;
+  int64_t R_lo = (c_vis - 31 + 31) / 32;  // ceil((c_vis - 31) / 32) for c_vis >= 0
+  if (c_vis < 31) R_lo = 0;
+  int64_t R_hi = (r_end + 31) / 32 - 1;   // last useful 32-row unit
+  R_lo = max(R_lo, 2 * qb0);
+  R_hi = min(R_hi, 2 * qb_last + 1);
+  int n_lo = 0, n_hi = 0;
+  if (wave_has_keys && n_blk > 0 && R_lo <= R_hi) {
+    const int64_t j_first = qb_last - R_hi / 2;          // walk block of the latest unit
+    const int64_t h_min = max<int64_t>(0, R_lo - 2 * (qb_last - j_first));
+    n_lo = static_cast<int>(2 * (j_first * g) + h_min);
+    const int64_t j_last = qb_last - R_lo / 2;           // walk block of the earliest unit
+    const int64_t h_max = min<int64_t>(1, R_hi - 2 * (qb_last - j_last));
+    n_hi = static_cast<int>(2 * (j_last * g + g - 1) + h_max + 1);
+  }
+  const bool any = n_lo < n_hi;
+  const bool w_ragged = w_key0 + KV_KW > a.s_kv;   // some key of the wave past the block
+
+  // ---- software pipeline over sub-blocks ----
+  // One wave per SIMD, so the wave itself must overlap its MFMAs with its
+  // vector work. Iteration n runs one stream of 32 MFMAs, A(n+1) -- S = Q K^T
+  // and dP = dO V^T of the next sub-block -- interleaved with C(n-1) --
+  // dV^T += dO^T P and dK^T += Q^T dS of the previous one -- with operands
+  // read a few MFMAs ahead, and after every MFMA the vector work of B(n): the
+  // probabilities P and dS of one element of this sub-block. Scores, P and dS
+  // are double-buffered by sub-block parity. The element mask (rare: the
+  // diagonal, ragged rows or keys, a document start) is applied to A(n+1)'s
+  // scores right after the stream.
   // S accumulator: lane holds key `col`; element a holds sub-block row
   // (a/4)*8 + hi*4 + a%4.
-  // Rows qa, da and the rows' lse and D (element e4*4 + j of the S
-  // accumulator is row e4*8 + hi*4 + j) of the next sub-block.
-  bf16x8 qa[D / 16], da[D / 16];
-  float4 l4[4], d4[4];
-  const bool w_ragged = w_key0 + KV_KW > a.s_kv;   // some key of the wave past the block
-  auto read_rows = [&](auto stage, int rb) INLINE {
-    const unsigned char *qb = q_stage(stage) + rb * ROW_B;
-    const unsigned char *db = d_stage(stage) + rb * ROW_B;
+  f32x16 s[2], dp[2];
+  bf16x8 pb[2][2], dsb[2][2];
+  // P and dS start at zero: the first C of the wave's range (of the
+  // sub-block before it) then adds nothing.
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      qa[ds] = *reinterpret_cast<const bf16x8 *>(qb + qoff[ds]);
-      da[ds] = *reinterpret_cast<const bf16x8 *>(db + qoff[ds]);
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      pb[i][j] = bf16x8{};
+      dsb[i][j] = bf16x8{};
     }
+  float4 l4[4], d4[4];  // lse (log2 units) and D of the rows of the sub-block of B
+
+  auto blk_q0 = [&](int it) INLINE -> int64_t { return (qb_last - it / g) * KV_QB; };
+  auto read_ld = [&](auto stage, int rb) INLINE {
     const float *ll = l_stage(stage) + rb;
     const float *ee = e_stage(stage) + rb;
 #pragma unroll
@@ -603,110 +675,121 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
       d4[e4] = *reinterpret_cast<const float4 *>(ee + e4 * 8 + hi * 4);
     }
   };
-  auto sub = [&](int it, int64_t q0, int rb, auto stage, bool last_in_blk) INLINE {
-    const int32_t *pp = p_stage(stage) + rb;
-    const int32_t *lp = lo_stage(stage) + rb;
-    const int64_t qlim = a.s_q - q0 - rb;     // rows past the sequence are masked
-    const int64_t last = min<int64_t>(KV_SUB, qlim) - 1;
-    // Nothing to do: no keys, no rows, the whole sub-block before the wave's
-    // first key (causal), or every query's document starting after the
-    // wave's last key.
-    bool skip = !wave_has_keys || qlim <= 0;
-    if (!skip && a.causal && pp[last] < w_kmin) skip = true;
-    if (!skip && DOC && lp[0] > w_kmax) skip = true;
-    // some query sees only part of the keys (diagonal, or a document start
-    // inside them); decided before the reads below, whose wait it would share
-    const bool diag = !skip && ((a.causal && pp[0] < w_kmax) || (DOC && lp[last] > w_kmin));
-    bf16x8 qt[2][D / 32], dt[2][D / 32], pb[2], dsb[2];
-    if (!skip) {
-      if (DOC) any = true;
-      // ---- A ----
-      f32x16 s = f32x16{}, dp = f32x16{};
+  // Two elements (el, el+1) of B: p = 2^(S scale log2 e - lse'),
+  // ds = p (dP - D), converted to bf16 together.
+  auto b_pair = [&](int par, int el) INLINE {
 #pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ds], kreg[ds], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ds], vreg[ds], dp, 0, 0, 0);
-      }
+    for (int j = el; j < el + 2; ++j) {
+      const float p = exp2_fast(fmaf(s[par][j], sl2, -l4[j >> 2][j & 3]));
+      pb[par][j >> 3][j & 7] = static_cast<__bf16>(p);
+      dsb[par][j >> 3][j & 7] = static_cast<__bf16>(p * (dp[par][j] - d4[j >> 2][j & 3]));
+    }
+  };
+  // Operand of A item a (k-step a/2; S from the Q rows when a is even, dP from
+  // the dO rows when odd) for the sub-block at rows rb of `stage`.
+  auto rd_a = [&](auto stage, int rb, int ai) INLINE -> bf16x8 {
+    const unsigned char *base = ((ai & 1) ? d_stage(stage) : q_stage(stage)) + rb * ROW_B;
+    return *reinterpret_cast<const bf16x8 *>(base + qoff(ai >> 1));
+  };
+  // Operand of C item c (16-row step c/8, d block (c/2)%4; dV from dO^T when
+  // c is even, dK from Q^T when odd), by the transposing read.
+  auto rd_c = [&](auto stage, int rb, int ci) INLINE -> bf16x8 {
+    const unsigned char *base = (ci & 1) ? q_stage(stage) : d_stage(stage);
+    return tread(base, (ci >> 1) & 3, rb + (ci >> 3) * 16);
+  };
+  auto mfma_a = [&](int par, int ai, const bf16x8 &o) INLINE {
+    const int ds = ai >> 1;
+    if (ai & 1)
+      dp[par] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, vreg[ds], ds == 0 ? f32x16{} : dp[par], 0, 0, 0);
+    else
+      s[par] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, kreg[ds], ds == 0 ? f32x16{} : s[par], 0, 0, 0);
+  };
+  auto mfma_c = [&](int par, int ci, const bf16x8 &o) INLINE {
+    const int ks = ci >> 3, db = (ci >> 1) & 3;
+    if (ci & 1)
+      dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, dsb[par][ks], dk[db], 0, 0, 0);
+    else
+      dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, pb[par][ks], dv[db], 0, 0, 0);
+  };
+  constexpr int DIST = 4;  // operand reads ahead of their MFMA
+  // The full stream: A(n+1) on even slots, C(n-1) on odd slots, a pair of B(n)
+  // elements after every fourth MFMA (the lse and D reads at the top of the
+  // iteration land meanwhile).
+  auto stream = [&](auto sa, int rb_a, int pa, auto sc, int rb_c, int pc, int pbp) INLINE {
+    auto rd = [&](int i) INLINE -> bf16x8 {
+      return (i & 1) ? rd_c(sc, rb_c, i >> 1) : rd_a(sa, rb_a, i >> 1);
+    };
+    bf16x8 op[DIST + 1];
+#pragma unroll
+    for (int i = 0; i < DIST; ++i) op[i] = rd(i);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i + DIST < 32) op[(i + DIST) % (DIST + 1)] = rd(i + DIST);
+      if (i & 1)
+        mfma_c(pc, i >> 1, op[i % (DIST + 1)]);
+      else
+        mfma_a(pa, i >> 1, op[i % (DIST + 1)]);
+      if ((i & 3) == 3) b_pair(pbp, 2 * (i >> 2));
       __builtin_amdgcn_sched_barrier(0);
-      const unsigned char *qb = q_stage(stage);
-      const unsigned char *db = d_stage(stage);
+    }
+  };
+  // A alone (before the wave's first sub-block) and C alone (after its last).
+  auto a_only = [&](auto sa, int rb_a, int pa) INLINE {
+    bf16x8 op[DIST + 1];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+    for (int i = 0; i < DIST; ++i) op[i] = rd_a(sa, rb_a, i);
 #pragma unroll
-        for (int dblk = 0; dblk < D / 32; ++dblk) {
-          dt[ks][dblk] = tr_read(db, toff, dblk, rb + ks * 16);
-          qt[ks][dblk] = tr_read(qb, toff, dblk, rb + ks * 16);
-        }
-      int4 p4[4], o4[4];
+    for (int i = 0; i < 16; ++i) {
+      if (i + DIST < 16) op[(i + DIST) % (DIST + 1)] = rd_a(sa, rb_a, i + DIST);
+      mfma_a(pa, i, op[i % (DIST + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto c_only = [&](auto sc, int rb_c, int pc) INLINE {
+    bf16x8 op[DIST + 1];
+#pragma unroll
+    for (int i = 0; i < DIST; ++i) op[i] = rd_c(sc, rb_c, i);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + DIST < 16) op[(i + DIST) % (DIST + 1)] = rd_c(sc, rb_c, i + DIST);
+      mfma_c(pc, i, op[i % (DIST + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Element mask of A's scores (sub-block at rows rb of `stage`, block rows
+  // from q0): rows past the sequence, keys past the block, a query before the
+  // key (causal), or a key before the query's document.
+  auto mask_a = [&](auto stage, int rb, int par, int64_t q0) INLINE {
+    const int64_t qlim = a.s_q - q0 - rb;
+    const int64_t row0 = q0 + rb;
+    const bool need = qlim < KV_SUB || w_ragged || (a.causal && row0 < c_kmax) ||
+                      (DOC && row0 + min<int64_t>(KV_SUB, qlim) - 1 >= c_dmin);
+    if (need) {
+      const int32_t *pp = p_stage(stage) + rb;
+      const int32_t *lp = lo_stage(stage) + rb;
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int r0 = e4 * 8 + hi * 4;
-        p4[e4] = int4{INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-        o4[e4] = int4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
-        if (diag) {
-          p4[e4] = *reinterpret_cast<const int4 *>(pp + r0);
-          if (DOC) o4[e4] = *reinterpret_cast<const int4 *>(lp + r0);
+        int4 p4 = int4{INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+        int4 o4 = int4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+        if (a.causal) p4 = *reinterpret_cast<const int4 *>(pp + r0);
+        if (DOC) o4 = *reinterpret_cast<const int4 *>(lp + r0);
+        const int32_t qp[4] = {p4.x, p4.y, p4.z, p4.w};
+        const int32_t ql[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool out = (r0 + j >= qlim) | (kpos > qp[j]) | (kpos < ql[j]) | !key_ok;
+          s[par][e4 * 4 + j] = out ? -INFINITY : s[par][e4 * 4 + j];
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- B ---- the element mask only where some element can be out
-      // (ragged rows or keys, the diagonal, a document start): a uniform branch.
-      const bool ragged = qlim < KV_SUB;
-      auto softmax = [&](auto masked_c) INLINE {
-        constexpr bool MASKED = decltype(masked_c)::value;
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int r0 = e4 * 8 + hi * 4;
-          const float lv[4] = {l4[e4].x, l4[e4].y, l4[e4].z, l4[e4].w};
-          const float dv4[4] = {d4[e4].x, d4[e4].y, d4[e4].z, d4[e4].w};
-          const int32_t qp[4] = {p4[e4].x, p4[e4].y, p4[e4].z, p4[e4].w};
-          const int32_t ql[4] = {o4[e4].x, o4[e4].y, o4[e4].z, o4[e4].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int el = e4 * 4 + j;
-            float x = s[el];
-            if constexpr (MASKED) {
-              const bool out =
-                  (r0 + j >= qlim) | (kpos > qp[j]) | (kpos < ql[j]) | !key_ok;
-              x = out ? -INFINITY : x;
-            }
-            const float p = exp2_fast(fmaf(x, sl2, -lv[j]));   // lse already in log2 units
-            pb[el >> 3][el & 7] = static_cast<__bf16>(p);
-            dsb[el >> 3][el & 7] = static_cast<__bf16>(p * (dp[el] - dv4[j]));
-          }
-        }
-      };
-      if (ragged | diag | w_ragged)
-        softmax(std::true_type{});
-      else
-        softmax(std::false_type{});
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (last_in_blk) {
-      // Block it+1 has landed everywhere; every wave is done with block it.
-      wait_own_loads();
-      __syncthreads();
-      if (it + 3 < n_it) issue_blk(it + 3, stage);
-    }
-    if (!skip) {
-      // ---- C ---- dV^T += dO^T P and dK^T += Q^T dS: A = dO^T / Q^T by the
-      // transposing read, B = P / dS (k-slots = queries of 16-row steps).
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int dblk = 0; dblk < D / 32; ++dblk) {
-          dv[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[ks][dblk], pb[ks], dv[dblk], 0, 0, 0);
-          dk[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[ks][dblk], dsb[ks], dk[dblk], 0, 0, 0);
-        }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Wave 0 loads every block's lse and converts it in place to log2 units
-  // (-inf, a query with no key, to +inf so that its probabilities are 0)
-  // once its own load has landed and before any wave reads it: block 0 before
-  // the first barrier, block it+1 at the start of block it (it landed at
-  // block it-1's barrier, and the other waves read it after block it's).
+  // (-inf, a query with no key, to +inf so that its probabilities are 0):
+  // block 0 before the first barrier, block it+1 in the second iteration of
+  // block it (it landed at the first one's barrier; the other waves read it
+  // after the second one's).
   auto prescale_lse = [&](auto stage) INLINE {
     if (wave == 0) {
       float *l = l_stage(stage);
@@ -717,33 +800,75 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using St0 = std::integral_constant<int, 0>;
   using St1 = std::integral_constant<int, 1>;
   using St2 = std::integral_constant<int, 2>;
-  // Block it lives in stage it % 3. Blocks 0..2 start streaming now; block
-  // it+3 is issued at block it's barrier.
+  // Block it lives in stage it % 3. Blocks 0 and 1 start streaming now; block
+  // it+2 is issued at the barrier of iteration 2 it, once every wave is done
+  // with block it-1 (its C ran in that iteration).
   if (n_it > 0) issue_blk(0, St0{});
   if (n_it > 1) issue_blk(1, St1{});
-  if (n_it > 2) issue_blk(2, St2{});
+  // Stage 2 is read (with zero P and dS) by the first iteration's C before any
+  // block lands in it: clear it so that it holds finite values.
+#pragma unroll
+  for (int i = 0; i < KV_TILE_B / (16 * KV_THREADS); ++i) {
+    reinterpret_cast<u32x4 *>(q_lds2)[tid + i * KV_THREADS] = u32x4{0, 0, 0, 0};
+    reinterpret_cast<u32x4 *>(d_lds2)[tid + i * KV_THREADS] = u32x4{0, 0, 0, 0};
+  }
   wait_own_loads();
   if (n_it > 0) prescale_lse(St0{});
   __syncthreads();
-  if (n_it > 0) read_rows(St0{}, 0);
-  auto step = [&](auto stage_c, int it) INLINE {
-    constexpr int S = decltype(stage_c)::value;
-    using SC = std::integral_constant<int, S>;
-    using SN = std::integral_constant<int, (S + 1) % 3>;
-    int64_t q0;
-    int h;
-    blk_of(it, &q0, &h);
-    (void)h;
-    if (it + 1 < n_it) prescale_lse(SN{});
-    sub(it, q0, 0, SC{}, false);
-    read_rows(SC{}, KV_SUB);
-    sub(it, q0, KV_SUB, SC{}, true);
-    if (it + 1 < n_it) read_rows(SN{}, 0);
+  if (n_lo == 0 && n_hi > 0) {
+    a_only(St0{}, 0, 0);
+    mask_a(St0{}, 0, 0, blk_q0(0));
+  }
+  const int n_sub = 2 * n_it;
+  // Iteration n (n % 6 = K): B on sub-block n, A on n+1, C on n-1.
+  auto step = [&](auto k_c, int n) INLINE {
+    constexpr int K = decltype(k_c)::value;
+    constexpr int H = K % 2;                 // half of its block
+    using SB = std::integral_constant<int, (K / 2) % 3>;         // stage of n's block
+    using SA = std::integral_constant<int, ((K + 1) / 2) % 3>;   // ... of n+1's
+    using SC = std::integral_constant<int, ((K + 5) / 2) % 3>;   // ... of n-1's
+    constexpr int RB = 32 * H, RB_O = 32 * (1 - H);  // rows of n; of n+1 and n-1
+    constexpr int PB = H, PO = 1 - H;                // parity of n; of n+-1
+    const int it = n >> 1;
+    asm volatile("" : "+v"(qoff0), "+v"(toff0[0]), "+v"(toff0[1]));  // pin: see qoff
+    // Inside the range the full stream runs; its A past the range computes
+    // scores nobody reads, and its C before the range adds zero P and dS.
+    if (n >= n_lo && n < n_hi) {
+      read_ld(SB{}, RB);
+      stream(SA{}, RB_O, PO, SC{}, RB_O, PO, PB);
+      if (n + 1 < n_hi) mask_a(SA{}, RB_O, PO, blk_q0((n + 1) >> 1));
+    } else if (n + 1 == n_lo) {
+      a_only(SA{}, RB_O, PO);
+      mask_a(SA{}, RB_O, PO, blk_q0((n + 1) >> 1));
+    } else if (n == n_hi) {
+      c_only(SC{}, RB_O, PO);
+    }
+    if constexpr (H == 0) {
+      wait_own_loads();  // block it+1 has landed
+      __syncthreads();
+      if (it + 2 < n_it) issue_blk(it + 2, SC{});
+    } else {
+      if (it + 1 < n_it) prescale_lse(SA{});
+      __syncthreads();
+    }
   };
-  for (int it = 0; it < n_it; it += 3) {
-    step(St0{}, it);
-    if (it + 1 < n_it) step(St1{}, it + 1);
-    if (it + 2 < n_it) step(St2{}, it + 2);
+  for (int n = 0; n < n_sub; n += 6) {
+    step(std::integral_constant<int, 0>{}, n);
+    step(std::integral_constant<int, 1>{}, n + 1);
+    if (n + 2 < n_sub) step(std::integral_constant<int, 2>{}, n + 2);
+    if (n + 3 < n_sub) step(std::integral_constant<int, 3>{}, n + 3);
+    if (n + 4 < n_sub) step(std::integral_constant<int, 4>{}, n + 4);
+    if (n + 5 < n_sub) step(std::integral_constant<int, 5>{}, n + 5);
+  }
+  // C of the last sub-block (its block's stage is still intact).
+  if (n_hi == n_sub && n_lo < n_hi) {
+    const int st = (n_it - 1) % 3;
+    if (st == 0)
+      c_only(St0{}, 32, 1);
+    else if (st == 1)
+      c_only(St1{}, 32, 1);
+    else
+      c_only(St2{}, 32, 1);
   }
 
   if (!key_ok || (DOC && !any)) return;
