@@ -58,6 +58,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 
 __device__ __forceinline__ void wait_own_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+
 // Number of entries < p (lower bound) / <= p (upper bound) in a non-decreasing array.
 __device__ __forceinline__ int64_t count_lt(const int32_t *pos, int64_t n, int32_t p) {
   int64_t lo = 0, hi = n;
@@ -684,6 +685,9 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
       pb[par][j >> 3][j & 7] = static_cast<__bf16>(p);
       dsb[par][j >> 3][j & 7] = static_cast<__bf16>(p * (dp[par][j] - d4[j >> 2][j & 3]));
     }
+    // Keep the pair here, between the MFMAs: otherwise the compiler sinks all
+    // of B past the stream, where nothing overlaps it.
+    asm volatile("" : "+v"(pb[par][el >> 3]), "+v"(dsb[par][el >> 3]));
   };
   // Operand of A item a (k-step a/2; S from the Q rows when a is even, dP from
   // the dO rows when odd) for the sub-block at rows rb of `stage`.
