@@ -312,24 +312,38 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
   // update (adding zeros). Without one the flag compiles away.
   bool any = false;
 
+  // Per tile: S^T and dP^T (32 MFMAs, K and V rows read a few MFMAs ahead),
+  // the element mask where needed, then dQ^T += K^T dS^T (16 MFMAs, K^T by the
+  // transposing read) with dS^T of the next k-step formed on the VALU between
+  // them. Scheduling fences keep the reads ahead of their MFMAs: left to
+  // itself the compiler waits for each read right before its MFMA.
+  constexpr int DIST = 4;
   auto process = [&](int t, auto stage) INLINE {
     const unsigned char *kb = k_stage(stage);
     const unsigned char *vb = v_stage(stage);
     f32x16 s[2], dp[2];
+    // Item i: k-step i/4, key block (i/2)%2; S^T from K when i is even, dP^T
+    // from V when odd.
+    auto rd_a = [&](int i) INLINE -> bf16x8 {
+      const unsigned char *base = (i & 1) ? vb : kb;
+      return *reinterpret_cast<const bf16x8 *>(base + koff[i >> 2] + ((i >> 1) & 1) * 32 * ROW_B);
+    };
+    {
+      bf16x8 op[DIST + 1];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      s[j] = f32x16{};
-      dp[j] = f32x16{};
-    }
+      for (int i = 0; i < DIST; ++i) op[i] = rd_a(i);
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kb + koff[ds] + j * 32 * ROW_B);
-        const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vb + koff[ds] + j * 32 * ROW_B);
-        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ds], s[j], 0, 0, 0);
-        dp[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dreg[ds], dp[j], 0, 0, 0);
+      for (int i = 0; i < 32; ++i) {
+        if (i + DIST < 32) op[(i + DIST) % (DIST + 1)] = rd_a(i + DIST);
+        const int ds = i >> 2, j = (i >> 1) & 1;
+        const bf16x8 o = op[i % (DIST + 1)];
+        if (i & 1)
+          dp[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, dreg[ds], ds == 0 ? f32x16{} : dp[j], 0, 0, 0);
+        else
+          s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, qreg[ds], ds == 0 ? f32x16{} : s[j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
     // Element e4*4 + j of key block kb holds key kb*32 + e4*8 + hi*4 + j.
     const int64_t key0 = kbeg + static_cast<int64_t>(t) * Q_BK;
     const bool ragged = key0 + Q_BK > a.s_kv;
@@ -350,22 +364,34 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
           }
         }
     }
-    // dS^T = P^T (dP^T - D) as the bf16 B operand of dQ^T += K^T dS^T.
+    // dS^T = P^T (dP^T - D) as the bf16 B operand of dQ^T += K^T dS^T:
+    // k-step ks holds accumulator elements (ks%2)*8 .. +7 of key block ks/2.
     bf16x8 dsb[4];
+    auto ds_pair = [&](int ks, int e) INLINE {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = ks >> 1, el = (ks & 1) * 8 + e;
+      for (int u = e; u < e + 2; ++u) {
+        const int j = ks >> 1, el = (ks & 1) * 8 + u;
         const float p = exp2_fast(fmaf(s[j][el], sl2, -lse2));
-        dsb[ks][e] = static_cast<__bf16>(p * (dp[j][el] - dlt));
+        dsb[ks][u] = static_cast<__bf16>(p * (dp[j][el] - dlt));
       }
+      asm volatile("" : "+v"(dsb[ks]));  // keep it between the MFMAs
+    };
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int e = 0; e < 8; e += 2) ds_pair(0, e);
+    auto rd_c = [&](int i) INLINE -> bf16x8 { return tr_read(kb, toff, i & 3, (i >> 2) * 16); };
+    {
+      bf16x8 op[DIST + 1];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kb, toff, db, ks * 16), dsb[ks],
-                                                          acc[db], 0, 0, 0);
+      for (int i = 0; i < DIST; ++i) op[i] = rd_c(i);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + DIST < 16) op[(i + DIST) % (DIST + 1)] = rd_c(i + DIST);
+        const int ks = i >> 2, db = i & 3;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (DIST + 1)], dsb[ks], acc[db], 0, 0, 0);
+        if (ks + 1 < 4) ds_pair(ks + 1, 2 * (i & 3));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
 
   using St0 = std::integral_constant<int, 0>;
