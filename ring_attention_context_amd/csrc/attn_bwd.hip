@@ -19,11 +19,12 @@
 //   * bwd_dkdv_kernel (bf16, d = 128): a wave owns 32 keys of one key/value
 //     head, with its K and V rows in registers; 4 waves share each block of 64
 //     queries (q, do, lse, D, positions) staged in LDS, for every query head of
-//     the GQA group, and work through it in 32-row sub-blocks, reading each
-//     sub-block's LDS operands up front. Per sub-block: S = Q K^T and
-//     dP = dO V^T (Q and dO rows by
-//     ds_read_b128), then dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T by
-//     the transposing read), so each lane ends up holding d-values of one key.
+//     the GQA group, and work through it in 32-row sub-blocks: A, S = Q K^T and
+//     dP = dO V^T (Q and dO rows by ds_read_b128); B, P and dS on the VALU; C,
+//     dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T by the transposing read),
+//     so each lane ends up holding d-values of one key. The sub-blocks run as
+//     a software pipeline: A of the next and C of the previous sub-block share
+//     one stream of MFMAs into which B of the current one is interleaved.
 // P and dS enter the MFMAs as bf16; every accumulation is fp32. dq, dk and dv
 // are float32 and ACCUMULATED into (+=): the ring adds one block per step.
 #include <climits>
