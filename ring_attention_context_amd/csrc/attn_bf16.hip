@@ -384,7 +384,6 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   float l_run = 0.f;        // this lane's half of the running sum (fp32 probabilities)
   float lh_run = 0.f;       // ... of the bf16-rounded probabilities fed to P V
   float lt = 0.f;           // this lane's half of the current tile's sum
-  float lht = 0.f;          // ... and of its bf16-rounded probabilities
   float alpha = 1.f;        // rescale factor pending for acc / l_run
   bool done = !wave_has_rows || w_nt == 0;
   bf16x8 pb[4];             // probabilities of the tile whose P V is next
@@ -474,16 +473,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
       asm volatile("" : "+v"(pb[ks]));
     }
     lt = (lp[0] + lp[1]) + (lp[2] + lp[3]);
-    const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-    float lh[2] = {0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        lh[e >> 2] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ks][e], pb[ks][e + 1]}, one,
-                                                     lh[e >> 2], false);
-    lht = lh[0] + lh[1];
-    asm volatile("" : "+v"(lt), "+v"(lht));
+    asm volatile("" : "+v"(lt));
   };
 
   // Matrix phase of step t: the score MFMAs of tile t+1 (K in stage `sn`)
@@ -516,6 +506,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
       }
     };
     bf16x8 op[DIST + 1];
+    const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    float lh[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < DIST; ++i) op[i] = rd(i);
 #pragma unroll
@@ -526,11 +518,16 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
         const int it = i >> 1, ds = it >> 1, kb = it & 1;
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, qreg[ds], ds == 0 ? f32x16{} : s[kb], 0, 0, 0);
       } else {
-        const int pi = i >> 1;
-        acc[pi % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, pb[pi / NDB], acc[pi % NDB], 0, 0, 0);
+        const int pi = i >> 1, ks = pi / NDB, db = pi % NDB;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, pb[ks], acc[db], 0, 0, 0);
+        // The sum of the bf16 probabilities (the weights P V just used): one
+        // pair per P V MFMA, on the VALU that the matrix phase leaves idle.
+        lh[db & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ks][2 * db], pb[ks][2 * db + 1]},
+                                                     one, lh[db & 1], false);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    lh_run += lh[0] + lh[1];
   };
 
   // Vector phase for the tile whose (masked) scores are in `s`: probabilities
@@ -556,7 +553,6 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
       lt_row = pair_sum(lt);
     }
     l_run += lt;
-    lh_run += lht;
     const bool need = lt_row > 0x1p8f;  // 2^TAU
     const float lg = __builtin_amdgcn_logf(lt_row);  // log2
     alpha = need ? exp2_fast(-lg) : 1.f;
