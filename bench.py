@@ -68,20 +68,19 @@ def visible_pairs_per_step(kind, S, N, rank, causal):
     return out
 
 
-def committed_traffic(w):
-    """HBM bytes per launch of the attention kernel from the committed counter
-    summary, if it was taken on this workload with the current kernel source
-    (else None)."""
+def committed_traffic(w, profile="attn_bf16_llama3_70b_128k_zigzag_counters.md",
+                      source="attn_bf16.hip", unit="launch"):
+    """HBM bytes per launch (or per ring step) of the measured kernels from the
+    committed counter summary, if it was taken on this workload with the
+    current kernel source (else None)."""
     if w.name != "llama3_70b_128k_zigzag" or w.rank != 0 or w.kind != "zigzag":
         return None
     try:
-        text = open(os.path.join(ROOT, "profiles",
-                                 "attn_bf16_llama3_70b_128k_zigzag_counters.md")).read()
-        src = open(os.path.join(ROOT, "ring_attention_context_amd", "csrc", "attn_bf16.hip"),
-                   "rb").read()
+        text = open(os.path.join(ROOT, "profiles", profile)).read()
+        src = open(os.path.join(ROOT, "ring_attention_context_amd", "csrc", source), "rb").read()
     except OSError:
         return None
-    m = re.search(r"traffic = ([\d,]+) bytes per launch", text)
+    m = re.search(r"traffic = ([\d,]+) bytes per " + unit, text)
     h = re.search(r"sha256 = ([0-9a-f]{64})", text)
     if not m or not h or h.group(1) != hashlib.sha256(src).hexdigest():
         return None
@@ -420,7 +419,10 @@ def run_backward(args, w, q, kc, vc, dev, props):
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "bwd_dq_kernel + bwd_dkdv_kernel per step",
+                     "traffic": committed_traffic(
+                         w, "attn_bwd_llama3_70b_128k_zigzag_kernel_trace.md", "attn_bwd.hip",
+                         "step"),
+                     "kernel": "bwd_dq_kernel + bwd_dkdv_kernel per step",
                      "avg_launch_ms": round(kern_ms / step_ms.size, 4),
                      "launches": int(step_ms.size),
                      "flops_per_launch_avg": total_flops / w.N},
