@@ -337,8 +337,7 @@ def run_allgather_backward(args, w, q, kc, vc, ds, call, stream, pairs, lengths,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(total_flops / (ev_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": None,
-                     "kernel": "whole ra_allgather_bwd call (gathers, dq and dK/dV kernels, "
-                               "scatter)",
+                     "kernel": "whole ra_allgather_bwd call (gathers, dq and dK/dV kernels)",
                      "avg_launch_ms": round(ev_ms, 4), "launches": len(evs),
                      "flops_per_launch_avg": total_flops},
         "cpu_baseline": cpu,

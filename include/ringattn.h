@@ -303,8 +303,9 @@ ra_status ra_allgather_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *byt
  * dv_chunks (the reduce-scatter's input: summing every rank's calls on the
  * same slots gives each chunk's dK, dV). workspace: >=
  * ra_allgather_bwd_workspace_bytes(): positions, D, document starts, the
- * gathered K and V of the sequence (bf16) and its dK, dV (float32). One
- * stream; step_events unused.
+ * gathered K and V of the sequence (bf16) and the chunk row of each
+ * position (int32; the gradients go straight into the slots). One stream;
+ * step_events unused.
  */
 ra_status ra_allgather_bwd(const ra_ring_desc *desc, const void *q, const void *k_chunks,
                            const void *v_chunks, const float *o, const float *lse,

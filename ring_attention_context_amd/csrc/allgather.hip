@@ -18,9 +18,10 @@
 // ra_allgather_bwd is the backward of the same scheme (§8: the all-gather's
 // backward is a reduce-scatter of dK, dV): the block backward of the rank's
 // queries against the gathered sequence (the kernels of the ring backward,
-// with K/V of all S keys), then the sequence's dK, dV cut back into the N
-// chunks and added to the caller's slots -- this rank's share of the
-// reduce-scatter.
+// with K/V of all S keys). The dK/dV kernel adds each key's gradient straight
+// into the caller's slot of the chunk that holds the key (a row map built
+// from the positions), so the sequence's dK, dV never exist on their own:
+// this rank's share of the reduce-scatter.
 #include <cmath>
 
 #include "ra_internal.h"
@@ -67,44 +68,26 @@ hipError_t launch_kv_gather(const void *chunks, void *full, const int32_t *pos, 
   return hipGetLastError();
 }
 
-// chunks[j, bi, a, :] += full[bi, pos[j*c + a], :] for float32 rows of
-// `row16` 16-byte units: the inverse of kv_gather_kernel, accumulating.
-__global__ __launch_bounds__(256) void kv_scatter_add_kernel(const float4 *__restrict__ full,
-                                                             float4 *__restrict__ chunks,
-                                                             const int32_t *__restrict__ pos,
-                                                             int64_t c, int32_t b, int64_t S,
-                                                             int64_t row16, int64_t total) {
+// row[pos[j*c + a]] = j*b*c + a: the row of chunk slot j (batch 0) that
+// holds the key at each position of the sequence, so that the backward
+// kernel adds each key's dK, dV straight into its chunk's slot.
+__global__ __launch_bounds__(256) void slot_rows_kernel(const int32_t *__restrict__ pos,
+                                                        int32_t *__restrict__ row, int64_t c,
+                                                        int32_t b, int64_t S) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < S;
        i += stride) {
-    const int64_t u = i % row16;
-    const int64_t row = i / row16;         // (j * b + bi) * c + a
-    const int64_t a = row % c;
-    const int64_t jb = row / c;
-    const int64_t bi = jb % b;
-    const int64_t j = jb / b;
-    const int64_t p = pos[j * c + a];
-    const float4 x = full[(bi * S + p) * row16 + u];
-    float4 y = chunks[i];
-    y.x += x.x;
-    y.y += x.y;
-    y.z += x.z;
-    y.w += x.w;
-    chunks[i] = y;
+    const int64_t j = i / c, a = i % c;
+    row[pos[i]] = static_cast<int32_t>(j * b * c + a);
   }
 }
 
-hipError_t launch_kv_scatter_add(const float *full, float *chunks, const int32_t *pos, int64_t c,
-                                 int32_t N, int32_t b, int64_t S, size_t row_bytes,
-                                 hipStream_t stream) {
-  const int64_t row16 = static_cast<int64_t>(row_bytes / 16);
-  const int64_t total = static_cast<int64_t>(N) * b * c * row16;
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 256 * 32) blocks = 256 * 32;
-  kv_scatter_add_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(
-      reinterpret_cast<const float4 *>(full), reinterpret_cast<float4 *>(chunks), pos, c, b, S,
-      row16, total);
+hipError_t launch_slot_rows(const int32_t *pos, int32_t *row, int64_t c, int32_t b, int64_t S,
+                            hipStream_t stream) {
+  if (S == 0) return hipSuccess;
+  int64_t blocks = (S + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  slot_rows_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(pos, row, c, b, S);
   return hipGetLastError();
 }
 
@@ -149,9 +132,8 @@ ra_status make_ag_plan(const ra_ring_desc *r, AgPlan *p) {
 struct AgBwdPlan {
   int64_t c = 0;
   size_t kv_bytes = 0;      // K (or V) of the sequence, bf16 [b, S, n_kv, d]
-  size_t g_bytes = 0;       // dK (or dV) of the sequence, float32
   size_t pos_off = 0, kvpos_off = 0, qlo_off = 0, delta_off = 0, k_off = 0, v_off = 0,
-         dk_off = 0, dv_off = 0, total = 0;
+         row_off = 0, total = 0;
 };
 
 ra_status make_ag_bwd_plan(const ra_ring_desc *r, AgBwdPlan *p) {
@@ -163,7 +145,6 @@ ra_status make_ag_bwd_plan(const ra_ring_desc *r, AgBwdPlan *p) {
   p->c = r->S / r->N;
   const size_t elems = static_cast<size_t>(r->b) * r->S * r->n_kv * r->d;
   p->kv_bytes = elems * 2;
-  p->g_bytes = elems * 4;
   size_t off = 0;
   p->pos_off = off;
   off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
@@ -177,10 +158,8 @@ ra_status make_ag_bwd_plan(const ra_ring_desc *r, AgBwdPlan *p) {
   off += align_up(p->kv_bytes);
   p->v_off = off;
   off += align_up(p->kv_bytes);
-  p->dk_off = off;
-  off += align_up(p->g_bytes);
-  p->dv_off = off;
-  off += align_up(p->g_bytes);
+  p->row_off = off;
+  off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
   p->total = off;
   return RA_OK;
 }
@@ -324,12 +303,10 @@ extern "C" ra_status ra_allgather_bwd(const ra_ring_desc *r, const void *q, cons
   float *delta = reinterpret_cast<float *>(ws + P.delta_off);
   unsigned char *kfull = ws + P.k_off;
   unsigned char *vfull = ws + P.v_off;
-  float *dkfull = reinterpret_cast<float *>(ws + P.dk_off);
-  float *dvfull = reinterpret_cast<float *>(ws + P.dv_off);
+  int32_t *slot_row = reinterpret_cast<int32_t *>(ws + P.row_off);
   const int32_t *q_pos = pos + static_cast<int64_t>(r->rank) * P.c;
   const size_t row_bytes = static_cast<size_t>(r->n_kv) * r->d * 2;
   const int64_t rows = static_cast<int64_t>(r->b) * P.c * r->n_q;
-  const int64_t g_elems = static_cast<int64_t>(r->b) * r->S * r->n_kv * r->d;
 
   st = hip_check(ra::launch_positions(r->kind, r->S, r->N, pos, s), "ra_allgather_bwd: positions");
   if (st == RA_OK)
@@ -343,9 +320,8 @@ extern "C" ra_status ra_allgather_bwd(const ra_ring_desc *r, const void *q, cons
   if (st == RA_OK)
     st = hip_check(ra::launch_fill_zero(dq, rows * r->d, s), "ra_allgather_bwd: zero dq");
   if (st == RA_OK)
-    st = hip_check(ra::launch_fill_zero(dkfull, g_elems, s), "ra_allgather_bwd: zero dK");
-  if (st == RA_OK)
-    st = hip_check(ra::launch_fill_zero(dvfull, g_elems, s), "ra_allgather_bwd: zero dV");
+    st = hip_check(ra::launch_slot_rows(pos, slot_row, P.c, r->b, r->S, s),
+                   "ra_allgather_bwd: slot rows");
   if (st == RA_OK)
     st = hip_check(ra::launch_kv_gather(k_chunks, kfull, pos, P.c, r->N, r->b, r->S, row_bytes, s),
                    "ra_allgather_bwd: K gather");
@@ -362,8 +338,10 @@ extern "C" ra_status ra_allgather_bwd(const ra_ring_desc *r, const void *q, cons
   a.lse = lse;
   a.delta = delta;
   a.dq = dq;
-  a.dk = dkfull;
-  a.dv = dvfull;
+  a.dk = dk_chunks;  // each key's dK, dV go straight into its chunk's slot
+  a.dv = dv_chunks;
+  a.kv_row = slot_row;
+  a.kv_row_bstride = P.c;
   a.q_pos = q_pos;
   a.kv_pos = kv_pos;
   a.q_lo = r->doc_start ? qlo : nullptr;
@@ -376,14 +354,5 @@ extern "C" ra_status ra_allgather_bwd(const ra_ring_desc *r, const void *q, cons
   a.scale = r->scale > 0.f ? r->scale : 1.0f / std::sqrt(static_cast<float>(r->d));
   a.causal = r->causal;
   st = hip_check(ra::launch_attn_bwd_bf16(a, s), "ra_allgather_bwd: backward launch");
-  const size_t g_row_bytes = static_cast<size_t>(r->n_kv) * r->d * 4;
-  if (st == RA_OK)
-    st = hip_check(ra::launch_kv_scatter_add(dkfull, dk_chunks, pos, P.c, r->N, r->b, r->S,
-                                             g_row_bytes, s),
-                   "ra_allgather_bwd: dK scatter");
-  if (st == RA_OK)
-    st = hip_check(ra::launch_kv_scatter_add(dvfull, dv_chunks, pos, P.c, r->N, r->b, r->S,
-                                             g_row_bytes, s),
-                   "ra_allgather_bwd: dV scatter");
   return st;
 }

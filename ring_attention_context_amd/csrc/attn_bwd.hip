@@ -904,8 +904,9 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   if (!key_ok || (DOC && !any)) return;
   // Accumulator element e4*4 + j of block dblk holds d = dblk*32 + e4*8 + hi*4 + j.
-  float *krow_out = a.dk + krow * D + hi * 4;
-  float *vrow_out = a.dv + krow * D + hi * 4;
+  const int64_t orow = a.kv_row ? (a.kv_row[key] + bi * a.kv_row_bstride) * a.n_kv + kvh : krow;
+  float *krow_out = a.dk + orow * D + hi * 4;
+  float *vrow_out = a.dv + orow * D + hi * 4;
 #pragma unroll
   for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll

@@ -51,6 +51,10 @@ struct BwdArgs {
   const int32_t *q_pos;
   const int32_t *kv_pos;
   const int32_t *q_lo;  // optional [s_q]: first visible key position (document start)
+  // optional [s_kv]: the dk/dv row of key j for batch 0 (batch bi adds
+  // bi * kv_row_bstride); without it key j of batch bi is row bi * s_kv + j
+  const int32_t *kv_row;
+  int64_t kv_row_bstride;
   int64_t s_q;
   int64_t s_kv;
   int32_t b;
