@@ -431,6 +431,60 @@ def run_backward(args, w, q, kc, vc, dev, props):
     print(json.dumps(out), flush=True)
 
 
+class ClockSampler:
+    """Samples the GPU's shader clock every ``period`` seconds on a background
+    thread while the timed region runs, so a result can be restated at the
+    clock the chip actually held. Source: the amdgpu ``pp_dpm_sclk`` file of
+    the device (the line marked ``*`` is the current clock)."""
+
+    def __init__(self, props, period=0.01):
+        import glob
+        import threading
+        self.path = None
+        try:
+            cards = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
+            addr = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}."
+            mine = [c for c in cards if os.path.realpath(os.path.dirname(c)).split("/")[-1]
+                    .startswith(addr)]
+            self.path = (mine or (cards if len(cards) == 1 else [None]))[0]
+        except Exception:  # noqa: BLE001
+            self.path = None
+        self.period, self.samples = period, []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*[Mm]hz", line)
+                    return int(m.group(1)) if m else None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except OSError:
+                return
+            if v:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def stop(self):
+        """Mean sampled clock in MHz, or None where no sample was read."""
+        if not self.path:
+            return None
+        self._stop.set()
+        self._thread.join()
+        return round(sum(self.samples) / len(self.samples), 1) if self.samples else None
+
+
 def time_ring(w, q, kc, vc, warmup, steps, flags=0):
     """Mean ms per ra_ring_fwd call and the median per-step ms (step events)."""
     import numpy as np
@@ -609,6 +663,7 @@ def main():
     ev_sets = [call.make_events() for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    clock = ClockSampler(props).start()
     t0 = time.perf_counter()
     start.record(compute)
     for i in range(args.steps):
@@ -616,6 +671,7 @@ def main():
     end.record(compute)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk = clock.stop()
     ev_ms = start.elapsed_time(end)
     ms_per_step = wall * 1e3 / args.steps
     value = total_flops / (ms_per_step * 1e-3) / 1e12
@@ -637,6 +693,9 @@ def main():
                 "flops_per_launch_avg": total_flops / w.N}
     log(f"[bench] per-step ms (median over calls): "
         f"{np.round(np.median(step_ms, axis=0), 3).tolist()}")
+    call_ms = step_ms.sum(axis=1)   # each call's N steps on the compute stream
+    log(f"[bench] per-call ms: median {np.median(call_ms):.3f}, min {call_ms.min():.3f}; "
+        f"shader clock {sclk} MHz")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -665,6 +724,13 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "event_ms_per_step": round(ev_ms / args.steps, 4),
+        "call_ms": {"median": round(float(np.median(call_ms)), 4),
+                    "min": round(float(call_ms.min()), 4)},
+        # The peak assumes 2.4 GHz; the chip holds a lower clock under this
+        # load. The same result against the peak at the sampled clock:
+        "sclk_mhz": sclk,
+        "pct_of_bf16_peak_at_sclk": (round(100 * value / (PEAK_BF16_TFLOPS * sclk / 2400.0), 2)
+                                     if sclk else None),
         "device": props.name,
     }
     print(json.dumps(out), flush=True)
