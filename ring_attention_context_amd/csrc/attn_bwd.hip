@@ -203,7 +203,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
 
   constexpr int TB = Q_WAVES / HW;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int lane = tid & 63;
   const int col = lane & 31;
   const int hi = lane >> 5;
@@ -245,7 +245,17 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
       if (DOC) w_lomax = a.q_lo[w_tok_last];
     }
   }
+  // (The searches read memory, so the compiler cannot see that their results
+  // agree across lanes: say so, and the loop's decisions stay scalar.)
+  nkeys = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(nkeys));
+  kbeg = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(kbeg));
   const int nt = nkeys > kbeg ? static_cast<int>((nkeys - kbeg + Q_BK - 1) / Q_BK) : 0;
+  // The wave's tiles: those whose first key is not after its last query.
+  int w_nt = wave_has_rows ? nt : 0;
+  if (a.causal && w_nt > 0) {
+    const int64_t c = wave_count<true>(a.kv_pos + kbeg, nkeys - kbeg, w_qmax, lane);
+    w_nt = min(w_nt, static_cast<int>((c + Q_BK - 1) / Q_BK));
+  }
 
   // This lane's query and upstream gradient: the B operands of S^T and dP^T.
   const uint16_t *qg = static_cast<const uint16_t *>(a.q);
@@ -308,10 +318,6 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-  bool done = !wave_has_rows || nt == 0;
-  // With a document mask many waves see no key at all: they skip the dq
-  // update (adding zeros). Without one the flag compiles away.
-  bool any = false;
 
   // Per tile: S^T and dP^T (32 MFMAs, K and V rows read a few MFMAs ahead),
   // the element mask where needed, then dQ^T += K^T dS^T (16 MFMAs, K^T by the
@@ -407,14 +413,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     wait_own_loads();  // tiles t (and t+1) have landed in this wave's share ...
     __syncthreads();   // ... and in everyone's; every wave is done with tile t-1
     if (t + 2 < nt) issue_tile(t + 2, SL{});
-    if (!done) {
-      if (a.causal && p_stage(SC{})[0] > w_qmax) {
-        done = true;  // this and every later tile is after the wave's last query
-      } else {
-        process(t, SC{});
-        if (DOC) any = true;
-      }
-    }
+    if (t < w_nt) process(t, SC{});
   };
   for (int t = 0; t < nt; t += 3) {
     step(St0{}, t);
@@ -422,7 +421,9 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     if (t + 2 < nt) step(St2{}, t + 2);
   }
 
-  if (!tok_ok || (DOC && !any)) return;
+  // With a document mask many waves see no key at all: they skip the dq
+  // update (adding zeros).
+  if (!tok_ok || (DOC && w_nt == 0)) return;
   // Accumulator element e4*4 + j of block db holds d = db*32 + e4*8 + hi*4 + j.
   float *drow = a.dq + row * D + hi * 4;
 #pragma unroll
