@@ -541,6 +541,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
                             : u32x4{0, 0, 0, 0};
     kreg[ds] = __builtin_bit_cast(bf16x8, rk);
     vreg[ds] = __builtin_bit_cast(bf16x8, rv);
+    asm volatile("" : "+a"(kreg[ds]), "+a"(vreg[ds]));  // they live in AGPRs (see mfma_a)
   }
   const float sl2 = a.scale * LOG2E;
 
@@ -729,12 +730,20 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const unsigned char *base = (ci & 1) ? q_stage(stage) : d_stage(stage);
     return tread(base, (ci >> 1) & 3, rb + (ci >> 3) * 16);
   };
+  // A's MFMAs are written out so that the K and V rows (read-only, the B
+  // operands) sit in AGPRs and S, dP land in VGPRs, where B reads them:
+  // left to itself the compiler keeps K, V in VGPRs and S, dP in AGPRs, and
+  // moves all 32 results out of AGPRs on every sub-block. The compiler's
+  // hazard checks do not see these MFMAs: their results are read by B one
+  // iteration later, or by the mask after acc_settle().
   auto mfma_a = [&](int par, int ai, const bf16x8 &o) INLINE {
     const int ds = ai >> 1;
-    if (ai & 1)
-      dp[par] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, vreg[ds], ds == 0 ? f32x16{} : dp[par], 0, 0, 0);
+    f32x16 &r = (ai & 1) ? dp[par] : s[par];
+    const bf16x8 &b = (ai & 1) ? vreg[ds] : kreg[ds];
+    if (ds == 0)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(r) : "v"(o), "a"(b));
     else
-      s[par] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, kreg[ds], ds == 0 ? f32x16{} : s[par], 0, 0, 0);
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(r) : "v"(o), "a"(b));
   };
   auto mfma_c = [&](int par, int ci, const bf16x8 &o) INLINE {
     const int ks = ci >> 3, db = (ci >> 1) & 3;
@@ -797,6 +806,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const bool need = qlim < KV_SUB || w_ragged || (a.causal && row0 < c_kmax) ||
                       (DOC && row0 + min<int64_t>(KV_SUB, qlim) - 1 >= c_dmin);
     if (need) {
+      // wait out the writes of the last A MFMAs (written out, see mfma_a)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
       const int32_t *pp = p_stage(stage) + rb;
       const int32_t *lp = lo_stage(stage) + rb;
 #pragma unroll
