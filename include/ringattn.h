@@ -223,8 +223,9 @@ ra_status ra_allgather_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
  * overwritten. step_events, if set, holds 2 hipEvent_t recorded on `stream`
  * just before and just after the attention launch. workspace: device, >= ra_allgather_workspace_bytes();
  * holds the positions, the gathered K and V of the sequence (for bf16 with
- * S % 8 == 0, V also transposed, RA_V_TRANSPOSED) and the queries' document
- * starts. Runs on `stream`.
+ * S % 8 == 0, V gathered straight into the transposed layout RA_V_TRANSPOSED,
+ * with the chunk row of every position) and the queries' document starts.
+ * Runs on `stream`.
  */
 ra_status ra_allgather_fwd(const ra_ring_desc *desc, const void *q, const void *k_chunks,
                            const void *v_chunks, float *o, float *lse, void *workspace,

@@ -269,7 +269,8 @@ def test_allgather_workspace_and_errors():
         return (x + 255) // 256 * 256
     # S = 1024, N = 4, c = 256; bf16 K/V of the sequence 1024 x 2 x 128 x 2 bytes each
     full = 1024 * 2 * 128 * 2
-    want = align(1024 * 4) * 2 + align(256 * 4) + 3 * align(full)   # K, V, V^T
+    # positions, key positions, document starts, K, V^T, the slot row of every position
+    want = align(1024 * 4) * 2 + align(256 * 4) + 2 * align(full) + align(1024 * 4)
     assert ra.ra_allgather_workspace_bytes(_ring()) == want
     # float32: no transposed copy
     full32 = 1024 * 2 * 128 * 4

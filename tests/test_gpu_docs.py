@@ -112,6 +112,8 @@ AG_CASES = [
     ("contiguous", 2, 768, 4, 4, "bf16", 1, 300, True),
     ("zigzag", 8, 2048, 16, 2, "bf16", 5, 1, True),      # one token per document
     ("zigzag", 4, 1024, 8, 2, "bf16", 2, 0, False),      # no documents: plain causal
+    ("zigzag", 2, 1000, 4, 2, "bf16", 0, 60, True),      # S % 64 != 0: ragged V^T tile
+    ("striped", 4, 1000, 8, 4, "bf16", 2, 60, True),
     ("zigzag", 2, 300, 4, 2, "bf16", 1, 40, True),       # c = 150: V kept row-major
     ("zigzag", 4, 256, 2, 1, "f32", 3, 20, True),
 ]
