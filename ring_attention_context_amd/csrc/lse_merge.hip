@@ -3,25 +3,37 @@
 //   M = max(lse, lse_b), lse' = M + ln(e^{lse-M} + e^{lse_b-M}),
 //   o' = e^{lse-lse'} o + e^{lse_b-lse'} o_b,
 // applied in place to float32 rows. The kernel is HBM-bound: per row it
-// reads o, o_b, lse, lse_b and writes o, lse (12 d + 12 bytes). Each thread
-// owns 16 bytes of a row, so a wave moves whole 512-byte rows at d = 128
-// with fully coalesced accesses.
+// reads o, o_b, lse, lse_b and writes o, lse (12 d + 12 bytes). A thread
+// owns U of the d/4 16-byte units of one row (U = min(4, d/4)), so the four
+// transcendentals of the weights are paid once per 16 U bytes: with T = d/4/U
+// threads per row, thread j takes units j, j + T, ..., so each load and store
+// instruction of a wave covers contiguous runs of 16 T bytes. d is a power of
+// two, so rows and units come from shifts.
 #include "ra_internal.h"
 
 namespace ra {
 namespace {
 
-__global__ __launch_bounds__(256) void lse_merge_kernel(int64_t rows, int32_t d4, float *o,
-                                                        float *lse, const float *o_b,
-                                                        const float *lse_b) {
-  const int64_t n = rows * d4;
+template <int U>
+__global__ __launch_bounds__(256) void lse_merge_kernel(int64_t n_units, int32_t shift,
+                                                        int32_t d4, float *o, float *lse,
+                                                        const float *o_b, const float *lse_b) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   float4 *o4 = reinterpret_cast<float4 *>(o);
   const float4 *ob4 = reinterpret_cast<const float4 *>(o_b);
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += stride) {
-    const int64_t r = i / d4;
-    const int32_t c = static_cast<int32_t>(i - r * d4);
+  constexpr int LU = U == 4 ? 2 : U == 2 ? 1 : 0;
+  const int32_t tpr = d4 >> LU;   // threads per row
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; u < n_units;
+       u += stride) {
+    const int64_t r = u >> (shift - LU);  // row (d4 = 1 << shift units per row)
+    const int32_t c = static_cast<int32_t>(u & (tpr - 1));
+    const int64_t i = (r << shift) + c;   // this thread's first unit; then every tpr-th
+    float4 x[U], y[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      x[k] = o4[i + k * tpr];
+      y[k] = ob4[i + k * tpr];
+    }
     const float l1 = lse[r];
     const float l2 = lse_b[r];
     const float m = fmaxf(l1, l2);
@@ -31,15 +43,16 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(int64_t rows, int32_t d4
       w1 = expf(l1 - out);
       w2 = expf(l2 - out);
     }
-    const float4 x = o4[i];
-    const float4 y = ob4[i];
-    float4 z;
-    z.x = w1 * x.x + w2 * y.x;
-    z.y = w1 * x.y + w2 * y.y;
-    z.z = w1 * x.z + w2 * y.z;
-    z.w = w1 * x.w + w2 * y.w;
-    o4[i] = z;
-    // Every lane of a row sits in the same wave (d4 divides 64) and reads
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      float4 z;
+      z.x = w1 * x[k].x + w2 * y[k].x;
+      z.y = w1 * x[k].y + w2 * y[k].y;
+      z.z = w1 * x[k].z + w2 * y[k].z;
+      z.w = w1 * x[k].w + w2 * y[k].w;
+      o4[i + k * tpr] = z;
+    }
+    // Every thread of a row sits in the same wave (tpr divides 64) and reads
     // lse[r] before this store is issued.
     if (c == 0) lse[r] = out;
   }
@@ -49,14 +62,22 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(int64_t rows, int32_t d4
 
 hipError_t launch_lse_merge(int64_t rows, int32_t d, float *o, float *lse, const float *o_b,
                             const float *lse_b, hipStream_t stream) {
-  const int32_t d4 = d / 4;
-  const int64_t n = rows * d4;
-  if (n == 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
+  const int32_t d4 = d / 4;  // a power of two, 1 .. 64
+  int32_t shift = 0;
+  while ((1 << shift) < d4) ++shift;
+  const int U = d4 >= 4 ? 4 : d4;
+  const int64_t n_units = rows * d4 / U;
+  if (n_units == 0) return hipSuccess;
+  int64_t blocks = (n_units + 255) / 256;
   // Enough waves to cover the 256 CUs several times; the rest is grid-stride.
   if (blocks > 256 * 16) blocks = 256 * 16;
-  lse_merge_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(rows, d4, o, lse, o_b,
-                                                                       lse_b);
+  const unsigned g = static_cast<unsigned>(blocks);
+  if (U == 4)
+    lse_merge_kernel<4><<<g, 256, 0, stream>>>(n_units, shift, d4, o, lse, o_b, lse_b);
+  else if (U == 2)
+    lse_merge_kernel<2><<<g, 256, 0, stream>>>(n_units, shift, d4, o, lse, o_b, lse_b);
+  else
+    lse_merge_kernel<1><<<g, 256, 0, stream>>>(n_units, shift, d4, o, lse, o_b, lse_b);
   return hipGetLastError();
 }
 

@@ -43,7 +43,8 @@ def _merge_case(rows, d, seed):
     return o, lse, ob, lseb
 
 
-@pytest.mark.parametrize("rows,d", [(1, 128), (1000, 128), (4099, 64), (64, 4), (777, 256)])
+@pytest.mark.parametrize("rows,d", [(1, 128), (1000, 128), (4099, 64), (64, 4), (33, 8),
+                                    (5, 16), (777, 256)])
 def test_lse_merge_matches_oracle(rows, d):
     o, lse, ob, lseb = _merge_case(rows, d, seed=rows + d)
     print(f"merge rows={rows} d={d}", flush=True)
