@@ -91,73 +91,6 @@ hipError_t launch_slot_rows(const int32_t *pos, int32_t *row, int64_t c, int32_t
   return hipGetLastError();
 }
 
-// vt[bi, h, e, p] = chunks[j, bi, a, h, e] for the position p = pos_j(a)
-// whose slot row src_row[p] = j*b*c + a (slot_rows_kernel): the V gather
-// and the transpose to [b, n_kv, d, S] in one pass, bf16. A workgroup moves a
-// 64-position x 64-channel tile through LDS: 16-byte loads along the channels
-// of each position's row, 16-byte stores along the positions of each channel
-// row. 16-byte chunk k of tile row r sits at chunk k ^ (r/8 % 8), so the
-// column reads of the store phase hit eight different chunks (no bank
-// conflicts) while the row writes stay contiguous. Rows past S read as zero
-// and are not stored (S % 8 == 0, so a stored 8-position chunk is whole).
-constexpr int GT = 64;  // tile edge (positions and channels)
-__global__ __launch_bounds__(256) void kv_gather_vt_kernel(const uint16_t *__restrict__ chunks,
-                                                           uint16_t *__restrict__ vt,
-                                                           const int32_t *__restrict__ src_row,
-                                                           int64_t c, int64_t S, int32_t n_kv,
-                                                           int32_t d) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[GT * GT];
-  const int tid = threadIdx.x;
-  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * GT;
-  const int e0 = blockIdx.y * GT;
-  const int bh = blockIdx.z;  // bi * n_kv + h
-  const int bi = bh / n_kv, h = bh - bi * n_kv;
-  const int c8 = tid & 7;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int r = (tid >> 3) + 32 * k;
-    const int64_t p = p0 + r;
-    uint4 x = uint4{0, 0, 0, 0};
-    if (p < S && e0 + c8 * 8 < d) {
-      const int64_t row = src_row[p] + static_cast<int64_t>(bi) * c;
-      x = *reinterpret_cast<const uint4 *>(chunks + (row * n_kv + h) * d + e0 + c8 * 8);
-    }
-    *reinterpret_cast<uint4 *>(tile + r * GT + ((c8 ^ ((r >> 3) & 7)) << 3)) = x;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int e = (tid >> 3) + 32 * k;  // channel row of the tile
-    const int pc = c8;                  // 8-position chunk
-    const int64_t p = p0 + pc * 8;
-    if (p >= S || e0 + e >= d) continue;
-    uint16_t v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = pc * 8 + i;  // (r >> 3) & 7 == pc
-      v[i] = tile[r * GT + (((e >> 3) ^ pc) << 3) + (e & 7)];
-    }
-    uint4 y;
-    y.x = v[0] | (static_cast<uint32_t>(v[1]) << 16);
-    y.y = v[2] | (static_cast<uint32_t>(v[3]) << 16);
-    y.z = v[4] | (static_cast<uint32_t>(v[5]) << 16);
-    y.w = v[6] | (static_cast<uint32_t>(v[7]) << 16);
-    *reinterpret_cast<uint4 *>(vt + (static_cast<int64_t>(bh) * d + e0 + e) * S + p) = y;
-  }
-}
-
-hipError_t launch_kv_gather_vt(const void *chunks, void *vt, const int32_t *src_row, int64_t c,
-                               int32_t b, int64_t S, int32_t n_kv, int32_t d, hipStream_t stream) {
-  if (b == 0 || S == 0) return hipSuccess;
-  const int64_t gx = (S + GT - 1) / GT, gy = (d + GT - 1) / GT;
-  const int64_t gz = static_cast<int64_t>(b) * n_kv;
-  if (gx > INT32_MAX || gz > 65535) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy), static_cast<unsigned>(gz));
-  kv_gather_vt_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(chunks),
-                                                static_cast<uint16_t *>(vt), src_row, c, S, n_kv, d);
-  return hipGetLastError();
-}
-
 struct AgPlan {
   int64_t c = 0;
   size_t full_bytes = 0;    // K (or V) of the whole sequence [b, S, n_kv, d]
@@ -300,8 +233,8 @@ extern "C" ra_status ra_allgather_fwd(const ra_ring_desc *r, const void *q, cons
     st = hip_check(ra::launch_slot_rows(pos, src_row, P.c, r->b, r->S, s),
                    "ra_allgather_fwd: slot rows");
     if (st == RA_OK)
-      st = hip_check(ra::launch_kv_gather_vt(v_chunks, vtfull, src_row, P.c, r->b, r->S, r->n_kv,
-                                             r->d, s),
+      st = hip_check(ra::launch_rows_to_vt(v_chunks, vtfull, src_row, P.c, r->b, r->S, r->n_kv,
+                                           r->d, s),
                      "ra_allgather_fwd: V gather (transposed)");
   } else if (st == RA_OK) {
     st = hip_check(ra::launch_kv_gather(v_chunks, vfull, pos, P.c, r->N, r->b, r->S, row_bytes, s),

@@ -97,6 +97,10 @@ hipError_t launch_gather_i32(const int32_t *src, const int32_t *idx, int32_t *ou
                              hipStream_t stream);
 hipError_t launch_v_transpose(int32_t b, int64_t s, int32_t n_kv, int32_t d, int32_t esize,
                               const void *v, void *vt, hipStream_t stream);
+// bf16 rows -> V^T [b, n_kv, d, s] with 16-byte accesses (s % 8 == 0, d % 8 == 0):
+// position p of batch bi is row (src_row ? src_row[p] : p) + bi * bstride of src.
+hipError_t launch_rows_to_vt(const void *src, void *vt, const int32_t *src_row, int64_t bstride,
+                             int32_t b, int64_t s, int32_t n_kv, int32_t d, hipStream_t stream);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

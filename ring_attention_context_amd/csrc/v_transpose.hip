@@ -2,9 +2,10 @@
 //
 // Data movement only. The bf16 attention kernel reads V^T tiles (d-rows of
 // keys) with plain 16-byte LDS reads; the ring produces that layout for each
-// incoming chunk on its copy stream. HBM-bound: each element is read once and
-// written once, through a 64 x 64 LDS tile so that both the reads (along d)
-// and the writes (along s) are contiguous across the wave.
+// incoming chunk on its copy stream, and the all-gather forward gathers V
+// straight into it. HBM-bound: each element is read once and written once,
+// through a 64 x 64 LDS tile so that both the reads (along d) and the writes
+// (along s) are contiguous across the wave.
 #include "ra_internal.h"
 
 namespace ra {
@@ -43,7 +44,72 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const T *__restrict__ 
   }
 }
 
+// bf16 with s % 8 == 0 and d % 8 == 0: 16-byte accesses on both sides.
+// Position p of batch bi is source row (src_row ? src_row[p] : p) + bi *
+// bstride of `src` [rows, n_kv, d]; vt is [b, n_kv, d, s]. A workgroup moves a
+// 64-position x 64-channel tile: 16-byte loads along the channels of each
+// position's row, 16-byte stores along the positions of each channel row.
+// 16-byte chunk k of tile row r sits at chunk k ^ (r/8 % 8), so the column
+// reads of the store phase hit eight different chunks (no bank conflicts)
+// while the row writes stay contiguous. Positions past s read as zero and are
+// not stored (a stored 8-position chunk is whole).
+__global__ __launch_bounds__(256) void rows_to_vt_kernel(const uint16_t *__restrict__ src,
+                                                         uint16_t *__restrict__ vt,
+                                                         const int32_t *__restrict__ src_row,
+                                                         int64_t bstride, int64_t s,
+                                                         int32_t n_kv, int32_t d) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TS * TS];
+  const int tid = threadIdx.x;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * TS;
+  const int e0 = blockIdx.y * TS;
+  const int bh = blockIdx.z;  // bi * n_kv + h
+  const int bi = bh / n_kv, h = bh - bi * n_kv;
+  const int c8 = tid & 7;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int r = (tid >> 3) + 32 * k;
+    const int64_t p = p0 + r;
+    uint4 x = uint4{0, 0, 0, 0};
+    if (p < s && e0 + c8 * 8 < d) {
+      const int64_t row = (src_row ? src_row[p] : p) + static_cast<int64_t>(bi) * bstride;
+      x = *reinterpret_cast<const uint4 *>(src + (row * n_kv + h) * d + e0 + c8 * 8);
+    }
+    *reinterpret_cast<uint4 *>(tile + r * TS + ((c8 ^ ((r >> 3) & 7)) << 3)) = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int e = (tid >> 3) + 32 * k;  // channel row of the tile
+    const int pc = c8;                  // 8-position chunk
+    const int64_t p = p0 + pc * 8;
+    if (p >= s || e0 + e >= d) continue;
+    uint16_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)  // tile row pc*8 + i, whose (row / 8) % 8 is pc
+      v[i] = tile[(pc * 8 + i) * TS + (((e >> 3) ^ pc) << 3) + (e & 7)];
+    uint4 y;
+    y.x = v[0] | (static_cast<uint32_t>(v[1]) << 16);
+    y.y = v[2] | (static_cast<uint32_t>(v[3]) << 16);
+    y.z = v[4] | (static_cast<uint32_t>(v[5]) << 16);
+    y.w = v[6] | (static_cast<uint32_t>(v[7]) << 16);
+    *reinterpret_cast<uint4 *>(vt + (static_cast<int64_t>(bh) * d + e0 + e) * s + p) = y;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rows_to_vt(const void *src, void *vt, const int32_t *src_row, int64_t bstride,
+                             int32_t b, int64_t s, int32_t n_kv, int32_t d, hipStream_t stream) {
+  if (b == 0 || s == 0) return hipSuccess;
+  const int64_t gx = (s + TS - 1) / TS, gy = (d + TS - 1) / TS;
+  const int64_t gz = static_cast<int64_t>(b) * n_kv;
+  if (gx > INT32_MAX || gz > 65535 || s % 8 || d % 8) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy), static_cast<unsigned>(gz));
+  rows_to_vt_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(src),
+                                              static_cast<uint16_t *>(vt), src_row, bstride, s,
+                                              n_kv, d);
+  return hipGetLastError();
+}
 
 hipError_t launch_v_transpose(int32_t b, int64_t s, int32_t n_kv, int32_t d, int32_t esize,
                               const void *v, void *vt, hipStream_t stream) {
@@ -53,6 +119,9 @@ hipError_t launch_v_transpose(int32_t b, int64_t s, int32_t n_kv, int32_t d, int
   const int64_t gz = static_cast<int64_t>(b) * n_kv;
   if (gx > INT32_MAX || gz > 65535) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy), static_cast<unsigned>(gz));
+  const bool a16 = ((reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(vt)) & 15) == 0;
+  if (esize == 2 && s % 8 == 0 && d % 8 == 0 && a16)
+    return launch_rows_to_vt(v, vt, nullptr, s, b, s, n_kv, d, stream);
   if (esize == 2)
     v_transpose_kernel<uint16_t><<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(v),
                                                            static_cast<uint16_t *>(vt), s, n_kv, d);

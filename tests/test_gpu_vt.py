@@ -25,6 +25,8 @@ def _gpu():
 @pytest.mark.parametrize("shape,dtype", [
     ((1, 1000, 2, 128), torch.bfloat16),   # ragged token tail
     ((2, 64, 3, 128), torch.bfloat16),
+    ((2, 200, 3, 72), torch.bfloat16),     # ragged channel tile (16-byte path)
+    ((1, 77, 2, 64), torch.bfloat16),      # s % 8 != 0: element-wise path
     ((1, 77, 5, 72), torch.float32),       # ragged channel tile
     ((3, 130, 1, 64), torch.float32),
 ])
