@@ -588,8 +588,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one rank's shard on ONE GPU; runs on more than one GPU "
-              "are not part of this build (--gpus must be 1)", file=sys.stderr)
+        print("bench.py measures one context-parallel rank's shard on ONE GPU (each rank's "
+              "work is replayed there); multi-GPU runs are not supported (--gpus must be 1)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
