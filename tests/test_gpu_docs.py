@@ -382,3 +382,65 @@ def test_allgather_bwd_workload_sampled_rows_and_invariant():
     err, m = _grad_close(dq[:, rows], rq, "dq rows")
     print(f"  dq rows {len(rows)}: max err {err:.2e} (max |ref| {m:.2e}); "
           f"max |sum dk| / sum |dk| {np.max(np.abs(tot) / mag):.2e}", flush=True)
+
+
+def test_allgather_batched_matches_oracle():
+    """b = 2 through the all-gather forward and backward (the batch strides of the
+    position -> chunk slot row map, of V gathered into V^T and of the dK, dV rows
+    added into the slots), each batch element against the oracle on its own;
+    S % 64 != 0 gives a ragged V^T tile."""
+    kind, N, S, n_q, n_kv, rank, b, d = "zigzag", 4, 1000, 8, 2, 1, 2, 128
+    print(f"all-gather batched b={b} {kind} N={N} S={S} rank={rank}", flush=True)
+    rng = np.random.default_rng(4242)
+    c = S // N
+    lengths = _lengths(rng, S, 60)
+    k, k64 = rand_inputs((b, S, n_kv, d), "bf16", rng)
+    v, v64 = rand_inputs((b, S, n_kv, d), "bf16", rng)
+    q, q64 = rand_inputs((b, c, n_q, d), "bf16", rng)
+    do, do64 = rand_inputs((b, c, n_q, d), "bf16", rng)
+    tq = to_device(q, "bf16")
+    kc = runner.chunk_kv(to_device(k, "bf16"), kind, N)
+    vc = runner.chunk_kv(to_device(v, "bf16"), kind, N)
+    ds = torch.from_numpy(runner.doc_start_positions(lengths)).cuda()
+    ids = odoc.doc_ids_from_lengths(lengths)
+    scale = np.float32(1 / np.sqrt(d))
+    desc, _ = ra.ring_desc(b=b, n_q=n_q, n_kv=n_kv, d=d, dtype=ra.RA_BF16, causal=True,
+                           kind=kind, S=S, N=N, rank=rank, doc_start=ds)
+    ws = torch.full((ra.ra_allgather_workspace_bytes(desc),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    o = torch.full((b, c, n_q, d), float("nan"), device="cuda")
+    lse = torch.full((b, c, n_q), float("nan"), device="cuda")
+    ra.ra_allgather_fwd(desc, tq, kc, vc, o, lse, ws)
+    torch.cuda.synchronize()
+    o_h, lse_h = o.cpu().numpy(), lse.cpu().numpy()
+    ref = []
+    for bi in range(b):
+        sl = slice(bi, bi + 1)
+        kc64 = np.stack([k64[sl][:, opart.partition_map(kind, S, N, j)] for j in range(N)])
+        vc64 = np.stack([v64[sl][:, opart.partition_map(kind, S, N, j)] for j in range(N)])
+        ro, rl = odoc.allgather_attention(q64[sl], kc64, vc64, kind, S, N, rank, ids, True,
+                                          scale)
+        e_o, e_l = compare(o_h[sl], lse_h[sl], ro, rl, "bf16", f"batch {bi} forward")
+        print(f"  batch {bi}: max|dO| {e_o:.2e} max|dlse| {e_l:.2e}", flush=True)
+        ref.append((kc64, vc64, ro, rl))
+    # the backward takes the oracle's o and lse, as the other backward tests do
+    o_ref = torch.from_numpy(np.concatenate([r[2] for r in ref]).astype(np.float32)).cuda()
+    lse_ref = torch.from_numpy(np.concatenate([r[3] for r in ref]).astype(np.float32)).cuda()
+    wsb = torch.full((ra.ra_allgather_bwd_workspace_bytes(desc),), 0xFF, dtype=torch.uint8,
+                     device="cuda")
+    dq = torch.full((b, c, n_q, d), float("nan"), device="cuda")
+    dkc = torch.zeros((N, b, c, n_kv, d), device="cuda")
+    dvc = torch.zeros_like(dkc)
+    ra.ra_allgather_bwd(desc, tq, kc, vc, o_ref, lse_ref, to_device(do, "bf16"), dq, dkc, dvc,
+                        wsb)
+    torch.cuda.synchronize()
+    dq_h, dk_h, dv_h = dq.cpu().numpy(), dkc.cpu().numpy(), dvc.cpu().numpy()
+    for bi in range(b):
+        sl = slice(bi, bi + 1)
+        kc64, vc64 = ref[bi][0], ref[bi][1]
+        rq, rkc, rvc = odoc.allgather_attention_bwd(q64[sl], kc64, vc64, do64[sl], kind, S, N,
+                                                    rank, ids, True, scale)
+        for got, want, name in ((dq_h[sl], rq, "dq"), (dk_h[:, sl], rkc, "dk"),
+                                (dv_h[:, sl], rvc, "dv")):
+            err, mag = _grad_close(got, want, f"batch {bi} {name}")
+            print(f"  batch {bi} {name}: max err {err:.2e} (max |ref| {mag:.2e})", flush=True)
