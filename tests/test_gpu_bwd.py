@@ -228,3 +228,54 @@ def test_full_workload_bwd_sampled_rows_and_invariant(name):
     err, m = grad_close(dq[:, rows], rq, f"{name} dq rows")
     print(f"  dq rows {len(rows)}: max err {err:.2e} (max |ref| {m:.2e}); "
           f"max |sum dk| / sum |dk| {np.max(np.abs(tot) / mag):.2e}", flush=True)
+
+
+def test_ring_batched_forward_and_backward():
+    """b = 2 through ra_ring_fwd and every rank's ra_ring_bwd (the [N, b, c, ...]
+    chunk layout and the per-batch rows of every step), against naive attention
+    and its backward over the whole sequence."""
+    kind, N, S, b = "zigzag", 4, 1536, 2
+    print(f"ring batched b={b} {kind} N={N} S={S}", flush=True)
+    w = synth.Workload("bwd_b2", b, S, N, kind, 8, 2, 128, "bf16", 1.0, True, seed=77)
+    rng = np.random.default_rng(77)
+    full = synth.draw(w.with_(N=1, kind="contiguous", rank=0))      # q for every token
+    k64, v64 = full.k64, full.v64
+    assert full.q.shape[0] == b
+    do_bits = synth.bf16_bits(rng.standard_normal(full.q.shape, dtype=np.float32))
+    do64 = synth.bf16_to_f32(do_bits).astype(np.float64)
+    want = obwd.naive_attention_bwd(full.q64, k64, v64, do64, np.arange(S), np.arange(S), True,
+                                    w.scale)
+    kc = runner.chunk_kv(runner.host_to_device(full.k, "bf16", "cuda"), kind, N)
+    vc = runner.chunk_kv(runner.host_to_device(full.v, "bf16", "cuda"), kind, N)
+    dkc = torch.zeros((N,) + tuple(kc.shape[1:]), device="cuda")
+    dvc = torch.zeros_like(dkc)
+    for rank in range(N):
+        pos = opart.partition_map(kind, S, N, rank)
+        o, lse = oatt.naive_attention(full.q64[:, pos], k64, v64, pos, np.arange(S), True, w.scale)
+        q = runner.host_to_device(full.q[:, pos], "bf16", "cuda")
+        if rank == 1:   # the forward of one rank, all steps
+            call = runner.RingCall(q, kc, vc, kind=kind, S=S, N=N, rank=rank, causal=True,
+                                   scale=float(w.scale))
+            go, gl = call()
+            torch.cuda.synchronize()
+            assert np.abs(go.cpu().numpy() - o).max() <= 1e-2
+            assert np.abs(gl.cpu().numpy() - lse).max() <= 2e-3
+        do = runner.host_to_device(do_bits[:, pos], "bf16", "cuda")
+        desc, _ = ra.ring_desc(b=b, n_q=8, n_kv=2, d=128, dtype=ra.RA_BF16, causal=True, kind=kind,
+                               S=S, N=N, rank=rank, scale=float(w.scale))
+        ws = torch.empty(ra.ra_ring_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xFF)
+        dq = torch.full(q.shape, float("nan"), device="cuda")
+        ra.ra_ring_bwd(desc, q, kc, vc, torch.from_numpy(o.astype(np.float32)).cuda(),
+                       torch.from_numpy(lse.astype(np.float32)).cuda(), do, dq, dkc, dvc, ws)
+        torch.cuda.synchronize()
+        grad_close(dq.cpu().numpy(), want[0][:, pos], f"b2 rank {rank} dq")
+    dk = np.zeros_like(k64)
+    dv = np.zeros_like(v64)
+    dkh, dvh = dkc.cpu().numpy(), dvc.cpu().numpy()
+    for j in range(N):
+        pj = opart.partition_map(kind, S, N, j)
+        dk[:, pj] = dkh[j]
+        dv[:, pj] = dvh[j]
+    grad_close(dk, want[1], "b2 dk")
+    grad_close(dv, want[2], "b2 dv")
