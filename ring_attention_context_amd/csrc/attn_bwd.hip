@@ -735,7 +735,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // left to itself the compiler keeps K, V in VGPRs and S, dP in AGPRs, and
   // moves all 32 results out of AGPRs on every sub-block. The compiler's
   // hazard checks do not see these MFMAs: their results are read by B one
-  // iteration later, or by the mask after acc_settle().
+  // iteration later (after several MFMAs), or by the element mask, which
+  // first waits out their writes.
   auto mfma_a = [&](int par, int ai, const bf16x8 &o) INLINE {
     const int ds = ai >> 1;
     f32x16 &r = (ai & 1) ? dp[par] : s[par];
