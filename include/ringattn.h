@@ -146,8 +146,10 @@ ra_status ra_v_transpose(int32_t b, int64_t s, int32_t n_kv, int32_t d, int32_t 
  * form: M = max(lse, lse_b), lse' = M + ln(e^{lse-M} + e^{lse_b-M}),
  * o' = e^{lse-lse'} o + e^{lse_b-lse'} o_b. A row with lse = lse_b = -inf
  * becomes (0, -inf).
- * rows: number of (token, head) rows; o, o_b: device float32 [rows, d];
- * lse, lse_b: device float32 [rows]. d % 4 == 0 and 1 <= d <= 256.
+ * rows: number of (token, head) rows; o, o_b: device float32 [rows, d],
+ * 16-byte aligned; lse, lse_b: device float32 [rows]. d must be a power of
+ * two in [4, 256]. Returns RA_ERR_INVALID_ARG for rows < 0, another d, a NULL
+ * or misaligned pointer (rows == 0 is a no-op that reads no pointer).
  */
 ra_status ra_lse_merge(int64_t rows, int32_t d, float *o, float *lse, const float *o_b,
                        const float *lse_b, void *stream);
