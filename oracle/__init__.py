@@ -25,7 +25,8 @@ Modules:
   (primary oracle), the per-block statistics and the two-block merge
   (secondary, block-then-merge oracle), and the ring schedule.
 * :mod:`oracle.partition` -- contiguous / zig-zag / striped token maps,
-  visible-pair counts, tile classification and ring efficiency.
+  visible-pair counts, tile classification, tile-level work and ring
+  efficiency.
 * :mod:`oracle.backward` -- the gradients of softmax attention (plain
   definition by the chain rule), one block's contributions with the global
   lse (§3 backward paragraph), and the ring backward (§4).
@@ -33,9 +34,16 @@ Modules:
   gathered into global order, and the rank's attention under the document
   mask (no attention across documents) combined with the causal rule.
 
-Parity status: every function here is pinned by ``tests/test_oracle*.py``
+Parity status: every public function here is pinned by ``tests/test_oracle*.py``
 against closed forms, brute force, a library special case or numbers the
-pages print. No function is "parity unpinned".
+pages print, and the planted-mistake tests show the pins catch a wrong
+sign, term, index or operand in each. The row-subset checkers
+(``attention.rows_attention``, ``documents.rows_attention_docs``) are pinned
+against brute-force loops on chosen rows; the work counts (``rank_work``,
+``tile_work_pairs``, ``tile_work_pairs_increasing``, ``tile_step_work``) against
+brute-force tile loops and the per-rank closed forms; the FLOP convention
+(``causal_adjusted_flops``) against counted multiply-adds and the
+communication-hiding thresholds §4 prints.
 """
 
 from . import attention, backward, documents, partition  # noqa: F401

@@ -139,6 +139,40 @@ def tile_work_pairs(q_pos, kv_pos, Bq, Bk, causal=True):
     return total
 
 
+def tile_work_pairs_increasing(q_pos, kv_pos, Bq, Bk):
+    """tile_work_pairs for causal attention when both position lists are
+    strictly increasing (every map of §2 / §6 is): a tile then holds a
+    visible pair exactly when its first key is not after its last query, so
+    the tile test needs only the two end positions (§7's per-tile skip).
+    Element slots of the non-skipped tiles; ragged tiles by their real size."""
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    kv_pos = np.asarray(kv_pos, dtype=np.int64)
+    c, s = q_pos.size, kv_pos.size
+    if c == 0 or s == 0:
+        return 0
+    q_starts = np.arange(0, c, Bq)
+    k_starts = np.arange(0, s, Bk)
+    q_last = q_pos[np.minimum(q_starts + Bq, c) - 1]
+    k_first = kv_pos[k_starts]
+    rows = np.minimum(q_starts + Bq, c) - q_starts
+    cols = np.minimum(k_starts + Bk, s) - k_starts
+    keep = k_first[None, :] <= q_last[:, None]
+    return int((rows[:, None] * cols[None, :] * keep).sum())
+
+
+def tile_step_work(kind, S, N, Bq, Bk):
+    """W[i, r]: element slots of the non-skipped (Bq x Bk) tiles that rank i
+    computes at ring step r, causal (the tile-level counterpart of
+    :func:`step_work`; §7: real kernels skip whole tiles, so the diagonal is
+    discounted at tile granularity)."""
+    maps = [partition_map(kind, S, N, i) for i in range(N)]
+    W = np.zeros((N, N), dtype=np.int64)
+    for i in range(N):
+        for r, src in enumerate(ring_sources(i, N)):
+            W[i, r] = tile_work_pairs_increasing(maps[i], maps[src], Bq, Bk)
+    return W
+
+
 def kv_bytes(b, s, n_kv, d_h, bytes_per_elem=2):
     """§8: full K/V of one layer is 2 * 2 * b * s * n_kv * d_h bytes in bf16
     (K and V, two bytes each)."""

@@ -5,7 +5,7 @@ Each ``pin_*`` takes an object ``A`` exposing ``naive_attention`` (the primary
 forward oracle, pinned on its own by tests/oracle_pins.py), ``partition_map``,
 and the functions of oracle/documents.py (``doc_ids_from_lengths``,
 ``doc_start``, ``visible_docs``, ``masked_attention``, ``allgather_kv``,
-``allgather_attention``, ``doc_visible_pairs``); it raises AssertionError when
+``allgather_attention``, ``rows_attention_docs``, ``doc_visible_pairs``); it raises AssertionError when
 the oracle disagrees.
 
 What pins what ("Context Parallelism and Ring Attention", §8 all-gather CP):
@@ -18,7 +18,8 @@ What pins what ("Context Parallelism and Ring Attention", §8 all-gather CP):
   the plain causal oracle;
 * every token its own document: a query sees only its own key, so o is its
   own V row and lse its own score;
-* brute force: Python loops with math.exp on tiny inputs;
+* brute force: Python loops with math.exp on tiny inputs (the whole
+  sequence, and chosen rows through rows_attention_docs);
 * the all-gather: gathering the chunks that the §6 maps cut from a sequence
   gives the sequence back bit for bit, for every map;
 * zig-zag and striped reordering (§6, masks on original positions): every
@@ -165,7 +166,36 @@ def pin_docs_pair_counts(A):
             assert A.doc_visible_pairs(qp, ids, causal) == brute
 
 
-DOC_PINS = [pin_docs_independent_documents, pin_docs_one_document, pin_docs_singletons,
+def pin_docs_rows(A):
+    """rows_attention_docs on chosen rows equals brute force with the document
+    mask on those rows, and the rows of the whole-sequence masked result."""
+    rng = np.random.default_rng(208)
+    lengths = [5, 2, 9, 4, 12]
+    S = sum(lengths)
+    ids = A.doc_ids_from_lengths(lengths)
+    doc_of = np.repeat(np.arange(len(lengths)), lengths)
+    q_all, k, v = _qkv(rng, 2, S, S, 4, 2, 3)
+    pos = np.arange(S)
+    rows = np.array([0, 4, 5, 6, 15, 20, S - 1])
+    for causal in (True, False):
+        o, lse = A.rows_attention_docs(q_all[:, rows], k, v, pos[rows], ids, causal, 0.65)
+        want_o, want_lse = A.masked_attention(q_all, k, v, A.visible_docs(pos, pos, ids, causal),
+                                              0.65)
+        assert np.max(np.abs(o - want_o[:, rows])) < 1e-12, "rows vs whole-sequence rows"
+        assert np.max(np.abs(lse - want_lse[:, rows])) < 1e-12
+        for bi in range(2):
+            for a, p in enumerate(rows):
+                for h in range(4):
+                    xs = [(j, 0.65 * sum(q_all[bi, p, h, e] * k[bi, j, h // 2, e] for e in range(3)))
+                          for j in range(S) if doc_of[j] == doc_of[p] and (j <= p or not causal)]
+                    tot = sum(math.exp(x) for _, x in xs)
+                    assert abs(lse[bi, a, h] - math.log(tot)) < 1e-12, "rows brute-force lse"
+                    for e in range(3):
+                        want = sum(math.exp(x) / tot * v[bi, j, h // 2, e] for j, x in xs)
+                        assert abs(o[bi, a, h, e] - want) < 1e-12, "rows brute-force o"
+
+
+DOC_PINS = [pin_docs_rows, pin_docs_independent_documents, pin_docs_one_document, pin_docs_singletons,
             pin_docs_brute_force, pin_docs_allgather_inverse, pin_docs_ranks_reassemble,
             pin_docs_pair_counts]
 

@@ -1,9 +1,11 @@
 """Checks that pin the CPU oracle to facts other than itself.
 
 Each ``pin_*`` function takes an object ``O`` exposing the oracle functions
-(``naive_attention``, ``block_attention``, ``merge``, ``merge_weights``,
-``ring_attention``, ``partition_map``, ``step_work``, ``visible_pairs``,
-``tile_classes``, ``ring_efficiency``, ``kv_bytes``) and raises
+(``naive_attention``, ``rows_attention``, ``block_attention``, ``merge``,
+``merge_weights``, ``ring_attention``, ``partition_map``, ``step_work``,
+``rank_work``, ``visible_pairs``, ``tile_classes``, ``tile_work_pairs``,
+``tile_work_pairs_increasing``, ``tile_step_work``, ``ring_efficiency``,
+``causal_adjusted_flops``, ``kv_bytes``) and raises
 AssertionError when the oracle disagrees with the pin. The tests run every
 pin against the real oracle, and against copies with a planted mistake to
 show that the pins catch them.
@@ -24,7 +26,12 @@ hs-black.github.io, unless stated):
   sum to 1 (§3); finite at |lse| = 700 (stable form);
 * block-then-merge equals the one-shot softmax (§3 worked example, §4 "after
   N steps every Q has seen all K/V");
-* maps and work counts against the numbers the pages print (tests/golden).
+* maps and work counts against the numbers the pages print (tests/golden);
+* per-rank work against its closed forms (contiguous, zig-zag, striped);
+* tile-level work against brute-force loops over tiles and the causal
+  triangle B^2 n (n + 1) / 2;
+* the FLOP convention against counted multiply-adds, and against the
+  communication-hiding thresholds the pages print (§4).
 """
 
 import math
@@ -254,7 +261,30 @@ def pin_merge_weights(O):
     assert np.allclose(w1 / w2, np.exp(l1 - l2), rtol=1e-12), "weight ratio e^{lse1-lse2}"
 
 
-ATTENTION_PINS = [pin_bruteforce, pin_torch_sdpa, pin_zero_query, pin_single_key,
+def pin_rows_attention(O):
+    """rows_attention on chosen rows equals brute force on those rows against
+    the whole sequence in global order, and the full naive result's rows."""
+    rng = np.random.default_rng(20)
+    S, N, d = 24, 4, 3
+    k = _rand((2, S, 2, d), rng)
+    v = _rand((2, S, 2, d), rng)
+    for kind in ("contiguous", "zigzag", "striped"):
+        for rank in (0, N - 1):
+            q_pos = np.asarray(O.partition_map(kind, S, N, rank))
+            q = _rand((2, q_pos.size, 4, d), rng)
+            rows = np.array([0, 2, q_pos.size - 1])
+            for causal in (True, False):
+                o, lse = O.rows_attention(q[:, rows], k, v, q_pos[rows], causal, 0.55)
+                o_bf, lse_bf = brute_force(q[:, rows], k, v, q_pos[rows], np.arange(S), causal,
+                                           0.55)
+                assert np.allclose(o, o_bf, rtol=0, atol=1e-12), "rows vs brute force (o)"
+                assert np.allclose(lse, lse_bf, rtol=0, atol=1e-12), "rows vs brute force (lse)"
+                o_n, lse_n = O.naive_attention(q, k, v, q_pos, np.arange(S), causal, 0.55)
+                assert np.allclose(o, o_n[:, rows], rtol=0, atol=1e-12), "rows vs naive rows"
+                assert np.allclose(lse, lse_n[:, rows], rtol=0, atol=1e-12)
+
+
+ATTENTION_PINS = [pin_rows_attention, pin_bruteforce, pin_torch_sdpa, pin_zero_query, pin_single_key,
                   pin_causality, pin_ring_equals_naive, pin_random_split_merge,
                   pin_merge_closed_forms, pin_merge_weights]
 
@@ -292,8 +322,8 @@ def pin_n4_rank_work(O):
     for c in (8, 32, 128):
         S, unit = N * c, (c // 2) ** 2
         for kind in ("contiguous", "zigzag"):
-            W = np.asarray(O.step_work(kind, S, N))
-            per_rank = W.sum(axis=1)
+            per_rank = np.asarray(O.rank_work(kind, S, N))
+            assert np.array_equal(per_rank, np.asarray(O.step_work(kind, S, N)).sum(axis=1))
             # the figure counts each chunk's own diagonal block as half a block;
             # the exact count adds the diagonal itself: c/2 pairs per rank
             units = (per_rank - c // 2) / unit
@@ -391,6 +421,110 @@ def pin_kv_bytes(O):
     assert O.kv_bytes(b, s, n_kv // 8, d) == int(gold["tp8_MiB"][0]) << 20
 
 
-PARTITION_PINS = [pin_maps_are_permutations, pin_map_definitions, pin_n4_rank_work,
+def pin_rank_work_closed_forms(O):
+    """Per-rank visible pairs (§5, §6): contiguous rank i sees all of the i
+    earlier segments plus its own triangle, i c^2 + c (c + 1) / 2; zig-zag
+    gives every rank S c / 2 + c / 2; striped rank i (positions a N + i) sees
+    N c (c - 1) / 2 + c (i + 1). Non-causal: c S for every rank."""
+    for N in (1, 2, 3, 4, 8):
+        for c in (2, 6, 10):
+            S = N * c
+            cont = np.asarray(O.rank_work("contiguous", S, N))
+            assert np.array_equal(cont, [i * c * c + c * (c + 1) // 2 for i in range(N)])
+            stri = np.asarray(O.rank_work("striped", S, N))
+            assert np.array_equal(stri, [N * c * (c - 1) // 2 + c * (i + 1) for i in range(N)])
+            zz = np.asarray(O.rank_work("zigzag", S, N))
+            assert np.array_equal(zz, [S * c // 2 + c // 2] * N)
+            for kind in ("contiguous", "zigzag", "striped"):
+                assert np.array_equal(np.asarray(O.rank_work(kind, S, N, False)), [c * S] * N)
+
+
+def _brute_tile_slots(q_pos, kv_pos, Bq, Bk, causal):
+    """Element slots of tiles holding at least one visible pair, by loops."""
+    total = 0
+    for a0 in range(0, len(q_pos), Bq):
+        for t0 in range(0, len(kv_pos), Bk):
+            qs = q_pos[a0:a0 + Bq]
+            ks = kv_pos[t0:t0 + Bk]
+            if any((not causal) or kp <= qp for qp in qs for kp in ks):
+                total += len(qs) * len(ks)
+    return total
+
+
+def pin_tile_work(O):
+    """Tile-level work (§7: kernels skip whole tiles): brute-force loops over
+    tiles; the causal triangle of one contiguous rank with square tiles,
+    B^2 n (n + 1) / 2; the per-step table against those counts."""
+    rng = np.random.default_rng(21)
+    for _ in range(20):
+        c, s = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+        q_pos = np.sort(rng.choice(100, c, replace=False))
+        kv_pos = np.sort(rng.choice(100, s, replace=False))
+        Bq, Bk = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        for causal in (True, False):
+            want = _brute_tile_slots(q_pos, kv_pos, Bq, Bk, causal)
+            assert O.tile_work_pairs(q_pos, kv_pos, Bq, Bk, causal) == want, "tile_work_pairs"
+        assert O.tile_work_pairs_increasing(q_pos, kv_pos, Bq, Bk) == \
+            _brute_tile_slots(q_pos, kv_pos, Bq, Bk, True), "tile_work_pairs_increasing"
+    for n, B in ((1, 4), (5, 8), (7, 3)):
+        pos = np.arange(n * B)
+        assert O.tile_work_pairs(pos, pos, B, B) == B * B * n * (n + 1) // 2, "triangle"
+        assert O.tile_work_pairs_increasing(pos, pos, B, B) == B * B * n * (n + 1) // 2
+    for kind in ("contiguous", "zigzag", "striped"):
+        for N in (1, 2, 4):
+            S = 2 * N * 12
+            W = np.asarray(O.tile_step_work(kind, S, N, 4, 8))
+            for i in range(N):
+                q_pos = O.partition_map(kind, S, N, i)
+                for r, src in enumerate(O.ring_sources(i, N)):
+                    kv_pos = O.partition_map(kind, S, N, src)
+                    assert W[i, r] == _brute_tile_slots(q_pos, kv_pos, 4, 8, True), (kind, i, r)
+
+
+def _brute_flops(b, c, s, n_q, d, q_pos, kv_pos, causal):
+    """Floating-point operations of the two matmuls, counted one multiply-add
+    (2 flops) at a time over every visible pair: d for the score q . k and d
+    for the output row p v."""
+    fl = 0
+    for _ in range(b):
+        for a in range(c):
+            for _h in range(n_q):
+                for j in range(s):
+                    if causal and kv_pos[j] > q_pos[a]:
+                        continue
+                    fl += 2 * d      # q . k
+                    fl += 2 * d      # p * v accumulated into o
+    return fl
+
+
+def pin_causal_adjusted_flops(O):
+    """The FLOP convention (§4): counted multiply-adds of the two matmuls over
+    the visible pairs; and the page's hiding thresholds c = (C/W) n_kv / n_h
+    (H100 node and cross-node, MHA and GQA 8/64), where the block's math
+    (causal_adjusted_flops of a full c x c block) equals its K/V transfer
+    (kv_bytes of one chunk)."""
+    b, n_q, d = 2, 3, 5
+    q_pos, kv_pos = np.array([1, 4, 6, 9]), np.array([0, 2, 4, 5, 7, 8, 10])
+    for causal in (True, False):
+        pairs = O.visible_pairs(q_pos, kv_pos, causal)
+        assert O.causal_adjusted_flops(b, n_q, d, pairs) == \
+            _brute_flops(b, len(q_pos), len(kv_pos), n_q, d, q_pos, kv_pos, causal)
+    gold = {k: float(v[0]) for k, v in read("comm_hiding_threshold.txt").items()}
+    C = gold["C_flops"]
+    d_h, n_h = 128, 64
+    for W, mha, gqa in ((gold["W_node_Bps"], gold["node_mha_tokens"], gold["node_gqa_8_64_tokens"]),
+                        (gold["W_cross_Bps"], gold["cross_mha_tokens"],
+                         gold["cross_gqa_8_64_tokens"])):
+        for n_kv, want in ((n_h, mha), (8, gqa)):
+            # T_math(c) = flops(c^2 pairs) / C grows as c^2, T_comm(c) = bytes(c) / W as c:
+            # they meet at c* = (bytes per token / W) / (flops per pair / C)
+            per_pair = O.causal_adjusted_flops(1, n_h, d_h, 1)
+            per_token = O.kv_bytes(1, 1, n_kv, d_h)
+            c_star = (per_token / W) / (per_pair / C)
+            assert abs(c_star - want) / want < 0.02, (W, n_kv, c_star, want)
+
+
+PARTITION_PINS = [pin_rank_work_closed_forms, pin_tile_work, pin_causal_adjusted_flops,
+                  pin_maps_are_permutations, pin_map_definitions, pin_n4_rank_work,
                   pin_contiguous_efficiency, pin_zigzag_table, pin_zigzag_rectangles,
                   pin_striped_balance, pin_causal_triangle_tiles, pin_kv_bytes]

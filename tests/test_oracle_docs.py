@@ -14,7 +14,7 @@ from oracle import attention, backward, documents, partition
 def namespace():
     """Late-bound view of the oracle: monkeypatched functions are seen."""
     names = ["doc_ids_from_lengths", "doc_start", "visible_docs", "masked_attention",
-             "allgather_kv", "allgather_attention", "doc_visible_pairs",
+             "allgather_kv", "allgather_attention", "rows_attention_docs", "doc_visible_pairs",
              "masked_attention_bwd", "allgather_attention_bwd"]
     ns = {n: (lambda n: lambda *a: getattr(documents, n)(*a))(n) for n in names}
     ns["naive_attention"] = lambda *a: attention.naive_attention(*a)
@@ -102,7 +102,22 @@ def ag_bwd_chunks_rolled(*a):
     return dq, np.roll(dkc, 1, axis=0), np.roll(dvc, 1, axis=0)
 
 
+real_rows_docs = documents.rows_attention_docs
+
+
+def rows_docs_no_causal(q, k, v, qp, ids, causal, scale):
+    return real_rows_docs(q, k, v, qp, ids, False, scale)
+
+
+def rows_docs_shifted_keys(q, k, v, qp, ids, causal, scale):
+    """Document mask taken one position off for the keys."""
+    vis = documents.visible_docs(qp, np.arange(k.shape[1]), np.roll(ids, 1), causal)
+    return documents.masked_attention(q, k, v, vis, scale)
+
+
 MUTANTS = {
+    "rows_docs_no_causal": ("rows_attention_docs", rows_docs_no_causal),
+    "rows_docs_shifted_keys": ("rows_attention_docs", rows_docs_shifted_keys),
     "masked_bwd_no_delta": ("masked_attention_bwd", masked_bwd_no_delta),
     "masked_bwd_dk_unscaled": ("masked_attention_bwd", masked_bwd_dk_unscaled),
     "ag_bwd_chunks_rolled": ("allgather_attention_bwd", ag_bwd_chunks_rolled),

@@ -13,6 +13,58 @@ real_naive = attention.naive_attention
 real_block = attention.block_attention
 real_merge = attention.merge
 real_map = partition.partition_map
+real_rows = attention.rows_attention
+real_tile_pairs = partition.tile_work_pairs
+real_tile_inc = partition.tile_work_pairs_increasing
+real_step_work = partition.step_work
+
+
+def rows_kv_shifted(q, k, v, qp, c, s):
+    """Keys placed one position later than their index."""
+    return real_naive(q, k, v, qp, np.arange(k.shape[1]) + 1, c, s)
+
+
+def rows_kv_reversed(q, k, v, qp, c, s):
+    return real_naive(q, k, v, qp, np.arange(k.shape[1])[::-1], c, s)
+
+
+def tile_pairs_diag_skipped(q_pos, kv_pos, Bq, Bk, causal=True):
+    """Counts only fully visible tiles (drops the diagonal ones)."""
+    cls = partition.tile_classes(q_pos, kv_pos, Bq, Bk, causal)
+    total = 0
+    for a in range(cls.shape[0]):
+        rows = min(Bq, len(q_pos) - a * Bq)
+        for t in range(cls.shape[1]):
+            if cls[a, t] == partition.FULL:
+                total += rows * min(Bk, len(kv_pos) - t * Bk)
+    return total
+
+
+def tile_inc_first_query(q_pos, kv_pos, Bq, Bk):
+    """Tests a tile's first key against its FIRST query instead of its last."""
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    kv_pos = np.asarray(kv_pos, dtype=np.int64)
+    c, s = q_pos.size, kv_pos.size
+    qs, ks = np.arange(0, c, Bq), np.arange(0, s, Bk)
+    keep = kv_pos[ks][None, :] <= q_pos[qs][:, None]
+    rows = np.minimum(qs + Bq, c) - qs
+    cols = np.minimum(ks + Bk, s) - ks
+    return int((rows[:, None] * cols[None, :] * keep).sum())
+
+
+def tile_inc_no_ragged(q_pos, kv_pos, Bq, Bk):
+    """Counts every tile at its full size (ragged tails over-counted)."""
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    kv_pos = np.asarray(kv_pos, dtype=np.int64)
+    c, s = q_pos.size, kv_pos.size
+    qs, ks = np.arange(0, c, Bq), np.arange(0, s, Bk)
+    keep = kv_pos[ks][None, :] <= q_pos[np.minimum(qs + Bq, c) - 1][:, None]
+    return int((Bq * Bk * keep).sum())
+
+
+def rank_work_columns(kind, S, N, causal=True):
+    """Sums the per-step table over ranks instead of over steps."""
+    return real_step_work(kind, S, N, causal).sum(axis=0)
 
 
 def merge_wrong_sign(o, lse, o_b, lse_b):
@@ -58,6 +110,14 @@ MUTANTS = {
     "striped_off_by_one": ("partition_map",
                            lambda kind, S, N, r: (np.arange(S)[np.arange(S) % N == (r + 1) % N]
                                                   if kind == "striped" else real_map(kind, S, N, r))),
+    "rows_kv_shifted": ("rows_attention", rows_kv_shifted),
+    "rows_kv_reversed": ("rows_attention", rows_kv_reversed),
+    "tile_pairs_diag_skipped": ("tile_work_pairs", tile_pairs_diag_skipped),
+    "tile_inc_first_query": ("tile_work_pairs_increasing", tile_inc_first_query),
+    "tile_inc_no_ragged": ("tile_work_pairs_increasing", tile_inc_no_ragged),
+    "flops_half": ("causal_adjusted_flops", lambda b, n_q, d, pairs: 2 * b * n_q * d * pairs),
+    "flops_per_head_missing": ("causal_adjusted_flops", lambda b, n_q, d, pairs: 4 * b * d * pairs),
+    "rank_work_columns": ("rank_work", rank_work_columns),
     "contiguous_reversed": ("partition_map",
                             lambda kind, S, N, r: (real_map(kind, S, N, N - 1 - r)
                                                    if kind == "contiguous" else real_map(kind, S, N, r))),
@@ -68,6 +128,11 @@ PATCH_SITES = {
     "block_attention": [attention],
     "merge": [attention],
     "partition_map": [attention, partition],
+    "rows_attention": [attention],
+    "tile_work_pairs": [partition],
+    "tile_work_pairs_increasing": [partition],
+    "causal_adjusted_flops": [partition],
+    "rank_work": [partition],
 }
 
 
