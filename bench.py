@@ -34,6 +34,13 @@ import re
 import sys
 import time
 
+# The CPU baseline's BLAS threads: every core this process may run on, fixed
+# before NumPy (and its BLAS) is first imported, and recorded in the line.
+_CORES = len(os.sched_getaffinity(0))
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, str(_CORES))
+BLAS_ENV = {v: os.environ[v] for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz, dense
@@ -68,6 +75,27 @@ def visible_pairs_per_step(kind, S, N, rank, causal):
     return out
 
 
+def tile_pairs_per_step(kind, S, N, rank, bq=32, bk=64):
+    """(query, key) slots the attention kernel computes at each ring step
+    under its tile skip: a wave owns bq consecutive queries of one head and
+    scans bk-key tiles up to the last tile whose first key is not after its
+    last query (the maps are increasing). Causal only."""
+    import numpy as np
+    from ring_attention_context_amd import ra_partition
+    q_pos = ra_partition(kind, S, N, rank).astype(np.int64)
+    c = len(q_pos)
+    q_last = q_pos[np.minimum(np.arange(0, c, bq) + bq, c) - 1]
+    rows = np.minimum(np.arange(0, c, bq) + bq, c) - np.arange(0, c, bq)
+    out = []
+    for r in range(N):
+        kv = ra_partition(kind, S, N, (rank - r) % N).astype(np.int64)
+        k_first = kv[np.arange(0, len(kv), bk)]
+        cols = np.minimum(np.arange(0, len(kv), bk) + bk, len(kv)) - np.arange(0, len(kv), bk)
+        keep = k_first[None, :] <= q_last[:, None]
+        out.append(int((rows[:, None] * cols[None, :] * keep).sum()))
+    return out
+
+
 def committed_traffic(w, profile="attn_bf16_llama3_70b_128k_zigzag_counters.md",
                       source="attn_bf16.hip", unit="launch"):
     """HBM bytes per launch (or per ring step) of the measured kernels from the
@@ -87,35 +115,64 @@ def committed_traffic(w, profile="attn_bf16_llama3_70b_128k_zigzag_counters.md",
     return int(m.group(1).replace(",", ""))
 
 
+def blas_threads():
+    """Threads the BLAS behind NumPy actually uses (threadpoolctl), else the env."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        return int(os.environ.get("OMP_NUM_THREADS", "1"))
+
+
 def cpu_baseline(w, seconds_hint=15.0):
     """Time the fp64 CPU oracle (as it stands) on a bounded sample of the same
-    workload: a few query rows x all heads against the full sequence."""
+    workload: a few query rows x all heads against the full sequence, by the
+    plain definition (rows_attention) and by the pages' block-then-merge ring
+    path (block_attention of every step's chunk, then merge) on a smaller
+    subset of the same rows. The full shard's time is extrapolated from the
+    plain path's rate (labelled as such)."""
     import numpy as np
     import synth
     from oracle import attention as oatt
     from oracle import partition as opart
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    threads = blas_threads()
     # size the sample so the oracle runs roughly seconds_hint seconds (the NumPy
     # oracle sustains roughly 25 GFLOP/s of fp64 on a 16-core host)
     per_row = 4 * w.d * w.n_q * (w.S / 2.0 if w.causal else w.S)
     rows_n = int(max(8, min(512, seconds_hint * 2.5e10 / per_row)))
     rows = synth.sample_rows(w.c, rows_n, w.seed)
     inp = synth.draw(w, q_rows=rows)
-    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)[rows]
+    q_all_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)
+    q_pos = q_all_pos[rows]
     k64, v64, q64 = inp.k64, inp.v64, inp.q64
     t0 = time.perf_counter()
     oatt.rows_attention(q64, k64, v64, q_pos, w.causal, w.scale)
     t = time.perf_counter() - t0
     pairs = opart.visible_pairs(q_pos, np.arange(w.S), w.causal)
     flops = 4 * w.b * w.n_q * w.d * pairs
+    total_pairs = opart.visible_pairs(q_all_pos, np.arange(w.S), w.causal)
+    # block-then-merge: the first few sampled rows through every ring step
+    sub = np.arange(min(len(rows), max(2, len(rows) // 8)))
+    t1 = time.perf_counter()
+    o = np.zeros((w.b, len(sub), w.n_q, w.d))
+    lse = np.full((w.b, len(sub), w.n_q), -np.inf)
+    for src in opart.ring_sources(w.rank, w.N):
+        kv_pos = opart.partition_map(w.kind, w.S, w.N, src)
+        o_b, lse_b = oatt.block_attention(q64[:, sub], k64[:, kv_pos], v64[:, kv_pos],
+                                          q_pos[sub], kv_pos, w.causal, w.scale)
+        o, lse = oatt.merge(o, lse, o_b, lse_b)
+    tb = time.perf_counter() - t1
+    pairs_b = opart.visible_pairs(q_pos[sub], np.arange(w.S), w.causal)
+    flops_b = 4 * w.b * w.n_q * w.d * pairs_b
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {w.c} query rows x {w.n_q} heads vs all {w.S} keys "
                       f"(fp64 NumPy naive softmax, {t:.1f} s, {pairs} visible pairs)",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "extrapolated_full_shard_s": round(t * total_pairs / pairs, 1),
+            "block_merge": {"value": flops_b / tb / 1e12, "unit": "TFLOP/s",
+                            "sample": f"{len(sub)} of the sampled rows x {w.n_q} heads, every "
+                                      f"ring step's block then the merge ({tb:.1f} s, "
+                                      f"{pairs_b} visible pairs)"},
+            "blas_env": BLAS_ENV, "host_cpus": _CORES}
 
 
 def cpu_baseline_bwd(w, seconds_hint=15.0):
@@ -126,11 +183,7 @@ def cpu_baseline_bwd(w, seconds_hint=15.0):
     import synth
     from oracle import backward as obwd
     from oracle import partition as opart
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    threads = blas_threads()
     per_row = 10 * w.d * w.n_q * (w.S / 2.0 if w.causal else w.S)
     rows_n = int(max(4, min(256, seconds_hint * 1.0e10 / per_row)))
     rows = synth.sample_rows(w.c, rows_n, w.seed)
@@ -147,7 +200,7 @@ def cpu_baseline_bwd(w, seconds_hint=15.0):
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {w.c} query rows x {w.n_q} heads vs all {w.S} keys "
                       f"(fp64 NumPy backward by the chain rule, {t:.1f} s, {pairs} visible pairs)",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "blas_env": BLAS_ENV, "host_cpus": _CORES}
 
 
 def doc_pairs(q_pos, doc_start):
@@ -166,11 +219,7 @@ def cpu_baseline_docs(w, lengths, seconds_hint=15.0, backward=False):
     import synth
     from oracle import documents as odoc
     from oracle import partition as opart
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    threads = blas_threads()
     per_row = (10 if backward else 4) * w.d * w.n_q * w.S   # every key scored, then masked
     rows_n = int(max(8, min(512, seconds_hint * 2.5e10 / per_row)))
     rows = synth.sample_rows(w.c, rows_n, w.seed)
@@ -195,7 +244,7 @@ def cpu_baseline_docs(w, lengths, seconds_hint=15.0, backward=False):
             "sample": f"{len(rows)} of {w.c} query rows x {w.n_q} heads vs all {w.S} keys "
                       f"under the document mask (fp64 NumPy {what}, {t:.1f} s, "
                       f"{pairs} visible pairs)",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "blas_env": BLAS_ENV, "host_cpus": _CORES}
 
 
 def run_allgather(args, w, dev, props):
@@ -540,22 +589,27 @@ def run_sweep(path, warmup, steps):
         vc = runner.chunk_kv(runner.host_to_device(inp.v, w0.dtype, dev), kind, w0.N)
         t = np.zeros((w0.N, w0.N))
         work = np.zeros((w0.N, w0.N), dtype=np.int64)
+        tiles = np.zeros((w0.N, w0.N), dtype=np.int64)
         for rank in range(w0.N):
             w = w0.with_(rank=rank)
             ms, step_ms = time_ring(w, q, kc, vc, warmup, steps)
             t[rank] = step_ms
             work[rank] = visible_pairs_per_step(kind, w.S, w.N, rank, True)
+            tiles[rank] = tile_pairs_per_step(kind, w.S, w.N, rank)
             log(f"[sweep] {kind} rank {rank}: {ms:.3f} ms/call")
         ring_ms = float(t.max(axis=0).sum())
         eta_meas = float(t.sum() / w0.N / ring_ms)
         eta_elem = float(work.sum() / w0.N / work.max(axis=0).sum())
+        eta_tile = float(tiles.sum() / w0.N / tiles.max(axis=0).sum())
         flops = 4 * w0.b * w0.n_q * w0.d * work.sum() / w0.N
         out["imbalance"].append({
             "kind": kind, "step_ms": t.tolist(), "pairs": work.tolist(),
+            "tile_slots_32x64": tiles.tolist(),
             "ring_ms_step_max": ring_ms, "eta_measured": eta_meas, "eta_element": eta_elem,
+            "eta_tile_32x64": eta_tile,
             "ring_tflops_per_rank": flops / (ring_ms * 1e-3) / 1e12})
         log(f"[sweep] {kind}: ring (step-max) {ring_ms:.2f} ms, eta measured {eta_meas:.4f}, "
-            f"element-level {eta_elem:.4f}")
+            f"element-level {eta_elem:.4f}, tile-level (32x64) {eta_tile:.4f}")
         del q, kc, vc
         torch.cuda.empty_cache()
     with open(path, "w") as f:

@@ -203,6 +203,13 @@ ra_status ra_ring_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
  * Step r computes the block of chunk (rank - r) mod N; the copy of the next
  * step's chunk into the idle half of the double buffer runs on `copy` while
  * step r computes on `compute` (or on `compute` with RA_RING_SERIALIZE).
+ * A causal step whose block no query of the rank can see (with the
+ * contiguous map, every later rank's chunk) launches no kernel: merging its
+ * statistics would be the identity. Its chunk still arrives on `copy`, as the
+ * ring forwards it; its step event is recorded as usual.
+ * After the call the workspace's first S int32 hold the position map of
+ * every rank (rank j's c positions at [j*c, (j+1)*c)), as ra_partition
+ * gives them.
  * On return all work is enqueued and `compute` is ordered after every copy;
  * `copy` first waits for the work already enqueued on `compute`.
  * Calls that share a workspace must be ordered on `compute`.

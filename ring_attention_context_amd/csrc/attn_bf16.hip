@@ -58,10 +58,19 @@
 //     is exact for any reference (o = acc / l, lse = ref + log2 l) as long as
 //     nothing overflows, which those bounds guarantee;
 //   * two row sums: l over the fp32 probabilities gives lse, and l^ over the
-//     bf16-rounded probabilities that enter P V (one v_dot2 per pair) divides
-//     the accumulator, so o is a convex combination of V rows with exactly the
-//     weights the MFMA used: a dominant key contributes its V row with no
-//     rounding error, which matters for peaked rows.
+//     bf16-rounded probabilities that enter P V divides the accumulator, so o
+//     is a convex combination of V rows with exactly the weights the MFMA
+//     used: a dominant key contributes its V row with no rounding error, which
+//     matters for peaked rows. l^ is formed on the matrix pipe by
+//     v_mfma_f32_4x4x4_16b_bf16 against a ones operand (each lane's own four
+//     values summed into element lane % 4 of its accumulator), eight per tile
+//     beside the P V MFMAs: the VALU's v_dot2 executes on the matrix pipe as
+//     well and cannot issue while another wave's MFMAs run, so one v_dot2 per
+//     pair stalled the vector phase of the other wave;
+//   * K / V loads use one buffer descriptor per operand for the workgroup's
+//     whole key range when every offset fits in 31 bits; a tile adds its
+//     offset to each lane's offset, so the loads after the barrier need no
+//     scalar descriptor arithmetic.
 // Workgroups are ordered heaviest query tile first (later positions see more
 // keys under the causal rule); consecutive workgroups cover the KV heads of one
 // token block, so with the round-robin dispatch over the 8 XCDs each XCD's L2
@@ -76,8 +85,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 #define INLINE __attribute__((always_inline))
@@ -177,7 +186,8 @@ __device__ __forceinline__ void barrier_keep_loads() {
 }
 
 // DOC: a document mask is given (a.q_lo); without it the mask code compiles away.
-template <int HW, bool VT, bool DOC>
+// NEAR: the launcher has checked that every offset of the key range fits in 31 bits.
+template <int HW, bool VT, bool DOC, bool NEAR>
 __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // One LDS object per stage and operand (the key positions of a tile sit
   // after its K rows): the compiler then sees that the asynchronous loads into
@@ -249,6 +259,10 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     }
   }
   const int nt = nkeys > kbeg ? static_cast<int>((nkeys - kbeg + BK - 1) / BK) : 0;
+  // Merging a block that no query of the workgroup can see leaves (o, lse) as
+  // they are (its statistics are the merge identity): nothing to load or write.
+  // nt is the same for every wave, so the whole workgroup leaves together.
+  if (a.merge && nt == 0) return;
   // Tiles of this wave, from the same counts (positions are non-decreasing):
   // w_nt tiles hold a key not after its last query; tiles from j_diag on hold
   // a key after its first query, and tiles before j_doc a key before its
@@ -338,7 +352,33 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   }
   // K rows (and key positions) of tile t into K stage `stage`: LOADS_PER_WAVE
   // loads per wave, plus one for wave 0 when causal.
+  // NEAR (every byte offset of the key range fits in 31 bits): one buffer
+  // descriptor per operand covers the workgroup's whole key range and stays in
+  // scalar registers through the loop; tile t adds its offset to each lane's.
+  // Keys past the block still fall outside the descriptor and read as zeros.
+  // Otherwise each tile gets a descriptor of its own.
+  const int64_t rows_left = a.s_kv - kbeg;
+  const __amdgpu_buffer_rsrc_t rk_all = make_rsrc(
+      kg + kv_base + kbeg * kv_row_bytes, rows_left > 0 ? (rows_left - 1) * kv_row_bytes + D * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rv_all =
+      VT ? make_rsrc(vg + vt_base + kbeg * 2, rows_left > 0 ? (D - 1) * vt_stride + rows_left * 2 : 0)
+         : make_rsrc(vg + kv_base + kbeg * kv_row_bytes,
+                     rows_left > 0 ? (rows_left - 1) * kv_row_bytes + D * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rp_all = make_rsrc(a.kv_pos + kbeg, rows_left * 4);
+  const uint32_t k_tile_b = static_cast<uint32_t>(BK * kv_row_bytes);
   auto issue_k = [&](int t, auto stage) INLINE {
+    if constexpr (NEAR) {
+      const uint32_t toff = static_cast<uint32_t>(t) * k_tile_b;
+#pragma unroll
+      for (int i = 0; i < LOADS_PER_WAVE; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk_all, (LDS_AS void *)(k_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16,
+            goff[i] + toff, 0, 0, 0);
+      if (a.causal && wave == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_all, (LDS_AS void *)p_stage(stage), 4,
+                                                 lane * 4 + static_cast<uint32_t>(t) * (BK * 4), 0, 0, 0);
+      return;
+    }
     const int64_t key0 = kbeg + static_cast<int64_t>(t) * BK;
     const int64_t left = a.s_kv - key0;  // rows before the end of the block
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + kv_base + key0 * kv_row_bytes,
@@ -355,6 +395,20 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   };
   // V (or V^T) of tile t into V stage `stage`: LOADS_PER_WAVE loads per wave.
   auto issue_v = [&](int t, auto stage) INLINE {
+    if constexpr (NEAR) {
+#pragma unroll
+      for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+        if constexpr (VT)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rv_all, (LDS_AS void *)(v_stage(stage) + (wave + WAVES * i) * 1024), 16,
+              vgoff[i] + static_cast<uint32_t>(t) * (BK * 2), 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rv_all, (LDS_AS void *)(v_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16,
+              goff[i] + static_cast<uint32_t>(t) * k_tile_b, 0, 0, 0);
+      }
+      return;
+    }
     const int64_t key0 = kbeg + static_cast<int64_t>(t) * BK;
     const int64_t left = a.s_kv - key0;
     // V^T: keys past the block in a d-row read the next d-row's first keys
@@ -382,8 +436,13 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
   float m_run = -INFINITY;  // reference of the exponentials (log2 units)
   float l_run = 0.f;        // this lane's half of the running sum (fp32 probabilities)
-  float lh_run = 0.f;       // ... of the bf16-rounded probabilities fed to P V
   float lt = 0.f;           // this lane's half of the current tile's sum
+  // bf16 sums by 4x4x4 MFMAs (B = ones): lane l's own sum sits in element
+  // l % 4, the other elements are other lanes' sums scaled by this lane's
+  // factors and are never read.
+  f32x4 lh4 = {};
+  const bf16x4 ones4 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f),
+                        static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   float alpha = 1.f;        // rescale factor pending for acc / l_run
   bool done = !wave_has_rows || w_nt == 0;
   bf16x8 pb[4];             // probabilities of the tile whose P V is next
@@ -443,7 +502,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
       l_run *= alpha;
-      lh_run *= alpha;
+      lh4 *= alpha;
       alpha = 1.f;
     }
   };
@@ -506,8 +565,6 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
       }
     };
     bf16x8 op[DIST + 1];
-    const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-    float lh[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < DIST; ++i) op[i] = rd(i);
 #pragma unroll
@@ -520,14 +577,16 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
       } else {
         const int pi = i >> 1, ks = pi / NDB, db = pi % NDB;
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, pb[ks], acc[db], 0, 0, 0);
-        // The sum of the bf16 probabilities (the weights P V just used): one
-        // pair per P V MFMA, on the VALU that the matrix phase leaves idle.
-        lh[db & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ks][2 * db], pb[ks][2 * db + 1]},
-                                                     one, lh[db & 1], false);
+        // The sum of the bf16 probabilities (the weights P V just used), four
+        // per 4x4x4 MFMA, two per k-step.
+        if ((db & 1) == 0)
+          lh4 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+              db == 0 ? bf16x4{pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]}
+                      : bf16x4{pb[ks][4], pb[ks][5], pb[ks][6], pb[ks][7]},
+              ones4, lh4, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    lh_run += lh[0] + lh[1];
   };
 
   // Vector phase for the tile whose (masked) scores are in `s`: probabilities
@@ -547,7 +606,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) acc[i] *= al;
       l_run *= al;
-      lh_run *= al;
+      lh4 *= al;
       m_run = m_new;
       softmax();
       lt_row = pair_sum(lt);
@@ -638,8 +697,12 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
 
   // ---- epilogue: o_b = acc / l^, lse_b = (ref + log2 l) ln 2; optional merge ----
   const float l_tot = pair_sum(l_run);
-  const float lh_tot = pair_sum(lh_run);
+  const int own = lane & 3;
+  const float lh_tot =
+      pair_sum(own == 0 ? lh4[0] : own == 1 ? lh4[1] : own == 2 ? lh4[2] : lh4[3]);
   if (!tok_ok) return;
+  // A row with no visible key in this block merges the identity: unchanged.
+  if (a.merge && !(l_tot > 0.f)) return;
   const float lse_new = l_tot > 0.f ? (m_run + __log2f(l_tot)) * LN2 : -INFINITY;
   const float inv = l_tot > 0.f && lh_tot > 0.f ? 1.f / lh_tot : 0.f;
   const int64_t row = (bi * a.s_q + tok) * a.n_q + h;
@@ -687,10 +750,24 @@ hipError_t launch_hw(const AttnArgs &a, hipStream_t stream) {
   const int64_t blocks = ntb * a.b * a.n_kv * ((a.n_q / a.n_kv) / HW);
   if (blocks == 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  if (a.q_lo)
-    attn_bf16_kernel<HW, VT, true><<<static_cast<unsigned>(blocks), THREADS, 0, stream>>>(a);
-  else
-    attn_bf16_kernel<HW, VT, false><<<static_cast<unsigned>(blocks), THREADS, 0, stream>>>(a);
+  // NEAR: the byte offsets into K, V (or V^T) and the key positions stay below
+  // 2^31 over the whole block plus the three tiles read past its end.
+  const int64_t rows = a.s_kv + 3 * BK;
+  const int64_t kv_row_bytes = static_cast<int64_t>(a.n_kv) * D * 2;
+  const bool near = rows * kv_row_bytes < (int64_t{1} << 31) &&
+                    (D - 1) * a.s_kv * 2 + rows * 2 < (int64_t{1} << 31);
+  const unsigned grid = static_cast<unsigned>(blocks);
+  if (a.q_lo) {
+    if (near)
+      attn_bf16_kernel<HW, VT, true, true><<<grid, THREADS, 0, stream>>>(a);
+    else
+      attn_bf16_kernel<HW, VT, true, false><<<grid, THREADS, 0, stream>>>(a);
+  } else {
+    if (near)
+      attn_bf16_kernel<HW, VT, false, true><<<grid, THREADS, 0, stream>>>(a);
+    else
+      attn_bf16_kernel<HW, VT, false, false><<<grid, THREADS, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

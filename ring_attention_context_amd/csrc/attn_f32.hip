@@ -122,6 +122,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 
   if (!tok_ok) return;
+  // A row with no visible key in this block merges the identity: unchanged.
+  if (a.merge && !(l_run > 0.f)) return;
   const int64_t row = (bi * a.s_q + tok) * a.n_q + h;
   const float lse_new = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;

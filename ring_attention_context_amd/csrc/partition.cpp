@@ -38,3 +38,19 @@ extern "C" ra_status ra_partition(int32_t kind, int64_t S, int32_t N, int32_t ra
       return fail(RA_ERR_INVALID_ARG, "ra_partition: unknown kind %d", kind);
   }
 }
+
+namespace ra {
+
+// Global position of local token a of rank `rank` (the maps above; arguments
+// already validated by the caller).
+int64_t map_position(int32_t kind, int64_t S, int32_t N, int32_t rank, int64_t a) {
+  const int64_t c = S / N;
+  if (kind == RA_PART_CONTIGUOUS) return rank * c + a;
+  if (kind == RA_PART_ZIGZAG) {
+    const int64_t h = c / 2;
+    return a < h ? rank * h + a : (2 * static_cast<int64_t>(N) - 1 - rank) * h + (a - h);
+  }
+  return a * N + rank;
+}
+
+}  // namespace ra

@@ -84,6 +84,15 @@ hipError_t launch_lse_merge(int64_t rows, int32_t d, float *o, float *lse, const
 // Checks shared by every call that takes an ra_ring_desc (all but its flags).
 ra_status check_ring_desc(const ra_ring_desc *r);
 hipError_t launch_positions(int32_t kind, int64_t S, int32_t N, int32_t *pos, hipStream_t stream);
+// Host: global position of local token a of rank `rank` under map `kind`.
+int64_t map_position(int32_t kind, int64_t S, int32_t N, int32_t rank, int64_t a);
+// Host: true when no query of rank `rank` can see any key of rank `src`'s
+// chunk under the causal rule (the maps are increasing, so this compares the
+// chunk's first key with the rank's last query).
+inline bool causally_empty(int32_t kind, int64_t S, int32_t N, int32_t rank, int32_t src) {
+  const int64_t c = S / N;
+  return c > 0 && map_position(kind, S, N, src, 0) > map_position(kind, S, N, rank, c - 1);
+}
 // D = dout . o per row (rows = b * s * n_q, d elements each; esize of dout 2 or 4).
 hipError_t launch_bwd_delta(int64_t rows, int32_t d, int32_t esize, const void *dout,
                             const float *o, float *delta, hipStream_t stream);

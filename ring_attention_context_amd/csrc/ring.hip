@@ -332,6 +332,16 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
       st = fill(step + 1);
       if (st != RA_OK) return st;
     }
+    // A block that no query of this rank can see (causal rule; step 0 is the
+    // rank's own chunk and never empty) adds nothing: its chunk still arrives
+    // (the ring forwards it) but no kernel reads it.
+    if (step > 0 && r->causal && ra::causally_empty(r->kind, r->S, N, rank, src)) {
+      if (step_ev) {
+        st = hip_check(hipEventRecord(step_ev[step + 1], sc), "ra_ring_fwd: step event");
+        if (st != RA_OK) return st;
+      }
+      continue;
+    }
     if (uses_buf(step) && !serialize) {
       st = hip_check(hipStreamWaitEvent(sc, ev->ready[step & 1], 0), "ra_ring_fwd: wait ready");
       if (st != RA_OK) return st;
@@ -360,6 +370,12 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
       st = hip_check(hipEventRecord(step_ev[step + 1], sc), "ra_ring_fwd: step event");
       if (st != RA_OK) return st;
     }
+  }
+  // Order `compute` after the last chunk's arrival also when its step was
+  // skipped (the next call reuses the buffers).
+  if (uses_buf(N - 1) && !serialize) {
+    st = hip_check(hipStreamWaitEvent(sc, ev->ready[(N - 1) & 1], 0), "ra_ring_fwd: join copies");
+    if (st != RA_OK) return st;
   }
   return RA_OK;
 }

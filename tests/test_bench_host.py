@@ -45,3 +45,18 @@ def test_clock_sampler_handles_no_marked_line_and_no_file(tmp_path):
     cs2 = bench.ClockSampler(_props())
     cs2.path = None             # no sysfs file on this machine
     assert cs2.start().stop() is None
+
+
+def test_bench_tile_counts_match_oracle():
+    """The map study's tile-level work (the kernel's 32-query x 64-key tile
+    skip, from the library's maps) equals the oracle's tile_step_work."""
+    import numpy as np
+    import bench
+    from oracle import partition as opart
+    for kind in opart.KINDS:
+        for N in (1, 2, 4, 8):
+            S = 2 * N * 192
+            got = np.array([bench.tile_pairs_per_step(kind, S, N, r) for r in range(N)])
+            assert np.array_equal(got, opart.tile_step_work(kind, S, N, 32, 64)), (kind, N)
+            got_el = np.array([bench.visible_pairs_per_step(kind, S, N, r, True) for r in range(N)])
+            assert np.array_equal(got_el, opart.step_work(kind, S, N)), (kind, N)

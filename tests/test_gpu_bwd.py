@@ -16,7 +16,8 @@ import torch
 
 import ring_attention_context_amd as ra
 import synth
-from gpu_util import rand_inputs, require_gpu, to_device
+from gpu_util import (key_slots, oracle_forward_rows, rand_inputs, require_gpu,
+                      sample_keys, to_device)
 from oracle import attention as oatt
 from oracle import backward as obwd
 from oracle import partition as opart
@@ -186,12 +187,64 @@ def test_ring_bwd_all_ranks_reassemble_sequence_gradients(case):
     grad_close(dv, want[2], f"{case} dv")
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_32k_zigzag", "llama3_70b_128k_zigzag"])
+def test_ring_bwd_32k_every_gradient_kind_against_oracle():
+    """The ring backward of the 32K Llama-3-8B shard at full size, fed the
+    oracle's o and lse of every row (rounded to float32, as the GPU receives
+    them): dq on 32 sampled rows x all heads, and this rank's dK, dV
+    contribution to 64+ sampled keys (chunk and half boundaries among them) x
+    all KV heads, element by element. A key's gradient needs the lse and
+    D = dout . o of every query that sees it, hence the full-row forward."""
+    w = synth.WORKLOADS["llama3_8b_32k_zigzag"]
+    print(f"workload {w.name} backward, oracle o / lse", flush=True)
+    inp = synth.draw(w)
+    q64, k64, v64 = inp.q64, inp.k64, inp.v64
+    ro, rl = oracle_forward_rows(w)
+    o32, lse32 = ro.astype(np.float32), rl.astype(np.float32)
+    q, kc, vc = runner.ring_inputs(inp.q, inp.k, inp.v, w.dtype, w.kind, w.N, "cuda")
+    rng = np.random.default_rng(w.seed + 1000)
+    do_bits = synth.bf16_bits(rng.standard_normal(tuple(q.shape), dtype=np.float32))
+    do64 = synth.bf16_to_f32(do_bits).astype(np.float64)
+    desc, _ = ra.ring_desc(b=w.b, n_q=w.n_q, n_kv=w.n_kv, d=w.d, dtype=ra.RA_BF16,
+                           causal=w.causal, kind=w.kind, S=w.S, N=w.N, rank=w.rank,
+                           scale=w.scale)
+    ws = torch.empty(ra.ra_ring_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    dq = torch.empty(tuple(q.shape), device="cuda")
+    dkc = torch.zeros(tuple(kc.shape), device="cuda")
+    dvc = torch.zeros_like(dkc)
+    ra.ra_ring_bwd(desc, q, kc, vc, torch.from_numpy(o32).cuda(), torch.from_numpy(lse32).cuda(),
+                   runner.host_to_device(do_bits, "bf16", "cuda"), dq, dkc, dvc, ws)
+    torch.cuda.synchronize()
+    dq, dkh, dvh = dq.cpu().numpy(), dkc.cpu().numpy(), dvc.cpu().numpy()
+    del q, kc, vc, dkc, dvc, ws
+    torch.cuda.empty_cache()
+    c = w.c
+    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)
+    rows = synth.sample_rows(c, 32, w.seed, must=[0, c // 2 - 1, c // 2, c - 1])
+    rq = obwd.rows_dq(q64[:, rows], k64, v64, do64[:, rows], q_pos[rows], np.arange(w.S),
+                      w.causal, w.scale)
+    err, m = grad_close(dq[:, rows], rq, "32K dq rows")
+    print(f"  dq rows {len(rows)}: max err {err:.2e} (max |ref| {m:.2e})", flush=True)
+    keys = sample_keys(w.kind, w.S, w.N, 64, w.seed)
+    D = obwd.delta(o32, do64)
+    _, rk, rv = obwd.block_attention_bwd(q64, k64[:, keys], v64[:, keys], do64, lse32, D, q_pos,
+                                         keys, w.causal, w.scale)
+    slots = key_slots(w.kind, w.S, w.N, keys)
+    got_k = np.stack([dkh[j][:, a] for j, a in slots], axis=1)
+    got_v = np.stack([dvh[j][:, a] for j, a in slots], axis=1)
+    for got, want, what in ((got_k, rk, "dk"), (got_v, rv, "dv")):
+        err, m = grad_close(got, want, f"32K {what} keys")
+        print(f"  {what} keys {len(keys)}: max err {err:.2e} (max |ref| {m:.2e})", flush=True)
+
+
+@pytest.mark.parametrize("name", ["llama3_70b_128k_zigzag"])
 def test_full_workload_bwd_sampled_rows_and_invariant(name):
-    """The ring backward at full size in the benchmark's configuration: dq on 32
-    sampled rows x all heads against the oracle (a row's dq depends on that row
-    only), and sum_j dk_j = 0 over the rank's whole contribution to every block
-    (each query's dx sums to zero over its visible keys)."""
+    """The 128K ring backward at full size in the benchmark's configuration
+    (the oracle cannot afford the lse of every row here): dq on 32 sampled
+    rows x all heads against the oracle (a row's dq depends on that row only);
+    sum_j dk_j = 0 over the rank's whole contribution to every block (each
+    query's dx sums to zero over its visible keys); and sum_j dv_j equals the
+    sum of dout over the queries of each KV head's group (each query's
+    probabilities sum to one over its visible keys)."""
     w = synth.WORKLOADS[name]
     print(f"workload {w.name} backward", flush=True)
     inp = synth.draw(w)
@@ -214,11 +267,16 @@ def test_full_workload_bwd_sampled_rows_and_invariant(name):
     dq = dq.cpu().numpy()
     dk = dkc.cpu().numpy().astype(np.float64)
     assert np.isfinite(dq).all() and np.isfinite(dk).all() and torch.isfinite(dvc).all()
+    dv_tot = dvc.sum(dim=(0, 1, 2)).double().cpu().numpy()       # [n_kv, d]
     del call, q, kc, vc, dkc, dvc, ws
     torch.cuda.empty_cache()
     tot = dk.sum(axis=(0, 1, 2))          # [n_kv, d]: every block, batch and key
     mag = np.abs(dk).sum(axis=(0, 1, 2))
     assert np.max(np.abs(tot) / mag) < 1e-3, np.max(np.abs(tot) / mag)
+    do_grp = synth.bf16_to_f32(do_bits).astype(np.float64).sum(axis=(0, 1))     # [n_q, d]
+    want_dv = do_grp.reshape(w.n_kv, w.n_q // w.n_kv, w.d).sum(axis=1)
+    err_dv = float(np.max(np.abs(dv_tot - want_dv)))
+    assert err_dv <= 1e-2 * float(np.max(np.abs(want_dv))), (err_dv, np.max(np.abs(want_dv)))
     c = w.c
     rows = synth.sample_rows(c, 32, w.seed, must=[0, c // 2 - 1, c // 2, c - 1])
     q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)
@@ -227,7 +285,8 @@ def test_full_workload_bwd_sampled_rows_and_invariant(name):
                       np.arange(w.S), w.causal, w.scale)
     err, m = grad_close(dq[:, rows], rq, f"{name} dq rows")
     print(f"  dq rows {len(rows)}: max err {err:.2e} (max |ref| {m:.2e}); "
-          f"max |sum dk| / sum |dk| {np.max(np.abs(tot) / mag):.2e}", flush=True)
+          f"max |sum dk| / sum |dk| {np.max(np.abs(tot) / mag):.2e}; "
+          f"max |sum dv - sum dout| {err_dv:.2e} (max {np.max(np.abs(want_dv)):.2e})", flush=True)
 
 
 def test_ring_batched_forward_and_backward():
@@ -279,3 +338,4 @@ def test_ring_batched_forward_and_backward():
         dv[:, pj] = dvh[j]
     grad_close(dk, want[1], "b2 dk")
     grad_close(dv, want[2], "b2 dv")
+

@@ -16,7 +16,9 @@ import torch
 
 import ring_attention_context_amd as ra
 import synth
-from gpu_util import compare, rand_inputs, require_gpu, to_device
+from gpu_util import (compare, key_slots, oracle_rows_threaded, rand_inputs, require_gpu,
+                      sample_keys, to_device)
+from oracle import backward as obwd
 from oracle import documents as odoc
 from oracle import partition as opart
 from ring_attention_context_amd import runner
@@ -166,9 +168,10 @@ def test_ring_with_doc_mask_matches_oracle(case):
 
 
 @pytest.mark.parametrize("name", sorted(synth.ALLGATHER_WORKLOADS))
-def test_allgather_workload_sampled_rows(name):
-    """Full-size all-gather run (every row on the GPU); 128 sampled rows x all
-    heads compared element by element with the oracle."""
+def test_allgather_workload_rows(name):
+    """Full-size all-gather run (every row on the GPU): the 32K shard compared
+    on every row x all heads, the 128K shard on 256 sampled rows (document
+    starts, chunk boundaries, seeded rows) x all heads, element by element."""
     w = synth.ALLGATHER_WORKLOADS[name]
     print(f"workload {w.name}", flush=True)
     inp = synth.draw(w)
@@ -187,10 +190,12 @@ def test_allgather_workload_sampled_rows(name):
     ids = odoc.doc_ids_from_lengths(lengths)
     # rows at document starts inside the shard, the chunk boundaries, and seeded rows
     firsts = np.searchsorted(q_pos, np.concatenate([[0], np.cumsum(lengths)[:-1]]))
-    rows = synth.sample_rows(c, 128, w.seed,
-                             must=[0, 1, c // 2 - 1, c // 2, c - 1, *firsts[:24].tolist()])
-    ro, rl = odoc.rows_attention_docs(inp.q64[:, rows], inp.k64, inp.v64, q_pos[rows], ids,
-                                      True, w.scale)
+    rows = np.arange(c) if w.S <= 32768 else synth.sample_rows(
+        c, 256, w.seed, must=[0, 1, c // 2 - 1, c // 2, c - 1, *firsts[:24].tolist()])
+    k64, v64 = inp.k64, inp.v64
+    ro, rl = oracle_rows_threaded(
+        lambda qr, qp: odoc.rows_attention_docs(qr, k64, v64, qp, ids, True, w.scale), rows,
+        inp.q64, q_pos)
     do, dl = compare(o[:, rows], lse[:, rows], ro, rl, w.dtype, w.name)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     print(f"  rows {len(rows)} max|dO| {do:.2e} max|dlse| {dl:.2e}", flush=True)
@@ -341,47 +346,77 @@ def test_ring_bwd_with_doc_mask_reassembles_sequence_gradients():
         print(f"  {name}: max err {err:.2e} (max |ref| {mag:.2e})", flush=True)
 
 
-def test_allgather_bwd_workload_sampled_rows_and_invariant():
-    """Full-size all-gather backward (32K, 14 documents): dq on 64 sampled rows
-    x all heads against the oracle (dq of a row depends on that row only), and
-    the invariant sum_j dk_j = 0 (each query's dx sums to zero over its keys)
-    over the rank's whole contribution."""
+def test_allgather_bwd_workload_every_gradient_kind_against_oracle():
+    """Full-size all-gather backward (32K, 14 documents), fed the oracle's
+    document-masked o and lse of every row (rounded to float32, as the GPU
+    receives them): dq on 64 sampled rows x all heads, this rank's dK, dV
+    contribution to 64+ sampled keys x all KV heads (a key's gradient comes
+    from the queries of its own document only, so the oracle's block backward
+    runs on those queries with the causal rule), element by element; and the
+    invariant sum_j dk_j = 0 over the rank's whole contribution."""
     w = synth.ALLGATHER_WORKLOADS["llama3_8b_32k_allgather_docs"]
-    print(f"workload {w.name} backward", flush=True)
+    print(f"workload {w.name} backward, oracle o / lse", flush=True)
     inp = synth.draw(w)
+    q64, k64, v64 = inp.q64, inp.k64, inp.v64
     lengths = synth.doc_lengths(w.S, w.seed)
+    ids = odoc.doc_ids_from_lengths(lengths)
+    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)
+    ro, rl = oracle_rows_threaded(
+        lambda qr, qp: odoc.rows_attention_docs(qr, k64, v64, qp, ids, True, w.scale),
+        np.arange(w.c), q64, q_pos)
+    o32, lse32 = ro.astype(np.float32), rl.astype(np.float32)
     q, kc, vc = runner.ring_inputs(inp.q, inp.k, inp.v, w.dtype, w.kind, w.N, "cuda")
     ds = torch.from_numpy(runner.doc_start_positions(lengths)).cuda()
-    call = runner.AllGatherCall(q, kc, vc, kind=w.kind, S=w.S, N=w.N, rank=w.rank, causal=True,
-                                scale=w.scale, doc_start=ds)
-    o, lse = call()
     rng = np.random.default_rng(w.seed + 1000)
     do_bits = synth.bf16_bits(rng.standard_normal(tuple(q.shape), dtype=np.float32))
+    do64 = synth.bf16_to_f32(do_bits).astype(np.float64)
     desc, _ = ra.ring_desc(b=1, n_q=w.n_q, n_kv=w.n_kv, d=w.d, dtype=ra.RA_BF16, causal=True,
                            kind=w.kind, S=w.S, N=w.N, rank=w.rank, scale=w.scale, doc_start=ds)
     ws = torch.empty(ra.ra_allgather_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     dq = torch.empty(tuple(q.shape), device="cuda")
     dkc = torch.zeros(tuple(kc.shape), device="cuda")
     dvc = torch.zeros_like(dkc)
-    ra.ra_allgather_bwd(desc, q, kc, vc, o, lse, to_device(do_bits, "bf16"), dq, dkc, dvc, ws)
+    ra.ra_allgather_bwd(desc, q, kc, vc, torch.from_numpy(o32).cuda(),
+                        torch.from_numpy(lse32).cuda(), to_device(do_bits, "bf16"), dq, dkc, dvc,
+                        ws)
     torch.cuda.synchronize()
-    dq, dk = dq.cpu().numpy(), dkc.cpu().numpy().astype(np.float64)
-    assert np.isfinite(dq).all() and np.isfinite(dk).all() and torch.isfinite(dvc).all()
-    # invariant: sum over every key of dk (per batch, kv head and channel) is 0
-    tot = dk.sum(axis=(0, 2))
-    mag = np.abs(dk).sum(axis=(0, 2))
+    dq, dkh, dvh = dq.cpu().numpy(), dkc.cpu().numpy(), dvc.cpu().numpy()
+    del q, kc, vc, dkc, dvc, ws
+    torch.cuda.empty_cache()
+    assert np.isfinite(dq).all() and np.isfinite(dkh).all() and np.isfinite(dvh).all()
+    dk64 = dkh.astype(np.float64)
+    tot = dk64.sum(axis=(0, 2))
+    mag = np.abs(dk64).sum(axis=(0, 2))
     assert np.max(np.abs(tot) / mag) < 1e-3, np.max(np.abs(tot) / mag)
     c = w.c
     rows = synth.sample_rows(c, 64, w.seed, must=[0, c // 2, c - 1])
-    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)
-    ids = odoc.doc_ids_from_lengths(lengths)
-    do64 = synth.bf16_to_f32(do_bits).astype(np.float64)
     vis = odoc.visible_docs(q_pos[rows], np.arange(w.S), ids, True)
-    rq, _, _ = odoc.masked_attention_bwd(inp.q64[:, rows], inp.k64, inp.v64, do64[:, rows], vis,
-                                         w.scale)
+    rq, _, _ = odoc.masked_attention_bwd(q64[:, rows], k64, v64, do64[:, rows], vis, w.scale)
     err, m = _grad_close(dq[:, rows], rq, "dq rows")
     print(f"  dq rows {len(rows)}: max err {err:.2e} (max |ref| {m:.2e}); "
           f"max |sum dk| / sum |dk| {np.max(np.abs(tot) / mag):.2e}", flush=True)
+    keys = sample_keys(w.kind, w.S, w.N, 64, w.seed)
+    starts = np.cumsum(np.concatenate([[0], lengths]))
+    keys = np.unique(np.concatenate([keys, starts[1:-1], starts[1:-1] - 1]))   # document edges
+    D = obwd.delta(o32, do64)
+    rk = np.zeros((1, len(keys), w.n_kv, w.d))
+    rv = np.zeros_like(rk)
+    for doc in np.unique(ids[keys]):
+        kk = np.nonzero(ids[keys] == doc)[0]
+        qq = np.nonzero(ids[q_pos] == doc)[0]
+        if qq.size == 0:
+            continue
+        _, dk_d, dv_d = obwd.block_attention_bwd(q64[:, qq], k64[:, keys[kk]], v64[:, keys[kk]],
+                                                 do64[:, qq], lse32[:, qq], D[:, qq], q_pos[qq],
+                                                 keys[kk], True, w.scale)
+        rk[:, kk] = dk_d
+        rv[:, kk] = dv_d
+    slots = key_slots(w.kind, w.S, w.N, keys)
+    got_k = np.stack([dkh[j][:, a] for j, a in slots], axis=1)
+    got_v = np.stack([dvh[j][:, a] for j, a in slots], axis=1)
+    for got, want, what in ((got_k, rk, "dk"), (got_v, rv, "dv")):
+        err, m = _grad_close(got, want, f"{what} keys")
+        print(f"  {what} keys {len(keys)}: max err {err:.2e} (max |ref| {m:.2e})", flush=True)
 
 
 def test_allgather_batched_matches_oracle():

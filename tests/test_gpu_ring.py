@@ -2,7 +2,8 @@
 
 Small rings are checked on every output; the five measured workloads run at
 full size in the same launch configuration the benchmark times and are
-checked on sampled query rows (all heads, every element of o and lse)."""
+checked on every row (the 32K shard) or 256 sampled query rows (all heads,
+every element of o and lse)."""
 
 import math
 
@@ -12,7 +13,7 @@ import torch
 
 import ring_attention_context_amd as ra
 import synth
-from gpu_util import compare, require_gpu
+from gpu_util import compare, oracle_forward_rows, require_gpu
 from oracle import attention as oatt
 from oracle import partition as opart
 from ring_attention_context_amd import runner
@@ -167,9 +168,12 @@ FULL = [
 
 
 @pytest.mark.parametrize("name,over", FULL, ids=lambda x: str(x))
-def test_full_workload_sampled_rows(name, over):
-    """Full-size run (all rows computed on the GPU); 128 sampled rows x all heads
-    compared element by element with the oracle."""
+def test_full_workload_rows(name, over):
+    """Full-size run (all rows computed on the GPU) in the benchmark's
+    configuration. The 32K Llama-3-8B shard is compared on every row x every
+    head; the larger workloads on 256 sampled rows (the zig-zag half boundaries
+    and diagonals, 16 rows at each end, the rest seeded uniform) x all heads,
+    every element of o and lse."""
     w = synth.WORKLOADS[name].with_(**over)
     print(f"workload {w.name} {over}", flush=True)
     inp = synth.draw(w)
@@ -178,11 +182,39 @@ def test_full_workload_sampled_rows(name, over):
     del q, kc, vc
     torch.cuda.empty_cache()
     c = w.c
-    rows = synth.sample_rows(c, 128, w.seed,
-                             must=[0, 1, c // 2 - 1, c // 2, c // 2 + 1, c - 1])
-    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)
-    ro, rl = oatt.rows_attention(inp.q64[:, rows], inp.k64, inp.v64, q_pos[rows], w.causal,
-                                 w.scale)
+    every_row = name == "llama3_8b_32k_zigzag" and not over
+    rows = np.arange(c) if every_row else synth.sample_rows(
+        c, 256, w.seed, must=[0, 1, c // 2 - 1, c // 2, c // 2 + 1, c - 1])
+    ro, rl = oracle_forward_rows(w, None if every_row else rows)
     do, dl = compare(o[:, rows], lse[:, rows], ro, rl, w.dtype, w.name)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     print(f"  rows {len(rows)} max|dO| {do:.2e} max|dlse| {dl:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("kind", opart.KINDS)
+def test_device_position_maps_bit_exact(kind):
+    """The position maps the ring writes into its workspace (the first S int32:
+    rank j's c positions at [j*c, (j+1)*c)) equal the oracle's maps bit for
+    bit, for N in {1, 2, 3, 4, 8, 32}; the backward's workspace the same."""
+    for N in (1, 2, 3, 4, 8, 32):
+        S = 2 * N * 24
+        rank = N // 2
+        print(f"positions {kind} N={N} S={S}", flush=True)
+        w = synth.Workload("pos", 1, S, N, kind, 1, 1, 128, "bf16", 1.0, True, seed=N, rank=rank)
+        inp = synth.draw(w)
+        q, kc, vc = device_inputs(w, inp)
+        call, _, _ = run_ring(w, q, kc, vc, poison=True)
+        got = call.workspace[:S * 4].view(torch.int32).cpu().numpy().reshape(N, S // N)
+        for j in range(N):
+            assert np.array_equal(got[j], opart.partition_map(kind, S, N, j)), (kind, N, j)
+        desc, _ = ra.ring_desc(b=1, n_q=1, n_kv=1, d=128, dtype=ra.RA_BF16, causal=True, kind=kind,
+                               S=S, N=N, rank=rank)
+        ws = torch.full((ra.ra_ring_bwd_workspace_bytes(desc),), 0xFF, dtype=torch.uint8,
+                        device="cuda")
+        dq = torch.empty(tuple(q.shape), device="cuda")
+        dkc = torch.zeros(tuple(kc.shape), device="cuda")
+        ra.ra_ring_bwd(desc, q, kc, vc, call.o, call.lse, q, dq, dkc, torch.zeros_like(dkc), ws)
+        torch.cuda.synchronize()
+        got = ws[:S * 4].view(torch.int32).cpu().numpy().reshape(N, S // N)
+        for j in range(N):
+            assert np.array_equal(got[j], opart.partition_map(kind, S, N, j)), ("bwd", kind, N, j)
