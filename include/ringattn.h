@@ -274,30 +274,43 @@ ra_status ra_block_attn_bwd(const ra_attn_desc *desc, const void *q, const void 
                             const void *v, const void *dout, const float *lse,
                             const float *delta, float *dq, float *dk, float *dv, void *stream);
 
-/* Workspace bytes ra_ring_bwd needs: positions (S int32), D (b*c*n_q floats)
- * and the queries' document starts (c int32). */
+/* Workspace bytes ra_ring_bwd needs: positions (S int32), D (b*c*n_q floats),
+ * the queries' document starts (c int32) and, for N > 1, the double buffer of
+ * the travelling block: two halves of K, V (bf16) and dK, dV (float32), one
+ * chunk each. */
 ra_status ra_ring_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
 
 /*
- * ra_ring_bwd -- the ring backward for rank `rank`, replayed on one GPU.
- * desc: as for ra_ring_fwd (bf16, d = 128; flags 0 or RA_RING_SERIALIZE,
- * which changes nothing here: one stream; doc_start optional).
+ * ra_ring_bwd -- the ring backward for rank `rank`, replayed on one GPU
+ * ("Context Parallelism and Ring Attention" §3 backward paragraph and §4:
+ * the accumulated dK, dV of a block travel around the ring with its K, V).
+ * desc: as for ra_ring_fwd (bf16, d = 128; flags 0 or RA_RING_SERIALIZE;
+ * doc_start optional).
  * q, dout: device [b, c, n_q, d] bf16, the rank's tokens in its local order;
  * o, lse: device float32 [b, c, n_q, d] and [b, c, n_q], the rank's forward
  * outputs (global o and lse); k_chunks, v_chunks: device [N, b, c, n_kv, d]
  * bf16 as for ra_ring_fwd.
  * dq: device float32 [b, c, n_q, d], overwritten with the rank's dQ.
- * dk_chunks, dv_chunks: device float32 [N, b, c, n_kv, d]; this rank's
- * contribution to block j's dK, dV is ADDED to slot j. These slots stand for
- * the gradient buffers that travel the ring with each block: calling every
- * rank on the same slots sums the sequence's dK, dV.
- * Step r works on block (rank - r) mod N, read in place; N+1 step events
- * (optional) are recorded before step 0 and after each step.
+ * dk_chunks, dv_chunks: device float32 [N, b, c, n_kv, d], slot j holding
+ * block j's dK, dV accumulated so far; this rank's contribution is ADDED:
+ * calling every rank on the same slots sums the sequence's dK, dV.
+ * Step r works on block (rank - r) mod N. With N > 1 the block's K, V and
+ * slot dK, dV are received into half r % 2 of the workspace's double buffer
+ * on `copy`, the step's two kernels run on `compute` against that half, and
+ * the updated dK, dV are sent back to the slot on `copy` (on `compute` with
+ * RA_RING_SERIALIZE or copy == compute); the result equals adding to the
+ * slots in place. A causal step whose block no query of the rank can see
+ * launches no kernel (its dK, dV pass through unchanged). After the call
+ * the workspace's first S int32 hold every rank's position map, as for
+ * ra_ring_fwd. N+1 step events (optional) are recorded on `compute` before
+ * step 0 and after each step's kernels.
+ * On return all work is enqueued and `compute` is ordered after every copy;
+ * `copy` first waits for the work already enqueued on `compute`.
  */
 ra_status ra_ring_bwd(const ra_ring_desc *desc, const void *q, const void *k_chunks,
                       const void *v_chunks, const float *o, const float *lse, const void *dout,
                       float *dq, float *dk_chunks, float *dv_chunks, void *workspace,
-                      size_t workspace_bytes, void *stream);
+                      size_t workspace_bytes, void *compute, void *copy);
 
 /* Workspace bytes ra_allgather_bwd needs for *desc (same validation as the call). */
 ra_status ra_allgather_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);

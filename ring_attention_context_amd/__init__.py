@@ -42,4 +42,5 @@ from ._lib import (  # noqa: F401
     ra_status_str,
     ra_v_transpose,
     ring_desc,
+    side_stream,
 )

@@ -79,7 +79,7 @@ def load_library(path=None):
     lib.ra_ring_bwd_workspace_bytes.argtypes = [ctypes.POINTER(RingDesc),
                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.ra_ring_bwd.argtypes = [ctypes.POINTER(RingDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                ctypes.c_size_t, vp]
+                                ctypes.c_size_t, vp, vp]
     lib.ra_allgather_workspace_bytes.argtypes = [ctypes.POINTER(RingDesc),
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.ra_allgather_fwd.argtypes = [ctypes.POINTER(RingDesc), vp, vp, vp, vp, vp, vp,
@@ -259,15 +259,32 @@ def ra_ring_bwd_workspace_bytes(desc):
     return out.value
 
 
+_SIDE_STREAMS = {}
+
+
+def side_stream(device=None):
+    """A second stream of the device (default priority), kept for the process:
+    the default copy stream of the ring backward."""
+    import torch
+    dev = torch.cuda.current_device() if device is None else torch.device(device).index
+    if dev not in _SIDE_STREAMS:
+        _SIDE_STREAMS[dev] = torch.cuda.Stream(device=dev)
+    return _SIDE_STREAMS[dev]
+
+
 def ra_ring_bwd(desc, q, k_chunks, v_chunks, o, lse, dout, dq, dk_chunks, dv_chunks, workspace,
-                stream=None):
-    """Ring backward of one rank; see ringattn.h. dk_chunks / dv_chunks are added to."""
+                stream=None, copy=None):
+    """Ring backward of one rank; see ringattn.h. dk_chunks / dv_chunks are added to.
+    ``copy``: the stream of the travelling block's transfers (default: a side
+    stream of q's device; pass ``stream`` itself to serialize)."""
     _need_contiguous(q, k_chunks, v_chunks, o, lse, dout, dq, dk_chunks, dv_chunks, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if copy is None:
+        copy = side_stream(q.device)
     _check(load_library().ra_ring_bwd(ctypes.byref(desc), _ptr(q), _ptr(k_chunks),
                                       _ptr(v_chunks), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                       _ptr(dk_chunks), _ptr(dv_chunks), _ptr(workspace),
-                                      ws_bytes, _stream(stream)))
+                                      ws_bytes, _stream(stream), _stream(copy)))
 
 
 def ra_allgather_workspace_bytes(desc):

@@ -384,11 +384,19 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
 //
 // The ring backward of "Context Parallelism and Ring Attention" §3 (backward
 // paragraph) and §4 for one rank: D = dout . o once; at step r the rank holds
-// the K/V block of rank (rank - r) mod N and adds that block's contribution
-// to its dQ and to the block's dK, dV. On a ring the accumulated dK, dV of a
-// block travel with it; here the caller's per-block output slots play that
-// role (this rank's contribution is added to whatever they hold), and the
-// blocks are read in place on one stream.
+// the K/V block of rank (rank - r) mod N together with that block's
+// accumulated dK, dV (on a ring they travel with it, §4 "can communication be
+// hidden"), adds the block's contribution to its dQ and to the travelling
+// dK, dV, and passes the block on. Replayed on one GPU, the caller's per-block
+// slots hold the accumulated dK, dV; for N > 1, step r "receives" block src's
+// K, V and accumulated dK, dV into half (r & 1) of a double buffer and, once
+// both kernels of the step have run on that half, "sends" the updated dK, dV
+// back to the slot. Receives and sends run on the copy stream, ordered by
+// events against the compute stream:
+//   receive(r)  into half r&1 follows send(r-2) out of it (same stream);
+//   send(r)     waits for step r's kernels;
+//   step r      waits for receive(r).
+// The result equals adding this rank's contribution to the slots in place.
 
 namespace ra {
 namespace {
@@ -397,6 +405,9 @@ struct BwdPlan {
   int64_t c = 0;
   size_t chunk_elems = 0;  // one K (or V) chunk [b, c, n_kv, d]
   size_t pos_off = 0, delta_off = 0, qlo_off = 0, total = 0;
+  size_t buf_off[2] = {0, 0};  // per half: K, V (bf16), dK, dV (fp32)
+  size_t kb = 0, vb = 0, dkb = 0, dvb = 0;  // offsets inside a half
+  bool ring = false;       // N > 1: the transfer is replayed through the buffer
 };
 
 ra_status make_bwd_plan(const ra_ring_desc *r, BwdPlan *p) {
@@ -412,6 +423,7 @@ ra_status make_bwd_plan(const ra_ring_desc *r, BwdPlan *p) {
     return fail(RA_ERR_UNSUPPORTED, "ring bwd: bf16 with d = 128 only");
   p->c = fp.c;
   p->chunk_elems = static_cast<size_t>(r->b) * fp.c * r->n_kv * r->d;
+  p->ring = r->N > 1;
   size_t off = 0;
   p->pos_off = off;
   off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
@@ -419,7 +431,41 @@ ra_status make_bwd_plan(const ra_ring_desc *r, BwdPlan *p) {
   off += align_up(static_cast<size_t>(r->b) * fp.c * r->n_q * sizeof(float));
   p->qlo_off = off;   // the rank's queries' document starts
   off += align_up(static_cast<size_t>(fp.c) * sizeof(int32_t));
+  if (p->ring) {
+    p->kb = 0;
+    p->vb = align_up(p->chunk_elems * 2);
+    p->dkb = 2 * align_up(p->chunk_elems * 2);
+    p->dvb = p->dkb + align_up(p->chunk_elems * 4);
+    const size_t half = p->dvb + align_up(p->chunk_elems * 4);
+    for (int i = 0; i < 2; ++i) {
+      p->buf_off[i] = off;
+      off += half;
+    }
+  }
   p->total = off;
+  return RA_OK;
+}
+
+struct BwdEvents {
+  hipEvent_t start, ready[2], done[2], sent;
+};
+
+ra_status bwd_events(BwdEvents **out) {
+  thread_local std::unordered_map<int, BwdEvents> cache;
+  int dev = 0;
+  ra_status st = hip_check(hipGetDevice(&dev), "ring bwd: hipGetDevice");
+  if (st != RA_OK) return st;
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    BwdEvents ev{};
+    hipEvent_t *all[6] = {&ev.start, &ev.ready[0], &ev.ready[1], &ev.done[0], &ev.done[1], &ev.sent};
+    for (hipEvent_t *e : all) {
+      st = hip_check(hipEventCreateWithFlags(e, hipEventDisableTiming), "ring bwd: hipEventCreate");
+      if (st != RA_OK) return st;
+    }
+    it = cache.emplace(dev, ev).first;
+  }
+  *out = &it->second;
   return RA_OK;
 }
 
@@ -439,14 +485,17 @@ extern "C" ra_status ra_ring_bwd_workspace_bytes(const ra_ring_desc *desc, size_
 extern "C" ra_status ra_ring_bwd(const ra_ring_desc *r, const void *q, const void *k_chunks,
                                  const void *v_chunks, const float *o, const float *lse,
                                  const void *dout, float *dq, float *dk_chunks, float *dv_chunks,
-                                 void *workspace, size_t workspace_bytes, void *stream) {
+                                 void *workspace, size_t workspace_bytes, void *compute,
+                                 void *copy) {
   using ra::fail;
   using ra::hip_check;
   ra::clear_error();
   ra::BwdPlan P;
   ra_status st = ra::make_bwd_plan(r, &P);
   if (st != RA_OK) return st;
-  hipStream_t sc = static_cast<hipStream_t>(stream);
+  hipStream_t sc = static_cast<hipStream_t>(compute);
+  hipStream_t sp = static_cast<hipStream_t>(copy);
+  const bool serialize = (r->flags & RA_RING_SERIALIZE) != 0 || sp == sc;
   hipEvent_t *step_ev = reinterpret_cast<hipEvent_t *>(r->step_events);
   const bool empty = r->b == 0 || P.c == 0;
   if (empty) {
@@ -484,8 +533,20 @@ extern "C" ra_status ra_ring_bwd(const ra_ring_desc *r, const void *q, const voi
     st = hip_check(ra::launch_gather_i32(r->doc_start, pos + static_cast<int64_t>(r->rank) * P.c,
                                          qlo, P.c, sc),
                    "ra_ring_bwd: document starts");
-  if (st == RA_OK && step_ev) st = hip_check(hipEventRecord(step_ev[0], sc), "ra_ring_bwd: step event");
   if (st != RA_OK) return st;
+
+  ra::BwdEvents *ev = nullptr;
+  if (P.ring && !serialize) {
+    st = ra::bwd_events(&ev);
+    // The copy stream reads slots the caller may have just written on `compute`.
+    if (st == RA_OK) st = hip_check(hipEventRecord(ev->start, sc), "ra_ring_bwd: event record");
+    if (st == RA_OK) st = hip_check(hipStreamWaitEvent(sp, ev->start, 0), "ra_ring_bwd: wait");
+    if (st != RA_OK) return st;
+  }
+  if (step_ev) {
+    st = hip_check(hipEventRecord(step_ev[0], sc), "ra_ring_bwd: step event");
+    if (st != RA_OK) return st;
+  }
 
   ra::BwdArgs a{};
   a.q = q;
@@ -505,18 +566,81 @@ extern "C" ra_status ra_ring_bwd(const ra_ring_desc *r, const void *q, const voi
   a.q_lo = r->doc_start ? qlo : nullptr;
   const unsigned char *kc = static_cast<const unsigned char *>(k_chunks);
   const unsigned char *vc = static_cast<const unsigned char *>(v_chunks);
-  const int N = r->N;
-  for (int step = 0; step < N; ++step) {
-    const int src = ((r->rank - step) % N + N) % N;
-    a.k = kc + static_cast<size_t>(src) * P.chunk_elems * 2;
-    a.v = vc + static_cast<size_t>(src) * P.chunk_elems * 2;
-    a.kv_pos = pos + static_cast<int64_t>(src) * P.c;
-    a.dk = dk_chunks + static_cast<size_t>(src) * P.chunk_elems;
-    a.dv = dv_chunks + static_cast<size_t>(src) * P.chunk_elems;
-    st = hip_check(ra::launch_attn_bwd_bf16(a, sc), "ra_ring_bwd: backward launch");
-    if (st == RA_OK && step_ev)
-      st = hip_check(hipEventRecord(step_ev[step + 1], sc), "ra_ring_bwd: step event");
+  const int N = r->N, rank = r->rank;
+  const size_t EB = P.chunk_elems * 2, FB = P.chunk_elems * 4;  // bf16 / fp32 chunk bytes
+  auto src_of = [&](int step) { return ((rank - step) % N + N) % N; };
+  auto half = [&](int step) { return ws + P.buf_off[step & 1]; };
+  hipStream_t cs = serialize ? sc : sp;
+  auto copy_bytes = [&](void *dst, const void *from, size_t n, const char *what) {
+    return hip_check(hipMemcpyAsync(dst, from, n, hipMemcpyDeviceToDevice, cs), what);
+  };
+  // Receive block `step`'s K, V and accumulated dK, dV into its buffer half.
+  auto receive = [&](int step) -> ra_status {
+    const size_t j = static_cast<size_t>(src_of(step));
+    unsigned char *h = half(step);
+    ra_status s2 = copy_bytes(h + P.kb, kc + j * EB, EB, "ra_ring_bwd: receive K");
+    if (s2 == RA_OK) s2 = copy_bytes(h + P.vb, vc + j * EB, EB, "ra_ring_bwd: receive V");
+    if (s2 == RA_OK)
+      s2 = copy_bytes(h + P.dkb, dk_chunks + j * P.chunk_elems, FB, "ra_ring_bwd: receive dK");
+    if (s2 == RA_OK)
+      s2 = copy_bytes(h + P.dvb, dv_chunks + j * P.chunk_elems, FB, "ra_ring_bwd: receive dV");
+    if (s2 == RA_OK && !serialize)
+      s2 = hip_check(hipEventRecord(ev->ready[step & 1], sp), "ra_ring_bwd: record ready");
+    return s2;
+  };
+  // Send block `step`'s updated dK, dV on (back to its slot) once its kernels ran.
+  auto send = [&](int step) -> ra_status {
+    const size_t j = static_cast<size_t>(src_of(step));
+    unsigned char *h = half(step);
+    ra_status s2 = RA_OK;
+    if (!serialize) s2 = hip_check(hipStreamWaitEvent(sp, ev->done[step & 1], 0), "ra_ring_bwd: wait done");
+    if (s2 == RA_OK)
+      s2 = copy_bytes(dk_chunks + j * P.chunk_elems, h + P.dkb, FB, "ra_ring_bwd: send dK");
+    if (s2 == RA_OK)
+      s2 = copy_bytes(dv_chunks + j * P.chunk_elems, h + P.dvb, FB, "ra_ring_bwd: send dV");
+    return s2;
+  };
+
+  if (P.ring) {
+    st = receive(0);
+    if (st == RA_OK) st = receive(1);
     if (st != RA_OK) return st;
   }
-  return RA_OK;
+  for (int step = 0; step < N; ++step) {
+    const int src = src_of(step);
+    // A block that no query of this rank can see (causal rule; step 0, the
+    // rank's own chunk, never is) gets no contribution: no kernel runs, and
+    // its dK, dV pass through unchanged.
+    const bool skip = step > 0 && r->causal && ra::causally_empty(r->kind, r->S, N, rank, src);
+    if (P.ring) {
+      unsigned char *h = half(step);
+      a.k = h + P.kb;
+      a.v = h + P.vb;
+      a.dk = reinterpret_cast<float *>(h + P.dkb);
+      a.dv = reinterpret_cast<float *>(h + P.dvb);
+      if (!serialize)
+        st = hip_check(hipStreamWaitEvent(sc, ev->ready[step & 1], 0), "ra_ring_bwd: wait ready");
+    } else {
+      a.k = kc + static_cast<size_t>(src) * EB;
+      a.v = vc + static_cast<size_t>(src) * EB;
+      a.dk = dk_chunks + static_cast<size_t>(src) * P.chunk_elems;
+      a.dv = dv_chunks + static_cast<size_t>(src) * P.chunk_elems;
+    }
+    a.kv_pos = pos + static_cast<int64_t>(src) * P.c;
+    if (st == RA_OK && !skip)
+      st = hip_check(ra::launch_attn_bwd_bf16(a, sc), "ra_ring_bwd: backward launch");
+    if (st == RA_OK && P.ring && !serialize)
+      st = hip_check(hipEventRecord(ev->done[step & 1], sc), "ra_ring_bwd: record done");
+    if (st == RA_OK && step_ev)
+      st = hip_check(hipEventRecord(step_ev[step + 1], sc), "ra_ring_bwd: step event");
+    if (st == RA_OK && P.ring) st = send(step);
+    if (st == RA_OK && P.ring && step + 2 < N) st = receive(step + 2);
+    if (st != RA_OK) return st;
+  }
+  if (P.ring && !serialize) {
+    // `compute` is ordered after the last send.
+    st = hip_check(hipEventRecord(ev->sent, sp), "ra_ring_bwd: record sent");
+    if (st == RA_OK) st = hip_check(hipStreamWaitEvent(sc, ev->sent, 0), "ra_ring_bwd: join copies");
+  }
+  return st;
 }

@@ -237,8 +237,16 @@ def test_backward_argument_errors():
         ra.ra_ring_bwd_workspace_bytes(_ring(flags=ra.RA_RING_UNFUSED_MERGE))
     def align(x):
         return (x + 255) // 256 * 256
-    assert ra.ra_ring_bwd_workspace_bytes(_ring()) == (align(1024 * 4) + align(256 * 8 * 4)
-                                                       + align(256 * 4))
+    # positions, D, document starts, and for N > 1 two halves of the travelling
+    # block: K, V (bf16) and dK, dV (float32), one [b, c, n_kv, d] chunk each
+    r = _ring()
+    chunk = r.b * (r.S // r.N) * r.n_kv * r.d
+    half = 2 * align(chunk * 2) + 2 * align(chunk * 4)
+    assert ra.ra_ring_bwd_workspace_bytes(r) == (align(1024 * 4) + align(256 * 8 * 4)
+                                                 + align(256 * 4) + 2 * half)
+    r1 = _ring(N=1, S=256, rank=0)
+    assert ra.ra_ring_bwd_workspace_bytes(r1) == (align(256 * 4) + align(256 * 8 * 4)
+                                                  + align(256 * 4))
 
 
 def test_document_mask_argument_errors():
@@ -308,3 +316,4 @@ def test_allgather_bwd_workspace_and_errors():
     args[6] = None       # dq
     st = lib.ra_allgather_bwd(ctypes.byref(desc), *args, FAKE, need, None)
     assert st == ra.RA_ERR_INVALID_ARG
+

@@ -339,3 +339,46 @@ def test_ring_batched_forward_and_backward():
     grad_close(dk, want[1], "b2 dk")
     grad_close(dv, want[2], "b2 dv")
 
+
+def test_ring_bwd_transfer_overlap_equals_serialized_bitwise():
+    """The travelling block's receives and sends on a second stream (overlapped
+    with the kernels) against the same copies on the compute stream: any
+    difference would be a race between a transfer and a kernel. Slots start
+    from nonzero "earlier ranks'" values and the workspace is NaN-poisoned;
+    both maps that skip (contiguous) and that do not (zig-zag) are run."""
+    for kind, rank in (("zigzag", 1), ("contiguous", 1)):
+        N, S, n_q, n_kv = 4, 4096, 8, 2
+        print(f"ring bwd transfer {kind} N={N} rank={rank}", flush=True)
+        rng = np.random.default_rng(91)
+        c = S // N
+        q, _ = rand_inputs((1, c, n_q, 128), "bf16", rng)
+        k, _ = rand_inputs((1, S, n_kv, 128), "bf16", rng)
+        v, _ = rand_inputs((1, S, n_kv, 128), "bf16", rng)
+        do, _ = rand_inputs((1, c, n_q, 128), "bf16", rng)
+        tq, tdo = to_device(q, "bf16"), to_device(do, "bf16")
+        kc = runner.chunk_kv(to_device(k, "bf16"), kind, N)
+        vc = runner.chunk_kv(to_device(v, "bf16"), kind, N)
+        call = runner.RingCall(tq, kc, vc, kind=kind, S=S, N=N, rank=rank, causal=True)
+        o, lse = call()
+        dk0 = torch.from_numpy(rng.standard_normal((N, 1, c, n_kv, 128)).astype(np.float32)).cuda()
+        dv0 = torch.from_numpy(rng.standard_normal((N, 1, c, n_kv, 128)).astype(np.float32)).cuda()
+        outs = []
+        for serialize in (False, True):
+            desc, _ = ra.ring_desc(b=1, n_q=n_q, n_kv=n_kv, d=128, dtype=ra.RA_BF16, causal=True,
+                                   kind=kind, S=S, N=N, rank=rank,
+                                   flags=ra.RA_RING_SERIALIZE if serialize else 0)
+            ws = torch.full((ra.ra_ring_bwd_workspace_bytes(desc),), 0xFF, dtype=torch.uint8,
+                            device="cuda")
+            dq = torch.full(tuple(tq.shape), float("nan"), device="cuda")
+            dkc, dvc = dk0.clone(), dv0.clone()
+            ra.ra_ring_bwd(desc, tq, kc, vc, o, lse, tdo, dq, dkc, dvc, ws)
+            torch.cuda.synchronize()
+            outs.append((dq.cpu().numpy(), dkc.cpu().numpy(), dvc.cpu().numpy()))
+        for a_, b_, what in zip(outs[0], outs[1], ("dq", "dk", "dv")):
+            assert not np.isnan(a_).any(), (kind, what)
+            assert np.array_equal(a_, b_), (kind, what)
+        # the chunks this rank cannot see (contiguous: later ranks) are passed on unchanged
+        for j in range(N):
+            if j > rank and kind == "contiguous":
+                assert np.array_equal(outs[0][1][j], dk0[j].cpu().numpy())
+                assert np.array_equal(outs[0][2][j], dv0[j].cpu().numpy())
