@@ -218,6 +218,28 @@ ra_status ra_ring_fwd(const ra_ring_desc *desc, const void *q, const void *k_chu
                       const void *v_chunks, float *o, float *lse, void *workspace,
                       size_t workspace_bytes, void *compute, void *copy);
 
+/* Size of the static device scratch of ra_ring_fwd_noalloc (64 MiB per GPU). */
+#define RA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * ra_ring_fwd_noalloc -- ra_ring_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments and result as ra_ring_fwd, without the
+ * workspace: the workspace is a static device array of
+ * RA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends, and the chunk copies run on `stream` (as with
+ * RA_RING_SERIALIZE). No call allocates memory, creates a stream or an event.
+ * Returns RA_ERR_INVALID_ARG, before enqueueing anything, when
+ * ra_ring_workspace_bytes(desc) exceeds RA_NOALLOC_SCRATCH_BYTES (for
+ * example the 32K Llama-3-8B shard fits: about 33 MB).
+ * Every call on one GPU shares the scratch: calls that may overlap on a GPU
+ * (different streams, or threads without ordering) race and must be ordered
+ * by the caller. Each call writes every scratch byte it reads first, so a
+ * call does not depend on what an earlier one left there.
+ */
+ra_status ra_ring_fwd_noalloc(const ra_ring_desc *desc, const void *q, const void *k_chunks,
+                              const void *v_chunks, float *o, float *lse, void *stream);
+
 /* Workspace bytes ra_allgather_fwd needs for *desc (same validation as the call). */
 ra_status ra_allgather_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
 

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     RA_ERR_INVALID_ARG,
     RA_ERR_UNSUPPORTED,
     RA_F32,
+    RA_NOALLOC_SCRATCH_BYTES,
     RA_OK,
     RA_PART_CONTIGUOUS,
     RA_PART_STRIPED,
@@ -38,6 +39,7 @@ from ._lib import (  # noqa: F401
     ra_ring_bwd,
     ra_ring_bwd_workspace_bytes,
     ra_ring_fwd,
+    ra_ring_fwd_noalloc,
     ra_ring_workspace_bytes,
     ra_status_str,
     ra_v_transpose,

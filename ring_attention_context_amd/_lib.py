@@ -26,7 +26,8 @@ EXPORTED = ("ra_partition", "ra_block_attn_fwd", "ra_v_transpose", "ra_lse_merge
             "ra_ring_workspace_bytes", "ra_ring_fwd", "ra_attn_bwd_delta", "ra_block_attn_bwd",
             "ra_ring_bwd_workspace_bytes", "ra_ring_bwd", "ra_allgather_workspace_bytes",
             "ra_allgather_fwd", "ra_allgather_bwd_workspace_bytes", "ra_allgather_bwd",
-            "ra_status_str", "ra_last_error")
+            "ra_ring_fwd_noalloc", "ra_status_str", "ra_last_error")
+RA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class RingAttnError(RuntimeError):
@@ -88,7 +89,9 @@ def load_library(path=None):
                                                      ctypes.POINTER(ctypes.c_size_t)]
     lib.ra_allgather_bwd.argtypes = [ctypes.POINTER(RingDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, ctypes.c_size_t, vp]
-    for name in ("ra_partition", "ra_block_attn_fwd", "ra_v_transpose", "ra_lse_merge",
+    lib.ra_ring_fwd_noalloc.argtypes = [ctypes.POINTER(RingDesc), vp, vp, vp, vp, vp, vp]
+    for name in ("ra_ring_fwd_noalloc", "ra_partition", "ra_block_attn_fwd", "ra_v_transpose",
+                 "ra_lse_merge",
                  "ra_ring_workspace_bytes", "ra_ring_fwd", "ra_attn_bwd_delta",
                  "ra_block_attn_bwd", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd",
                  "ra_allgather_workspace_bytes", "ra_allgather_fwd",
@@ -251,6 +254,15 @@ def ra_ring_fwd(desc, q, k_chunks, v_chunks, o, lse, workspace, compute=None, co
     _check(load_library().ra_ring_fwd(ctypes.byref(desc), _ptr(q), _ptr(k_chunks),
                                       _ptr(v_chunks), _ptr(o), _ptr(lse), _ptr(workspace),
                                       ws_bytes, _stream(compute), _stream(copy)))
+
+
+def ra_ring_fwd_noalloc(desc, q, k_chunks, v_chunks, o, lse, stream=None):
+    """ra_ring_fwd with the library's static scratch as workspace and the copies
+    on ``stream``; allocates nothing (see ringattn.h for the size limit)."""
+    _need_contiguous(q, k_chunks, v_chunks, o, lse)
+    _check(load_library().ra_ring_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_chunks),
+                                              _ptr(v_chunks), _ptr(o), _ptr(lse),
+                                              _stream(stream)))
 
 
 def ra_ring_bwd_workspace_bytes(desc):

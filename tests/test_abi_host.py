@@ -317,3 +317,16 @@ def test_allgather_bwd_workspace_and_errors():
     st = lib.ra_allgather_bwd(ctypes.byref(desc), *args, FAKE, need, None)
     assert st == ra.RA_ERR_INVALID_ARG
 
+
+def test_noalloc_rejects_rings_beyond_its_scratch():
+    """ra_ring_fwd_noalloc checks the ring's workspace against the static
+    scratch before touching the GPU, and validates the descriptor like
+    ra_ring_fwd."""
+    lib = ra.load_library()
+    big = _ring(S=1 << 20, N=8, n_q=8, n_kv=8)        # ~1 GiB of double buffer
+    assert ra.ra_ring_workspace_bytes(big) > ra.RA_NOALLOC_SCRATCH_BYTES
+    st = lib.ra_ring_fwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == ra.RA_ERR_INVALID_ARG and "scratch" in ra.ra_last_error(), ra.ra_last_error()
+    bad = _ring(N=3)                                     # 1024 % 6 != 0 for zig-zag
+    assert lib.ra_ring_fwd_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == ra.RA_ERR_INVALID_ARG
