@@ -733,10 +733,26 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // A's MFMAs are written out so that the K and V rows (read-only, the B
   // operands) sit in AGPRs and S, dP land in VGPRs, where B reads them:
   // left to itself the compiler keeps K, V in VGPRs and S, dP in AGPRs, and
-  // moves all 32 results out of AGPRs on every sub-block. The compiler's
-  // hazard checks do not see these MFMAs: their results are read by B one
-  // iteration later (after several MFMAs), or by the element mask, which
-  // first waits out their writes.
+  // moves all 32 results out of AGPRs on every sub-block.
+  // Wait states. The hardware does not interlock a VALU read of a VGPR that
+  // an XDL (matrix) instruction writes: the CDNA3 / CDNA4 instruction-set
+  // guides' table of MAI dependencies requires the reader to issue at least
+  // 11 wait states after an 8-pass XDL write (5 / 7 / 11 / 19 for 2 / 4 / 8 /
+  // 16 passes on gfx940; gfx950 adds one), which the compiler's hazard
+  // recognizer inserts for the MFMAs it emits itself. These written-out
+  // MFMAs (32x32x16 bf16: 8 passes) are invisible to it, so every reader of
+  // S and dP keeps the distance by construction:
+  //   * the element mask, the only reader right after an A stream, first
+  //     issues three s_nop 7 (24 wait states, above even the 16-pass need);
+  //   * B reads a sub-block's S and dP in the next iteration's stream, its
+  //     first pair after that stream's fourth MFMA: at least four MFMAs (each
+  //     holding the matrix pipe for 8 passes) have issued after the last A
+  //     write (five after a full stream, four after A alone), far beyond 12
+  //     wait states;
+  //   * nothing else reads s or dp (the empty asm statements that pin them
+  //     emit no instruction).
+  // C's MFMAs are compiler-emitted builtins, so its results (dk, dv) and its
+  // operands written by B are covered by the compiler's own checks.
   auto mfma_a = [&](int par, int ai, const bf16x8 &o) INLINE {
     const int ds = ai >> 1;
     f32x16 &r = (ai & 1) ? dp[par] : s[par];
@@ -807,7 +823,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const bool need = qlim < KV_SUB || w_ragged || (a.causal && row0 < c_kmax) ||
                       (DOC && row0 + min<int64_t>(KV_SUB, qlim) - 1 >= c_dmin);
     if (need) {
-      // wait out the writes of the last A MFMAs (written out, see mfma_a)
+      // 24 wait states after the last written-out A MFMA before the VALU
+      // reads its results (the requirement is set out at mfma_a).
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
       const int32_t *pp = p_stage(stage) + rb;
       const int32_t *lp = lo_stage(stage) + rb;
