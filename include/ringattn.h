@@ -296,8 +296,9 @@ ra_status ra_block_attn_bwd(const ra_attn_desc *desc, const void *q, const void 
                             const void *v, const void *dout, const float *lse,
                             const float *delta, float *dq, float *dk, float *dv, void *stream);
 
-/* Workspace bytes ra_ring_bwd needs: positions (S int32), D (b*c*n_q floats),
- * the queries' document starts (c int32) and, for N > 1, the double buffer of
+/* Workspace bytes ra_ring_bwd needs: positions (S int32), D and the lse in
+ * log2 units per query head (2*b*c*n_q floats, head-major), the queries'
+ * document starts (c int32) and, for N > 1, the double buffer of
  * the travelling block: two halves of K, V (bf16) and dK, dV (float32), one
  * chunk each. */
 ra_status ra_ring_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
@@ -347,8 +348,9 @@ ra_status ra_allgather_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *byt
  * contribution to chunk j's dK, dV is ADDED to slot j of dk_chunks /
  * dv_chunks (the reduce-scatter's input: summing every rank's calls on the
  * same slots gives each chunk's dK, dV). workspace: >=
- * ra_allgather_bwd_workspace_bytes(): positions, D, document starts, the
- * gathered K and V of the sequence (bf16) and the chunk row of each
+ * ra_allgather_bwd_workspace_bytes(): positions, D and the log2 lse
+ * (head-major), document starts, the gathered K and V of the sequence
+ * (bf16) and the chunk row of each
  * position (int32; the gradients go straight into the slots). One stream;
  * step_events unused.
  */

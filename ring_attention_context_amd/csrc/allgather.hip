@@ -156,8 +156,8 @@ ra_status make_ag_bwd_plan(const ra_ring_desc *r, AgBwdPlan *p) {
   off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
   p->qlo_off = off;
   off += align_up(static_cast<size_t>(p->c) * sizeof(int32_t));
-  p->delta_off = off;
-  off += align_up(static_cast<size_t>(r->b) * p->c * r->n_q * sizeof(float));
+  p->delta_off = off;  // D, then the lse in log2 units: head-major [b, n_q, c] each
+  off += align_up(2 * static_cast<size_t>(r->b) * p->c * r->n_q * sizeof(float));
   p->k_off = off;
   off += align_up(p->kv_bytes);
   p->v_off = off;
@@ -326,7 +326,8 @@ extern "C" ra_status ra_allgather_bwd(const ra_ring_desc *r, const void *q, cons
     st = hip_check(ra::launch_gather_i32(r->doc_start, q_pos, qlo, P.c, s),
                    "ra_allgather_bwd: document starts");
   if (st == RA_OK)
-    st = hip_check(ra::launch_bwd_delta(rows, r->d, 2, dout, o, delta, s), "ra_allgather_bwd: delta");
+    st = hip_check(ra::launch_bwd_prep(r->b, P.c, r->n_q, dout, o, lse, delta, delta + rows, s),
+                   "ra_allgather_bwd: delta");
   if (st == RA_OK)
     st = hip_check(ra::launch_fill_zero(dq, rows * r->d, s), "ra_allgather_bwd: zero dq");
   if (st == RA_OK)
@@ -345,8 +346,9 @@ extern "C" ra_status ra_allgather_bwd(const ra_ring_desc *r, const void *q, cons
   a.k = kfull;
   a.v = vfull;
   a.dout = dout;
-  a.lse = lse;
+  a.lse = delta + rows;
   a.delta = delta;
+  a.hm = 1;
   a.dq = dq;
   a.dk = dk_chunks;  // each key's dK, dV go straight into its chunk's slot
   a.dv = dv_chunks;

@@ -16,15 +16,19 @@
 //     P^T = 2^(S^T scale log2 e - lse log2 e), dS^T = P^T (dP^T - D), and
 //     dQ^T += K^T dS^T (K^T operands by the transposing ds_read_b64_tr_b16).
 //     Every lane holds one query, so lse and D are per-lane constants;
-//   * bwd_dkdv_kernel (bf16, d = 128): a wave owns 32 keys of one key/value
-//     head, with its K and V rows in registers; 4 waves share each block of 64
-//     queries (q, do, lse, D, positions) staged in LDS, for every query head of
-//     the GQA group, and work through it in 32-row sub-blocks: A, S = Q K^T and
-//     dP = dO V^T (Q and dO rows by ds_read_b128); B, P and dS on the VALU; C,
-//     dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T by the transposing read),
-//     so each lane ends up holding d-values of one key. The sub-blocks run as
-//     a software pipeline: A of the next and C of the previous sub-block share
-//     one stream of MFMAs into which B of the current one is interleaved.
+//   * bwd_dkdv_kernel (bf16, d = 128): a workgroup owns 128 keys of one
+//     key/value head in four groups of 32, one group per SIMD, and walks the
+//     blocks of 64 queries (q, do, lse, D, positions, staged in LDS) of every
+//     query head of the GQA group in 32-row sub-blocks. Each SIMD runs two
+//     waves with split roles: the producer holds the group's K and V rows and
+//     computes A, S = Q K^T and dP = dO V^T (Q and dO rows by ds_read_b128),
+//     and B, P and dS on the VALU, which it hands over through LDS in the
+//     B-operand lane order; the consumer holds the dK^T and dV^T accumulators
+//     and computes C, dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T by the
+//     transposing read). One barrier per sub-block moves the pipeline on: the
+//     producer runs A of the next and B of the current sub-block while the
+//     consumer runs C of the previous one, so the producer's exponentials
+//     overlap the consumer's MFMAs on the same SIMD.
 // P and dS enter the MFMAs as bf16; every accumulation is fp32. dq, dk and dv
 // are float32 and ACCUMULATED into (+=): the ring adds one block per step.
 #include <climits>
@@ -137,10 +141,17 @@ __device__ __forceinline__ bf16x8 tr_read(const unsigned char *base, const uint3
 
 // ---------------------------------------------------------------- D = do . o
 
-template <typename T, int DD>
+// HM: instead of delta[r], write the head-major pair delta_t, lse_t
+// [b, n_q, s] -- D and the row's lse in log2 units (+inf for a query with no
+// visible key) -- the per-row arrays the dK/dV kernel stages, one contiguous
+// run per head and query block.
+template <typename T, int DD, bool HM>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(int64_t rows, const T *__restrict__ dout,
                                                         const float *__restrict__ o,
-                                                        float *__restrict__ delta) {
+                                                        float *__restrict__ delta,
+                                                        int64_t s, int32_t n_q,
+                                                        const float *__restrict__ lse,
+                                                        float *__restrict__ lse_t) {
   constexpr int TPR = DD / 8;  // threads per row, 8 elements each
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -163,11 +174,20 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(int64_t rows, const T *_
       x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
       x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
     }
-    float s = x[0] * o0.x + x[1] * o0.y + x[2] * o0.z + x[3] * o0.w +
-              x[4] * o1.x + x[5] * o1.y + x[6] * o1.z + x[7] * o1.w;
+    float sum = x[0] * o0.x + x[1] * o0.y + x[2] * o0.z + x[3] * o0.w +
+                x[4] * o1.x + x[5] * o1.y + x[6] * o1.z + x[7] * o1.w;
 #pragma unroll
-    for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-    if (t == 0) delta[r] = s;
+    for (int m = TPR / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+    if (t == 0) {
+      if constexpr (HM) {
+        const int64_t h = r % n_q, bt = r / n_q;
+        const int64_t hr = ((bt / s) * n_q + h) * s + bt % s;
+        delta[hr] = sum;
+        lse_t[hr] = lse_log2(lse[r]);
+      } else {
+        delta[r] = sum;
+      }
+    }
   }
 }
 
@@ -273,8 +293,9 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
   }
   const int32_t qpos = !a.causal ? INT_MAX - 1 : (tok_ok ? a.q_pos[tok] : INT_MIN);
   const int32_t qlo = DOC && tok_ok ? a.q_lo[tok] : INT_MIN;  // document start
-  const float lse2 = tok_ok ? lse_log2(a.lse[row]) : INFINITY;
-  const float dlt = tok_ok ? a.delta[row] : 0.f;
+  const int64_t hrow = (static_cast<int64_t>(bi) * a.n_q + h) * a.s_q + tok;
+  const float lse2 = !tok_ok ? INFINITY : a.hm ? a.lse[hrow] : lse_log2(a.lse[row]);
+  const float dlt = !tok_ok ? 0.f : a.hm ? a.delta[hrow] : a.delta[row];
   const float sl2 = a.scale * LOG2E;
 
   uint32_t koff[D / 16];
@@ -442,76 +463,61 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dK, dV
 
-constexpr int KV_WAVES = 4;
+constexpr int KV_GROUPS = 4;                 // key groups of 32 keys, one per SIMD
+constexpr int KV_WAVES = 2 * KV_GROUPS;      // a producer and a consumer wave per group
 constexpr int KV_THREADS = KV_WAVES * 64;
-constexpr int KV_KW = 32;                    // keys per wave
-constexpr int KV_KT = KV_WAVES * KV_KW;      // keys per workgroup
+constexpr int KV_KW = 32;                    // keys per group
+constexpr int KV_KT = KV_GROUPS * KV_KW;     // keys per workgroup
 constexpr int KV_QB = 64;                    // queries per staged block (two 32-row sub-blocks)
 constexpr int KV_SUB = 32;
-constexpr int KV_TILE_B = KV_QB * ROW_B;     // 16 KiB (q or do)
+constexpr int KV_TILE_B = KV_QB * ROW_B;     // 16 KiB (q or dout rows)
 constexpr int KV_LOADS = KV_TILE_B / (1024 * KV_WAVES);
+constexpr int KV_NSTAGE = 3;
+// LDS: KV_NSTAGE stages of one query block -- q rows, dout rows and, per row,
+// the lse (log2 units), delta, position and document start -- then the P / dS
+// hand-over buffers, two per group (P then dS, each two 1 KiB k-steps in the
+// lane order of the B operand).
+constexpr int ST_Q = 0;
+constexpr int ST_D = ST_Q + KV_TILE_B;
+constexpr int ST_L = ST_D + KV_TILE_B;
+constexpr int ST_E = ST_L + KV_QB * 4;
+constexpr int ST_P = ST_E + KV_QB * 4;
+constexpr int ST_O = ST_P + KV_QB * 4;
+constexpr int STAGE_B = ST_O + KV_QB * 4;
+constexpr int XG_B = 4 * 1024;
+constexpr int XCH = KV_NSTAGE * STAGE_B;
+constexpr int KV_LDS_B = XCH + KV_GROUPS * 2 * XG_B;
+static_assert(KV_LOADS * 1024 * KV_WAVES == KV_TILE_B, "block split over waves");
+static_assert(STAGE_B % 256 == 0, "stage bases leave the swizzled address bits alone");
+static_assert(KV_LDS_B <= 160 * 1024, "LDS of one workgroup");
 
 template <bool DOC>
 __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char q_lds0[KV_TILE_B], q_lds1[KV_TILE_B],
-      q_lds2[KV_TILE_B];
-  __shared__ __attribute__((aligned(16))) unsigned char d_lds0[KV_TILE_B], d_lds1[KV_TILE_B],
-      d_lds2[KV_TILE_B];
-  // per stage: lse (64 floats), delta (64 floats), positions (64 int32) of the block's rows
-  __shared__ __attribute__((aligned(16))) float l_lds0[64], l_lds1[64], l_lds2[64];
-  __shared__ __attribute__((aligned(16))) float e_lds0[64], e_lds1[64], e_lds2[64];
-  __shared__ __attribute__((aligned(16))) int32_t p_lds0[64], p_lds1[64], p_lds2[64];
-  // ... and the rows' document starts (document mask)
-  __shared__ __attribute__((aligned(16))) int32_t o_lds0[64], o_lds1[64], o_lds2[64];
-  auto q_stage = [&](auto s) INLINE -> unsigned char * {
-    constexpr int v = decltype(s)::value;
-    return v == 0 ? q_lds0 : v == 1 ? q_lds1 : q_lds2;
-  };
-  auto d_stage = [&](auto s) INLINE -> unsigned char * {
-    constexpr int v = decltype(s)::value;
-    return v == 0 ? d_lds0 : v == 1 ? d_lds1 : d_lds2;
-  };
-  auto l_stage = [&](auto s) INLINE -> float * {
-    constexpr int v = decltype(s)::value;
-    return v == 0 ? l_lds0 : v == 1 ? l_lds1 : l_lds2;
-  };
-  auto e_stage = [&](auto s) INLINE -> float * {
-    constexpr int v = decltype(s)::value;
-    return v == 0 ? e_lds0 : v == 1 ? e_lds1 : e_lds2;
-  };
-  auto p_stage = [&](auto s) INLINE -> int32_t * {
-    constexpr int v = decltype(s)::value;
-    return v == 0 ? p_lds0 : v == 1 ? p_lds1 : p_lds2;
-  };
-  auto lo_stage = [&](auto s) INLINE -> int32_t * {
-    constexpr int v = decltype(s)::value;
-    return v == 0 ? o_lds0 : v == 1 ? o_lds1 : o_lds2;
-  };
-
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[KV_LDS_B];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int lane = tid & 63;
   const int col = lane & 31;
   const int hi = lane >> 5;
+  const int grp = wave & (KV_GROUPS - 1);
+  const bool producer = wave < KV_GROUPS;
 
   // ---- workgroup -> (batch, kv head, key tile); earliest keys (most queries) first ----
-  const int64_t nkt = (a.s_kv + KV_KT - 1) / KV_KT;
   const int64_t inner = static_cast<int64_t>(a.b) * a.n_kv;
   const int64_t kt = blockIdx.x / inner;
   const int kvh = static_cast<int>(blockIdx.x % a.n_kv);
   const int bi = static_cast<int>((blockIdx.x / a.n_kv) % a.b);
-  (void)nkt;
   const int g = a.n_q / a.n_kv;
 
   const int64_t wg_key0 = kt * KV_KT;
-  const int64_t w_key0 = wg_key0 + wave * KV_KW;
+  const int64_t w_key0 = wg_key0 + grp * KV_KW;
   const int64_t key = w_key0 + col;
   const bool key_ok = key < a.s_kv;
-  const bool wave_has_keys = w_key0 < a.s_kv;
+  const bool grp_has_keys = w_key0 < a.s_kv;
   const int32_t kpos = !key_ok ? INT_MAX : (a.causal ? a.kv_pos[key] : INT_MIN);
-  // The wave's first and last key positions (causal skips and masks).
+  // The group's first and last key positions (causal skips and masks).
   int32_t w_kmin = INT_MIN, w_kmax = INT_MIN;
-  if (a.causal && wave_has_keys) {
+  if (a.causal && grp_has_keys) {
     w_kmin = a.kv_pos[w_key0];
     w_kmax = a.kv_pos[min(w_key0 + KV_KW, a.s_kv) - 1];
   }
@@ -519,56 +525,62 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // ---- query range that can see any key of the workgroup ----
   // Causal: from the first query at or after its first key. With a document
   // mask, up to the last query whose document starts at or before its last
-  // key (document starts are non-decreasing).
+  // key (document starts are non-decreasing). (The searches read memory, so
+  // the compiler cannot see that their results agree across lanes: say so.)
   int64_t q_first = 0, q_end = a.s_q;
   if (a.causal) q_first = count_lt(a.q_pos, a.s_q, a.kv_pos[wg_key0]);
   if (DOC) q_end = count_le(a.q_lo, a.s_q, a.kv_pos[min(wg_key0 + KV_KT, a.s_kv) - 1]);
-  const int64_t qb0 = q_first / KV_QB;
-  const int64_t nqb = (q_end + KV_QB - 1) / KV_QB;
+  const int64_t qb0 = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(q_first / KV_QB));
+  const int64_t nqb = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((q_end + KV_QB - 1) / KV_QB));
   const int64_t n_blk = nqb > qb0 ? nqb - qb0 : 0;   // query blocks per head
   const int n_it = static_cast<int>(n_blk * g);
+  const int n_sub = 2 * n_it;
+  const int64_t qb_last = qb0 + n_blk - 1;
 
-  // ---- this lane's key: B operands of S = Q K^T and dP = dO V^T ----
-  const uint16_t *kg = static_cast<const uint16_t *>(a.k);
-  const uint16_t *vg = static_cast<const uint16_t *>(a.v);
-  bf16x8 kreg[D / 16], vreg[D / 16];
-  const int64_t krow = (static_cast<int64_t>(bi) * a.s_kv + (key_ok ? key : 0)) * a.n_kv + kvh;
-#pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds) {
-    const u32x4 rk = key_ok ? *reinterpret_cast<const u32x4 *>(kg + krow * D + ds * 16 + hi * 8)
-                            : u32x4{0, 0, 0, 0};
-    const u32x4 rv = key_ok ? *reinterpret_cast<const u32x4 *>(vg + krow * D + ds * 16 + hi * 8)
-                            : u32x4{0, 0, 0, 0};
-    kreg[ds] = __builtin_bit_cast(bf16x8, rk);
-    vreg[ds] = __builtin_bit_cast(bf16x8, rv);
-    asm volatile("" : "+a"(kreg[ds]), "+a"(vreg[ds]));  // they live in AGPRs (see mfma_a)
+  // ---- the group's sub-blocks ----
+  // Sub-block n = 2 it + h holds rows 32h .. 32h+31 of the block of iteration
+  // it. A sub-block whose rows are all before the group's first key (causal),
+  // or all start their document after its last key, or lie past the
+  // sequence, sees none of the group's keys. In row terms the useful first
+  // rows r (multiples of 32) satisfy c_vis - 31 <= r < r_end; they form one
+  // range of blocks in the walk, whose first and last blocks may have one
+  // useless half per head (those run fully masked and add nothing). n_lo ..
+  // n_hi is that range in the walk. c_kmax / c_dmin decide which sub-blocks
+  // need the element mask.
+  int64_t c_vis = 0, c_kmax = 0, r_end = a.s_q, c_dmin = a.s_q;
+  if (a.causal && grp_has_keys) {
+    c_vis = wave_count<false>(a.q_pos, a.s_q, w_kmin, lane);
+    c_kmax = wave_count<false>(a.q_pos, a.s_q, w_kmax, lane);
   }
-  const float sl2 = a.scale * LOG2E;
-
-  // Q / dO rows by ds_read_b128 (row = query col), chunk 2*ds + hi: the
-  // swizzle is an XOR of the chunk index, so k-step ds reads at qoff0 with
-  // bits 5..7 XORed by ds. Likewise the transposing reads of d block db are at
-  // toff0 with bits 6..7 XORed by db. (`pin` keeps the compiler from hoisting
-  // the XORs back into eight registers each.)
-  uint32_t qoff0 = col * ROW_B + (((hi ^ swz(col & 15))) << 4);
-  auto qoff = [&](int ds) INLINE -> uint32_t { return qoff0 ^ (static_cast<uint32_t>(ds) << 5); };
-  uint32_t toff0[2];
-  {
-    uint32_t toff[2][D / 32];
-    tr_offsets(lane, toff);
-    toff0[0] = toff[0][0];
-    toff0[1] = toff[1][0];
+  if (DOC && grp_has_keys) {
+    r_end = min(r_end, wave_count<true>(a.q_lo, a.s_q, w_kmax, lane));
+    c_dmin = wave_count<true>(a.q_lo, a.s_q, w_kmin, lane);
   }
-  auto tread = [&](const unsigned char *base, int db, int row0) INLINE -> bf16x8 {
-    const uint32_t x = static_cast<uint32_t>(db) << 6;
-    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (LDS_AS bf16x4 *)(base + (toff0[0] ^ x) + row0 * ROW_B));
-    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (LDS_AS bf16x4 *)(base + (toff0[1] ^ x) + row0 * ROW_B));
-    return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-  };
+  int64_t R_lo = (c_vis - 31 + 31) / 32;  // ceil((c_vis - 31) / 32) for c_vis >= 0
+  if (c_vis < 31) R_lo = 0;
+  int64_t R_hi = (r_end + 31) / 32 - 1;   // last useful 32-row unit
+  R_lo = max(R_lo, 2 * qb0);
+  R_hi = min(R_hi, 2 * qb_last + 1);
+  int n_lo = 0, n_hi = 0;
+  if (grp_has_keys && n_blk > 0 && R_lo <= R_hi) {
+    const int64_t j_first = qb_last - R_hi / 2;          // walk block of the latest unit
+    const int64_t h_min = max<int64_t>(0, R_lo - 2 * (qb_last - j_first));
+    n_lo = static_cast<int>(2 * (j_first * g) + h_min);
+    const int64_t j_last = qb_last - R_lo / 2;           // walk block of the earliest unit
+    const int64_t h_max = min<int64_t>(1, R_hi - 2 * (qb_last - j_last));
+    n_hi = static_cast<int>(2 * (j_last * g + g - 1) + h_max + 1);
+  }
+  n_lo = __builtin_amdgcn_readfirstlane(n_lo);
+  n_hi = __builtin_amdgcn_readfirstlane(n_hi);
+  const bool any = n_lo < n_hi;
+  const bool w_ragged = w_key0 + KV_KW > a.s_kv;   // some key of the group past the block
 
   // ---- staging of one query block (iteration it -> head, block) ----
+  // Iteration it -> (query block, head): blocks from the last one down, the g
+  // heads of a block back to back. Every workgroup of a kv head then walks the
+  // same blocks in the same order (they differ only in where they stop), so
+  // workgroups resident together read each block while it is in L2. Block it
+  // lives in stage it % 3.
   const unsigned char *qbytes = static_cast<const unsigned char *>(a.q);
   const unsigned char *dbytes = static_cast<const unsigned char *>(a.dout);
   const int64_t q_row_bytes = static_cast<int64_t>(a.n_q) * D * 2;
@@ -578,362 +590,302 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int r = 4 * (wave + KV_WAVES * i) + (lane >> 4);
     goff[i] = static_cast<uint32_t>(r * q_row_bytes + (((lane & 15) ^ swz(r & 15)) << 4));
   }
-  // Iteration it -> (query block, head): blocks from the last one down, the g
-  // heads of a block back to back. Every workgroup of a kv head then walks the
-  // same blocks in the same order (they differ only in where they stop), so
-  // workgroups resident together read each block while it is in L2.
+  auto stage_b = [&](int it) INLINE -> uint32_t {
+    return static_cast<uint32_t>(it % KV_NSTAGE) * STAGE_B;
+  };
   auto blk_of = [&](int it, int64_t *q0, int *h) INLINE {
     const int64_t j = it / g;
     *q0 = (qb0 + n_blk - 1 - j) * KV_QB;
     *h = kvh * g + static_cast<int>(it - j * g);
   };
-  auto issue_blk = [&](int it, auto stage) INLINE {
+  auto blk_q0 = [&](int it) INLINE -> int64_t { return (qb_last - it / g) * KV_QB; };
+  // A block's loads: KV_LOADS 16-byte loads each of its q and dout rows per
+  // wave; waves 0-3 also stage one per-row array each (lse, delta, positions
+  // when causal, document starts with a document mask).
+  auto issue_blk = [&](int it) INLINE {
     int64_t q0;
     int h;
     blk_of(it, &q0, &h);
     const int64_t left = a.s_q - q0;
     const int64_t rbase = (static_cast<int64_t>(bi) * a.s_q + q0) * a.n_q + h;
+    const uint32_t sb = stage_b(it);
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc(qbytes + rbase * D * 2, (left - 1) * q_row_bytes + D * 2);
     const __amdgpu_buffer_rsrc_t rd =
         make_rsrc(dbytes + rbase * D * 2, (left - 1) * q_row_bytes + D * 2);
 #pragma unroll
     for (int i = 0; i < KV_LOADS; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rq, (LDS_AS void *)(q_stage(stage) + 4 * (wave + KV_WAVES * i) * ROW_B), 16, goff[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rd, (LDS_AS void *)(d_stage(stage) + 4 * (wave + KV_WAVES * i) * ROW_B), 16, goff[i], 0, 0, 0);
+      const uint32_t row_b = sb + 4 * (wave + KV_WAVES * i) * ROW_B;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (LDS_AS void *)(smem + row_b + ST_Q), 16, goff[i],
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LDS_AS void *)(smem + row_b + ST_D), 16, goff[i],
+                                               0, 0, 0);
     }
-    // lse and delta rows q0 + lane of head h (stride n_q floats); positions q0 + lane.
-    if (wave == 0) {
-      const __amdgpu_buffer_rsrc_t rl =
-          make_rsrc(a.lse + rbase, ((left - 1) * a.n_q + 1) * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LDS_AS void *)l_stage(stage), 4,
-                                               lane * a.n_q * 4, 0, 0, 0);
-    } else if (wave == 1) {
-      const __amdgpu_buffer_rsrc_t re =
-          make_rsrc(a.delta + rbase, ((left - 1) * a.n_q + 1) * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (LDS_AS void *)e_stage(stage), 4,
-                                               lane * a.n_q * 4, 0, 0, 0);
+    // lse and delta of rows q0 + lane of head h: head-major runs (hm), else
+    // rows with stride n_q floats; positions and document starts q0 + lane.
+    const int64_t hbase = (static_cast<int64_t>(bi) * a.n_q + h) * a.s_q + q0;
+    if (wave < 2) {
+      const float *src = wave == 0 ? a.lse : a.delta;
+      const __amdgpu_buffer_rsrc_t rr =
+          a.hm ? make_rsrc(src + hbase, left * 4) : make_rsrc(src + rbase, ((left - 1) * a.n_q + 1) * 4);
+      const uint32_t lo = a.hm ? lane * 4 : lane * a.n_q * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (LDS_AS void *)(smem + sb + (wave == 0 ? ST_L : ST_E)),
+                                               4, lo, 0, 0, 0);
     } else if (wave == 2 && a.causal) {
       const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.q_pos + q0, left * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (LDS_AS void *)p_stage(stage), 4, lane * 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (LDS_AS void *)(smem + sb + ST_P), 4, lane * 4,
                                                0, 0, 0);
     } else if (DOC && wave == 3) {
-      const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_lo + q0, left * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (LDS_AS void *)lo_stage(stage), 4, lane * 4,
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.q_lo + q0, left * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (LDS_AS void *)(smem + sb + ST_O), 4, lane * 4,
                                                0, 0, 0);
     }
   };
+  // Unless the lse comes in log2 units already (hm), wave 0 converts each
+  // block's lse in place (-inf, a query with no key, to +inf so that its
+  // probabilities are 0) in the iteration before its first B.
+  auto prescale_lse = [&](int it) INLINE {
+    if (wave == 0 && !a.hm) {
+      float *l = reinterpret_cast<float *>(smem + stage_b(it) + ST_L);
+      l[lane] = lse_log2(l[lane]);
+    }
+  };
+  // Iteration n (from -1 to n_sub): the producer runs A on sub-block n+1 and
+  // B on n, the consumer C on n-1. Block j+3 goes into the stage of block j,
+  // whose last C ran in iteration 2j+2: its loads are issued at the start of
+  // iteration 2j+3 and have landed by the barrier that ends iteration 2j+4
+  // (every even iteration waits for the loads in flight); wave 0 converts its
+  // lse in iteration 2j+5, before B of its first sub-block in 2j+6. The
+  // barrier that ends each iteration publishes the P and dS the producers
+  // wrote for the consumers' next iteration.
+  auto begin_iter = [&](int n) INLINE {
+    if ((n & 1) && n >= 3 && (n + 3) / 2 < n_it) issue_blk((n + 3) / 2);
+    if ((n & 1) && (n + 1) / 2 < n_it) prescale_lse((n + 1) / 2);
+  };
+  auto end_iter = [&](int n) INLINE {
+    if ((n & 1) == 0) wait_own_loads();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS writes and reads done
+    __builtin_amdgcn_s_barrier();
+  };
 
+  if (n_it > 0) issue_blk(0);
+  if (n_it > 1) issue_blk(1);
+  if (n_it > 2) issue_blk(2);
+  wait_own_loads();
+  __syncthreads();
+
+  // Q / dO rows by ds_read_b128 (row = query col), chunk 2*ds + hi: the
+  // swizzle is an XOR of the chunk index, so k-step ds reads at qoff0 with
+  // bits 5..7 XORed by ds. Likewise the transposing reads of d block db are at
+  // toff0 with bits 6..7 XORed by db. Stage bases and row offsets are
+  // multiples of 256 and leave those bits alone.
+  const uint32_t qoff0 = col * ROW_B + (((hi ^ swz(col & 15))) << 4);
+  uint32_t toff0[2];
+  {
+    uint32_t toff[2][D / 32];
+    tr_offsets(lane, toff);
+    toff0[0] = toff[0][0];
+    toff0[1] = toff[1][0];
+  }
+  // This group's hand-over buffers: parity x at xch + x * XG_B; P of k-step
+  // ks at + ks * 1 KiB, dS at + 2 KiB + ks * 1 KiB, lane l at + 16 l.
+  const uint32_t xch = XCH + grp * 2 * XG_B + lane * 16;
+  const float sl2 = a.scale * LOG2E;
+  constexpr int DIST = 4;  // operand reads ahead of their MFMA
+
+  if (producer) {
+    // ---- producer: A (S = Q K^T, dP = dO V^T) and B (P, dS) ----
+    // This lane's key: the B operands of S = Q K^T and dP = dO V^T.
+    const uint16_t *kg = static_cast<const uint16_t *>(a.k);
+    const uint16_t *vg = static_cast<const uint16_t *>(a.v);
+    bf16x8 kreg[D / 16], vreg[D / 16];
+    const int64_t krow = (static_cast<int64_t>(bi) * a.s_kv + (key_ok ? key : 0)) * a.n_kv + kvh;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      const u32x4 rk = key_ok ? *reinterpret_cast<const u32x4 *>(kg + krow * D + ds * 16 + hi * 8)
+                              : u32x4{0, 0, 0, 0};
+      const u32x4 rv = key_ok ? *reinterpret_cast<const u32x4 *>(vg + krow * D + ds * 16 + hi * 8)
+                              : u32x4{0, 0, 0, 0};
+      kreg[ds] = __builtin_bit_cast(bf16x8, rk);
+      vreg[ds] = __builtin_bit_cast(bf16x8, rv);
+    }
+    // S accumulator: lane holds key `col`; element e holds sub-block row
+    // (e/4)*8 + hi*4 + e%4. Scores are double-buffered by sub-block parity.
+    f32x16 s[2], dp[2];
+    bf16x8 pb[2], dsb[2];   // P and dS of the sub-block in B, per k-step
+    float4 l4[4], d4[4];    // its rows' lse (log2 units) and D
+    // Operand of A item ai (k-step ai/2; S from the Q rows when ai is even, dP
+    // from the dO rows when odd); qa = stage base + rows + qoff0.
+    auto rd_a = [&](uint32_t qa, int ai) INLINE -> bf16x8 {
+      const uint32_t off = (qa ^ (static_cast<uint32_t>(ai >> 1) << 5)) + ((ai & 1) ? ST_D : ST_Q);
+      return *reinterpret_cast<const bf16x8 *>(smem + off);
+    };
+    auto mfma_a = [&](int par, int ai, const bf16x8 &o) INLINE {
+      const int ds = ai >> 1;
+      if (ai & 1)
+        dp[par] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, vreg[ds], ds == 0 ? f32x16{} : dp[par], 0, 0, 0);
+      else
+        s[par] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, kreg[ds], ds == 0 ? f32x16{} : s[par], 0, 0, 0);
+    };
+    auto read_ld = [&](uint32_t sb, int rb) INLINE {
+      const float *ll = reinterpret_cast<const float *>(smem + sb + ST_L) + rb;
+      const float *ee = reinterpret_cast<const float *>(smem + sb + ST_E) + rb;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        l4[e4] = *reinterpret_cast<const float4 *>(ll + e4 * 8 + hi * 4);
+        d4[e4] = *reinterpret_cast<const float4 *>(ee + e4 * 8 + hi * 4);
+      }
+    };
+    // Two elements (el, el+1) of B: p = 2^(S scale log2 e - lse'),
+    // ds = p (dP - D), converted to bf16 together.
+    auto b_pair = [&](int par, int el) INLINE {
+#pragma unroll
+      for (int j = el; j < el + 2; ++j) {
+        const float p = exp2_fast(fmaf(s[par][j], sl2, -l4[j >> 2][j & 3]));
+        pb[j >> 3][j & 7] = static_cast<__bf16>(p);
+        dsb[j >> 3][j & 7] = static_cast<__bf16>(p * (dp[par][j] - d4[j >> 2][j & 3]));
+      }
+      // Keep the pair here, between the MFMAs: otherwise the compiler sinks
+      // all of B past the stream, where nothing overlaps it.
+      asm volatile("" : "+v"(pb[el >> 3]), "+v"(dsb[el >> 3]));
+    };
+    auto write_x = [&](int par) INLINE {
+      unsigned char *x = smem + xch + par * XG_B;
+      *reinterpret_cast<bf16x8 *>(x) = pb[0];
+      *reinterpret_cast<bf16x8 *>(x + 1024) = pb[1];
+      *reinterpret_cast<bf16x8 *>(x + 2048) = dsb[0];
+      *reinterpret_cast<bf16x8 *>(x + 3072) = dsb[1];
+    };
+    // A of one sub-block (16 MFMAs), with B of another interleaved (a pair
+    // after every odd MFMA) when WITH_B.
+    auto a_stream = [&](auto with_b, uint32_t qa, int pa, int pbp) INLINE {
+      constexpr bool WB = decltype(with_b)::value;
+      bf16x8 op[DIST + 1];
+#pragma unroll
+      for (int i = 0; i < DIST; ++i) op[i] = rd_a(qa, i);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + DIST < 16) op[(i + DIST) % (DIST + 1)] = rd_a(qa, i + DIST);
+        mfma_a(pa, i, op[i % (DIST + 1)]);
+        if (WB && (i & 1)) b_pair(pbp, i - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto b_only = [&](int pbp) INLINE {
+#pragma unroll
+      for (int el = 0; el < 16; el += 2) b_pair(pbp, el);
+    };
+    // Element mask of A's scores (sub-block at rows rb of the stage at sb,
+    // block rows from q0): rows past the sequence, keys past the block, a
+    // query before the key (causal), or a key before the query's document.
+    auto mask_a = [&](uint32_t sb, int rb, int par, int64_t q0) INLINE {
+      const int qlim = static_cast<int>(min<int64_t>(a.s_q - q0 - rb, KV_SUB));
+      const int64_t row0 = q0 + rb;
+      const bool need = qlim < KV_SUB || w_ragged || (a.causal && row0 < c_kmax) ||
+                        (DOC && row0 + qlim - 1 >= c_dmin);
+      if (need) {
+        const int32_t *pp = reinterpret_cast<const int32_t *>(smem + sb + ST_P) + rb;
+        const int32_t *lp = reinterpret_cast<const int32_t *>(smem + sb + ST_O) + rb;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int r0 = e4 * 8 + hi * 4;
+          int4 p4 = int4{INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+          int4 o4 = int4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+          if (a.causal) p4 = *reinterpret_cast<const int4 *>(pp + r0);
+          if (DOC) o4 = *reinterpret_cast<const int4 *>(lp + r0);
+          const int32_t qp[4] = {p4.x, p4.y, p4.z, p4.w};
+          const int32_t ql[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool out = (r0 + j >= qlim) | (kpos > qp[j]) | (kpos < ql[j]) | !key_ok;
+            s[par][e4 * 4 + j] = out ? -INFINITY : s[par][e4 * 4 + j];
+          }
+        }
+      }
+    };
+    // Iteration n with its parity PAR compile-time: B on sub-block n (scores
+    // s[PAR]), A on n+1 (into s[1 - PAR]).
+    auto step = [&](auto par_c, int n) INLINE {
+      constexpr int PAR = decltype(par_c)::value;
+      begin_iter(n);
+      const bool do_a = n + 1 >= n_lo && n + 1 < n_hi;
+      const bool do_b = n >= n_lo && n < n_hi;
+      const int ja = (n + 1) >> 1, jb = n >> 1;
+      const uint32_t sba = stage_b(ja), sbb = stage_b(jb);
+      const uint32_t qa = sba + 32 * (1 - PAR) * ROW_B + qoff0;
+      if (do_b) read_ld(sbb, 32 * PAR);
+      if (do_a && do_b) {
+        a_stream(std::true_type{}, qa, 1 - PAR, PAR);
+      } else if (do_a) {
+        a_stream(std::false_type{}, qa, 1 - PAR, PAR);
+      } else if (do_b) {
+        b_only(PAR);
+      }
+      if (do_b) write_x(PAR);
+      if (do_a) mask_a(sba, 32 * (1 - PAR), 1 - PAR, blk_q0(ja));
+      end_iter(n);
+    };
+    for (int n = -1; n <= n_sub; n += 2) {
+      step(std::integral_constant<int, 1>{}, n);
+      step(std::integral_constant<int, 0>{}, n + 1);
+    }
+    return;
+  }
+
+  // ---- consumer: C (dV^T += dO^T P, dK^T += Q^T dS) ----
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
     dk[i] = f32x16{};
     dv[i] = f32x16{};
   }
-
-  // ---- the wave's sub-blocks ----
-  // Sub-block n = 2 it + h holds rows 32h .. 32h+31 of the block of iteration
-  // it. A sub-block whose rows are all before the wave's first key (causal),
-  // or all start their document after its last key, or lie past the
-  // sequence, sees none of the wave's keys. In row terms the useful first rows
-  // r (multiples of 32) satisfy c_vis - 31 <= r < r_end; they form one range
-  // of blocks in the walk, whose first and last blocks may have one useless
-  // half per head (those run fully masked and add nothing). n_lo .. n_hi is
-  // that range in the walk. c_kmax / c_dmin decide which sub-blocks need the
-  // element mask.
-  int64_t c_vis = 0, c_kmax = 0, r_end = a.s_q, c_dmin = a.s_q;
-  if (a.causal && wave_has_keys) {
-    c_vis = wave_count<false>(a.q_pos, a.s_q, w_kmin, lane);
-    c_kmax = wave_count<false>(a.q_pos, a.s_q, w_kmax, lane);
-  }
-  if (DOC && wave_has_keys) {
-    r_end = min(r_end, wave_count<true>(a.q_lo, a.s_q, w_kmax, lane));
-    c_dmin = wave_count<true>(a.q_lo, a.s_q, w_kmin, lane);
-  }
-  const int64_t qb_last = qb0 + n_blk - 1;
-  int64_t R_lo = (c_vis - 31 + 31) / 32;  // ceil((c_vis - 31) / 32) for c_vis >= 0
-  if (c_vis < 31) R_lo = 0;
-  int64_t R_hi = (r_end + 31) / 32 - 1;   // last useful 32-row unit
-  R_lo = max(R_lo, 2 * qb0);
-  R_hi = min(R_hi, 2 * qb_last + 1);
-  int n_lo = 0, n_hi = 0;
-  if (wave_has_keys && n_blk > 0 && R_lo <= R_hi) {
-    const int64_t j_first = qb_last - R_hi / 2;          // walk block of the latest unit
-    const int64_t h_min = max<int64_t>(0, R_lo - 2 * (qb_last - j_first));
-    n_lo = static_cast<int>(2 * (j_first * g) + h_min);
-    const int64_t j_last = qb_last - R_lo / 2;           // walk block of the earliest unit
-    const int64_t h_max = min<int64_t>(1, R_hi - 2 * (qb_last - j_last));
-    n_hi = static_cast<int>(2 * (j_last * g + g - 1) + h_max + 1);
-  }
-  const bool any = n_lo < n_hi;
-  const bool w_ragged = w_key0 + KV_KW > a.s_kv;   // some key of the wave past the block
-
-  // ---- software pipeline over sub-blocks ----
-  // One wave per SIMD, so the wave itself must overlap its MFMAs with its
-  // vector work. Iteration n runs one stream of 32 MFMAs, A(n+1) -- S = Q K^T
-  // and dP = dO V^T of the next sub-block -- interleaved with C(n-1) --
-  // dV^T += dO^T P and dK^T += Q^T dS of the previous one -- with operands
-  // read a few MFMAs ahead, and after every MFMA the vector work of B(n): the
-  // probabilities P and dS of one element of this sub-block. Scores, P and dS
-  // are double-buffered by sub-block parity. The element mask (rare: the
-  // diagonal, ragged rows or keys, a document start) is applied to A(n+1)'s
-  // scores right after the stream.
-  // S accumulator: lane holds key `col`; element a holds sub-block row
-  // (a/4)*8 + hi*4 + a%4.
-  f32x16 s[2], dp[2];
-  bf16x8 pb[2][2], dsb[2][2];
-  // P and dS start at zero: the first C of the wave's range (of the
-  // sub-block before it) then adds nothing.
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      pb[i][j] = bf16x8{};
-      dsb[i][j] = bf16x8{};
-    }
-  float4 l4[4], d4[4];  // lse (log2 units) and D of the rows of the sub-block of B
-
-  auto blk_q0 = [&](int it) INLINE -> int64_t { return (qb_last - it / g) * KV_QB; };
-  auto read_ld = [&](auto stage, int rb) INLINE {
-    const float *ll = l_stage(stage) + rb;
-    const float *ee = e_stage(stage) + rb;
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      l4[e4] = *reinterpret_cast<const float4 *>(ll + e4 * 8 + hi * 4);
-      d4[e4] = *reinterpret_cast<const float4 *>(ee + e4 * 8 + hi * 4);
-    }
+  bf16x8 pc[2], dsc[2];  // P and dS of the sub-block in C, per k-step
+  // Operand of C item ci (16-row step ci/8, d block (ci/2)%4; dV from dO^T
+  // when ci is even, dK from Q^T when odd), by the transposing read; t0 / t1 =
+  // stage base + rows + toff0[0 / 1].
+  auto rd_c = [&](uint32_t t0, uint32_t t1, int ci) INLINE -> bf16x8 {
+    const uint32_t x = static_cast<uint32_t>((ci >> 1) & 3) << 6;
+    const uint32_t off = ((ci & 1) ? ST_Q : ST_D) + (ci >> 3) * 16 * ROW_B;
+    const bf16x4 v0 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(smem + (t0 ^ x) + off));
+    const bf16x4 v1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(smem + (t1 ^ x) + off));
+    return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
   };
-  // Two elements (el, el+1) of B: p = 2^(S scale log2 e - lse'),
-  // ds = p (dP - D), converted to bf16 together.
-  auto b_pair = [&](int par, int el) INLINE {
+  auto step = [&](auto par_c, int n) INLINE {
+    constexpr int PAR = decltype(par_c)::value;   // parity of n; C runs on n-1
+    begin_iter(n);
+    if (n - 1 >= n_lo && n - 1 < n_hi) {
+      const unsigned char *x = smem + xch + (1 - PAR) * XG_B;
+      pc[0] = *reinterpret_cast<const bf16x8 *>(x);
+      pc[1] = *reinterpret_cast<const bf16x8 *>(x + 1024);
+      dsc[0] = *reinterpret_cast<const bf16x8 *>(x + 2048);
+      dsc[1] = *reinterpret_cast<const bf16x8 *>(x + 3072);
+      const uint32_t base = stage_b((n - 1) >> 1) + 32 * (1 - PAR) * ROW_B;
+      const uint32_t t0 = base + toff0[0], t1 = base + toff0[1];
+      bf16x8 op[DIST + 1];
 #pragma unroll
-    for (int j = el; j < el + 2; ++j) {
-      const float p = exp2_fast(fmaf(s[par][j], sl2, -l4[j >> 2][j & 3]));
-      pb[par][j >> 3][j & 7] = static_cast<__bf16>(p);
-      dsb[par][j >> 3][j & 7] = static_cast<__bf16>(p * (dp[par][j] - d4[j >> 2][j & 3]));
-    }
-    // Keep the pair here, between the MFMAs: otherwise the compiler sinks all
-    // of B past the stream, where nothing overlaps it.
-    asm volatile("" : "+v"(pb[par][el >> 3]), "+v"(dsb[par][el >> 3]));
-  };
-  // Operand of A item a (k-step a/2; S from the Q rows when a is even, dP from
-  // the dO rows when odd) for the sub-block at rows rb of `stage`.
-  auto rd_a = [&](auto stage, int rb, int ai) INLINE -> bf16x8 {
-    const unsigned char *base = ((ai & 1) ? d_stage(stage) : q_stage(stage)) + rb * ROW_B;
-    return *reinterpret_cast<const bf16x8 *>(base + qoff(ai >> 1));
-  };
-  // Operand of C item c (16-row step c/8, d block (c/2)%4; dV from dO^T when
-  // c is even, dK from Q^T when odd), by the transposing read.
-  auto rd_c = [&](auto stage, int rb, int ci) INLINE -> bf16x8 {
-    const unsigned char *base = (ci & 1) ? q_stage(stage) : d_stage(stage);
-    return tread(base, (ci >> 1) & 3, rb + (ci >> 3) * 16);
-  };
-  // A's MFMAs are written out so that the K and V rows (read-only, the B
-  // operands) sit in AGPRs and S, dP land in VGPRs, where B reads them:
-  // left to itself the compiler keeps K, V in VGPRs and S, dP in AGPRs, and
-  // moves all 32 results out of AGPRs on every sub-block.
-  // Wait states. The hardware does not interlock a VALU read of a VGPR that
-  // an XDL (matrix) instruction writes: the CDNA3 / CDNA4 instruction-set
-  // guides' table of MAI dependencies requires the reader to issue at least
-  // 11 wait states after an 8-pass XDL write (5 / 7 / 11 / 19 for 2 / 4 / 8 /
-  // 16 passes on gfx940; gfx950 adds one), which the compiler's hazard
-  // recognizer inserts for the MFMAs it emits itself. These written-out
-  // MFMAs (32x32x16 bf16: 8 passes) are invisible to it, so every reader of
-  // S and dP keeps the distance by construction:
-  //   * the element mask, the only reader right after an A stream, first
-  //     issues three s_nop 7 (24 wait states, above even the 16-pass need);
-  //   * B reads a sub-block's S and dP in the next iteration's stream, its
-  //     first pair after that stream's fourth MFMA: at least four MFMAs (each
-  //     holding the matrix pipe for 8 passes) have issued after the last A
-  //     write (five after a full stream, four after A alone), far beyond 12
-  //     wait states;
-  //   * nothing else reads s or dp (the empty asm statements that pin them
-  //     emit no instruction).
-  // C's MFMAs are compiler-emitted builtins, so its results (dk, dv) and its
-  // operands written by B are covered by the compiler's own checks.
-  auto mfma_a = [&](int par, int ai, const bf16x8 &o) INLINE {
-    const int ds = ai >> 1;
-    f32x16 &r = (ai & 1) ? dp[par] : s[par];
-    const bf16x8 &b = (ai & 1) ? vreg[ds] : kreg[ds];
-    if (ds == 0)
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(r) : "v"(o), "a"(b));
-    else
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(r) : "v"(o), "a"(b));
-  };
-  auto mfma_c = [&](int par, int ci, const bf16x8 &o) INLINE {
-    const int ks = ci >> 3, db = (ci >> 1) & 3;
-    if (ci & 1)
-      dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, dsb[par][ks], dk[db], 0, 0, 0);
-    else
-      dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, pb[par][ks], dv[db], 0, 0, 0);
-  };
-  constexpr int DIST = 4;  // operand reads ahead of their MFMA
-  // The full stream: A(n+1) on even slots, C(n-1) on odd slots, a pair of B(n)
-  // elements after every fourth MFMA (the lse and D reads at the top of the
-  // iteration land meanwhile).
-  auto stream = [&](auto sa, int rb_a, int pa, auto sc, int rb_c, int pc, int pbp) INLINE {
-    auto rd = [&](int i) INLINE -> bf16x8 {
-      return (i & 1) ? rd_c(sc, rb_c, i >> 1) : rd_a(sa, rb_a, i >> 1);
-    };
-    bf16x8 op[DIST + 1];
+      for (int i = 0; i < DIST; ++i) op[i] = rd_c(t0, t1, i);
 #pragma unroll
-    for (int i = 0; i < DIST; ++i) op[i] = rd(i);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i + DIST < 32) op[(i + DIST) % (DIST + 1)] = rd(i + DIST);
-      if (i & 1)
-        mfma_c(pc, i >> 1, op[i % (DIST + 1)]);
-      else
-        mfma_a(pa, i >> 1, op[i % (DIST + 1)]);
-      if ((i & 3) == 3) b_pair(pbp, 2 * (i >> 2));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // A alone (before the wave's first sub-block) and C alone (after its last).
-  auto a_only = [&](auto sa, int rb_a, int pa) INLINE {
-    bf16x8 op[DIST + 1];
-#pragma unroll
-    for (int i = 0; i < DIST; ++i) op[i] = rd_a(sa, rb_a, i);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i + DIST < 16) op[(i + DIST) % (DIST + 1)] = rd_a(sa, rb_a, i + DIST);
-      mfma_a(pa, i, op[i % (DIST + 1)]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  auto c_only = [&](auto sc, int rb_c, int pc) INLINE {
-    bf16x8 op[DIST + 1];
-#pragma unroll
-    for (int i = 0; i < DIST; ++i) op[i] = rd_c(sc, rb_c, i);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i + DIST < 16) op[(i + DIST) % (DIST + 1)] = rd_c(sc, rb_c, i + DIST);
-      mfma_c(pc, i, op[i % (DIST + 1)]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // Element mask of A's scores (sub-block at rows rb of `stage`, block rows
-  // from q0): rows past the sequence, keys past the block, a query before the
-  // key (causal), or a key before the query's document.
-  auto mask_a = [&](auto stage, int rb, int par, int64_t q0) INLINE {
-    const int64_t qlim = a.s_q - q0 - rb;
-    const int64_t row0 = q0 + rb;
-    const bool need = qlim < KV_SUB || w_ragged || (a.causal && row0 < c_kmax) ||
-                      (DOC && row0 + min<int64_t>(KV_SUB, qlim) - 1 >= c_dmin);
-    if (need) {
-      // 24 wait states after the last written-out A MFMA before the VALU
-      // reads its results (the requirement is set out at mfma_a).
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-      const int32_t *pp = p_stage(stage) + rb;
-      const int32_t *lp = lo_stage(stage) + rb;
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int r0 = e4 * 8 + hi * 4;
-        int4 p4 = int4{INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-        int4 o4 = int4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
-        if (a.causal) p4 = *reinterpret_cast<const int4 *>(pp + r0);
-        if (DOC) o4 = *reinterpret_cast<const int4 *>(lp + r0);
-        const int32_t qp[4] = {p4.x, p4.y, p4.z, p4.w};
-        const int32_t ql[4] = {o4.x, o4.y, o4.z, o4.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool out = (r0 + j >= qlim) | (kpos > qp[j]) | (kpos < ql[j]) | !key_ok;
-          s[par][e4 * 4 + j] = out ? -INFINITY : s[par][e4 * 4 + j];
-        }
+      for (int i = 0; i < 16; ++i) {
+        if (i + DIST < 16) op[(i + DIST) % (DIST + 1)] = rd_c(t0, t1, i + DIST);
+        const int ks = i >> 3, db = (i >> 1) & 3;
+        if (i & 1)
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (DIST + 1)], dsc[ks], dk[db], 0, 0, 0);
+        else
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (DIST + 1)], pc[ks], dv[db], 0, 0, 0);
       }
     }
+    end_iter(n);
   };
-
-  // Wave 0 loads every block's lse and converts it in place to log2 units
-  // (-inf, a query with no key, to +inf so that its probabilities are 0):
-  // block 0 before the first barrier, block it+1 in the second iteration of
-  // block it (it landed at the first one's barrier; the other waves read it
-  // after the second one's).
-  auto prescale_lse = [&](auto stage) INLINE {
-    if (wave == 0) {
-      float *l = l_stage(stage);
-      l[lane] = lse_log2(l[lane]);
-    }
-  };
-
-  using St0 = std::integral_constant<int, 0>;
-  using St1 = std::integral_constant<int, 1>;
-  using St2 = std::integral_constant<int, 2>;
-  // Block it lives in stage it % 3. Blocks 0 and 1 start streaming now; block
-  // it+2 is issued at the barrier of iteration 2 it, once every wave is done
-  // with block it-1 (its C ran in that iteration).
-  if (n_it > 0) issue_blk(0, St0{});
-  if (n_it > 1) issue_blk(1, St1{});
-  // Stage 2 is read (with zero P and dS) by the first iteration's C before any
-  // block lands in it: clear it so that it holds finite values.
-#pragma unroll
-  for (int i = 0; i < KV_TILE_B / (16 * KV_THREADS); ++i) {
-    reinterpret_cast<u32x4 *>(q_lds2)[tid + i * KV_THREADS] = u32x4{0, 0, 0, 0};
-    reinterpret_cast<u32x4 *>(d_lds2)[tid + i * KV_THREADS] = u32x4{0, 0, 0, 0};
-  }
-  wait_own_loads();
-  if (n_it > 0) prescale_lse(St0{});
-  __syncthreads();
-  if (n_lo == 0 && n_hi > 0) {
-    a_only(St0{}, 0, 0);
-    mask_a(St0{}, 0, 0, blk_q0(0));
-  }
-  const int n_sub = 2 * n_it;
-  // Iteration n (n % 6 = K): B on sub-block n, A on n+1, C on n-1.
-  auto step = [&](auto k_c, int n) INLINE {
-    constexpr int K = decltype(k_c)::value;
-    constexpr int H = K % 2;                 // half of its block
-    using SB = std::integral_constant<int, (K / 2) % 3>;         // stage of n's block
-    using SA = std::integral_constant<int, ((K + 1) / 2) % 3>;   // ... of n+1's
-    using SC = std::integral_constant<int, ((K + 5) / 2) % 3>;   // ... of n-1's
-    constexpr int RB = 32 * H, RB_O = 32 * (1 - H);  // rows of n; of n+1 and n-1
-    constexpr int PB = H, PO = 1 - H;                // parity of n; of n+-1
-    const int it = n >> 1;
-    asm volatile("" : "+v"(qoff0), "+v"(toff0[0]), "+v"(toff0[1]));  // pin: see qoff
-    // Inside the range the full stream runs; its A past the range computes
-    // scores nobody reads, and its C before the range adds zero P and dS.
-    if (n >= n_lo && n < n_hi) {
-      read_ld(SB{}, RB);
-      stream(SA{}, RB_O, PO, SC{}, RB_O, PO, PB);
-      if (n + 1 < n_hi) mask_a(SA{}, RB_O, PO, blk_q0((n + 1) >> 1));
-    } else if (n + 1 == n_lo) {
-      a_only(SA{}, RB_O, PO);
-      mask_a(SA{}, RB_O, PO, blk_q0((n + 1) >> 1));
-    } else if (n == n_hi) {
-      c_only(SC{}, RB_O, PO);
-    }
-    if constexpr (H == 0) {
-      wait_own_loads();  // block it+1 has landed
-      __syncthreads();
-      if (it + 2 < n_it) issue_blk(it + 2, SC{});
-    } else {
-      if (it + 1 < n_it) prescale_lse(SA{});
-      __syncthreads();
-    }
-  };
-  for (int n = 0; n < n_sub; n += 6) {
-    step(std::integral_constant<int, 0>{}, n);
-    step(std::integral_constant<int, 1>{}, n + 1);
-    if (n + 2 < n_sub) step(std::integral_constant<int, 2>{}, n + 2);
-    if (n + 3 < n_sub) step(std::integral_constant<int, 3>{}, n + 3);
-    if (n + 4 < n_sub) step(std::integral_constant<int, 4>{}, n + 4);
-    if (n + 5 < n_sub) step(std::integral_constant<int, 5>{}, n + 5);
-  }
-  // C of the last sub-block (its block's stage is still intact).
-  if (n_hi == n_sub && n_lo < n_hi) {
-    const int st = (n_it - 1) % 3;
-    if (st == 0)
-      c_only(St0{}, 32, 1);
-    else if (st == 1)
-      c_only(St1{}, 32, 1);
-    else
-      c_only(St2{}, 32, 1);
+  for (int n = -1; n <= n_sub; n += 2) {
+    step(std::integral_constant<int, 1>{}, n);
+    step(std::integral_constant<int, 0>{}, n + 1);
   }
 
   if (!key_ok || (DOC && !any)) return;
   // Accumulator element e4*4 + j of block dblk holds d = dblk*32 + e4*8 + hi*4 + j.
+  const int64_t krow = (static_cast<int64_t>(bi) * a.s_kv + key) * a.n_kv + kvh;
   const int64_t orow = a.kv_row ? (a.kv_row[key] + bi * a.kv_row_bstride) * a.n_kv + kvh : krow;
   float *krow_out = a.dk + orow * D + hi * 4;
   float *vrow_out = a.dv + orow * D + hi * 4;
@@ -981,13 +933,28 @@ hipError_t launch_bwd_delta(int64_t rows, int32_t d, int32_t esize, const void *
   if (blocks > 256 * 16) blocks = 256 * 16;
   const unsigned nb = static_cast<unsigned>(blocks);
   if (esize == 2 && d == 128)
-    bwd_delta_kernel<uint16_t, 128><<<nb, 256, 0, stream>>>(rows, static_cast<const uint16_t *>(dout), o, delta);
+    bwd_delta_kernel<uint16_t, 128, false><<<nb, 256, 0, stream>>>(
+        rows, static_cast<const uint16_t *>(dout), o, delta, 1, 1, nullptr, nullptr);
   else if (esize == 2 && d == 64)
-    bwd_delta_kernel<uint16_t, 64><<<nb, 256, 0, stream>>>(rows, static_cast<const uint16_t *>(dout), o, delta);
+    bwd_delta_kernel<uint16_t, 64, false><<<nb, 256, 0, stream>>>(
+        rows, static_cast<const uint16_t *>(dout), o, delta, 1, 1, nullptr, nullptr);
   else if (d == 128)
-    bwd_delta_kernel<float, 128><<<nb, 256, 0, stream>>>(rows, static_cast<const float *>(dout), o, delta);
+    bwd_delta_kernel<float, 128, false><<<nb, 256, 0, stream>>>(
+        rows, static_cast<const float *>(dout), o, delta, 1, 1, nullptr, nullptr);
   else
-    bwd_delta_kernel<float, 64><<<nb, 256, 0, stream>>>(rows, static_cast<const float *>(dout), o, delta);
+    bwd_delta_kernel<float, 64, false><<<nb, 256, 0, stream>>>(
+        rows, static_cast<const float *>(dout), o, delta, 1, 1, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(int32_t b, int64_t s, int32_t n_q, const void *dout, const float *o,
+                           const float *lse, float *delta_t, float *lse_t, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(b) * s * n_q;
+  if (rows == 0) return hipSuccess;
+  int64_t blocks = (rows * (D / 8) + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  bwd_delta_kernel<uint16_t, D, true><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(
+      rows, static_cast<const uint16_t *>(dout), o, delta_t, s, n_q, lse, lse_t);
   return hipGetLastError();
 }
 

@@ -36,8 +36,10 @@ struct AttnArgs {
 
 // Arguments of one backward launch (one key block against a query shard):
 // q, dout [b, s_q, n_q, d]; k, v [b, s_kv, n_kv, d]; lse, delta [b, s_q, n_q]
-// (the global lse of the forward and D = dout . o); dq [b, s_q, n_q, d] and
-// dk, dv [b, s_kv, n_kv, d] float32, accumulated into.
+// (the global lse of the forward and D = dout . o) or, with hm, head-major
+// [b, n_q, s_q] with the lse in log2 units (+inf for a query with no visible
+// key); dq [b, s_q, n_q, d] and dk, dv [b, s_kv, n_kv, d] float32,
+// accumulated into.
 struct BwdArgs {
   const void *q;
   const void *k;
@@ -45,6 +47,7 @@ struct BwdArgs {
   const void *dout;
   const float *lse;
   const float *delta;
+  int32_t hm;
   float *dq;
   float *dk;
   float *dv;
@@ -96,6 +99,11 @@ inline bool causally_empty(int32_t kind, int64_t S, int32_t N, int32_t rank, int
 // D = dout . o per row (rows = b * s * n_q, d elements each; esize of dout 2 or 4).
 hipError_t launch_bwd_delta(int64_t rows, int32_t d, int32_t esize, const void *dout,
                             const float *o, float *delta, hipStream_t stream);
+// The backward's per-row arrays, head-major [b, n_q, s]: D = dout . o and the
+// lse in log2 units (+inf for -inf); dout bf16 [b, s, n_q, 128], o, lse as
+// for the forward's outputs.
+hipError_t launch_bwd_prep(int32_t b, int64_t s, int32_t n_q, const void *dout, const float *o,
+                           const float *lse, float *delta_t, float *lse_t, hipStream_t stream);
 // dq, dk, dv += the gradient contributions of one key block (bf16, d = 128).
 hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 // p[0 .. n) = 0 (a kernel, so that callers may capture it in a graph).

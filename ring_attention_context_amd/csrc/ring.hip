@@ -427,8 +427,8 @@ ra_status make_bwd_plan(const ra_ring_desc *r, BwdPlan *p) {
   size_t off = 0;
   p->pos_off = off;
   off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
-  p->delta_off = off;
-  off += align_up(static_cast<size_t>(r->b) * fp.c * r->n_q * sizeof(float));
+  p->delta_off = off;  // D, then the lse in log2 units: head-major [b, n_q, c] each
+  off += align_up(2 * static_cast<size_t>(r->b) * fp.c * r->n_q * sizeof(float));
   p->qlo_off = off;   // the rank's queries' document starts
   off += align_up(static_cast<size_t>(fp.c) * sizeof(int32_t));
   if (p->ring) {
@@ -523,9 +523,11 @@ extern "C" ra_status ra_ring_bwd(const ra_ring_desc *r, const void *q, const voi
   int32_t *pos = reinterpret_cast<int32_t *>(ws + P.pos_off);
   float *delta = reinterpret_cast<float *>(ws + P.delta_off);
   const int64_t rows = static_cast<int64_t>(r->b) * P.c * r->n_q;
+  float *lse_t = delta + rows;
   st = hip_check(ra::launch_positions(r->kind, r->S, r->N, pos, sc), "ra_ring_bwd: positions");
   if (st == RA_OK)
-    st = hip_check(ra::launch_bwd_delta(rows, r->d, 2, dout, o, delta, sc), "ra_ring_bwd: delta");
+    st = hip_check(ra::launch_bwd_prep(r->b, P.c, r->n_q, dout, o, lse, delta, lse_t, sc),
+                   "ra_ring_bwd: delta");
   if (st == RA_OK)
     st = hip_check(ra::launch_fill_zero(dq, rows * r->d, sc), "ra_ring_bwd: zero dq");
   int32_t *qlo = reinterpret_cast<int32_t *>(ws + P.qlo_off);
@@ -551,8 +553,9 @@ extern "C" ra_status ra_ring_bwd(const ra_ring_desc *r, const void *q, const voi
   ra::BwdArgs a{};
   a.q = q;
   a.dout = dout;
-  a.lse = lse;
+  a.lse = lse_t;
   a.delta = delta;
+  a.hm = 1;
   a.dq = dq;
   a.s_q = P.c;
   a.s_kv = P.c;

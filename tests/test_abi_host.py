@@ -237,15 +237,16 @@ def test_backward_argument_errors():
         ra.ra_ring_bwd_workspace_bytes(_ring(flags=ra.RA_RING_UNFUSED_MERGE))
     def align(x):
         return (x + 255) // 256 * 256
-    # positions, D, document starts, and for N > 1 two halves of the travelling
-    # block: K, V (bf16) and dK, dV (float32), one [b, c, n_kv, d] chunk each
+    # positions, D and log2 lse (head-major), document starts, and for N > 1 two
+    # halves of the travelling block: K, V (bf16) and dK, dV (float32), one
+    # [b, c, n_kv, d] chunk each
     r = _ring()
     chunk = r.b * (r.S // r.N) * r.n_kv * r.d
     half = 2 * align(chunk * 2) + 2 * align(chunk * 4)
-    assert ra.ra_ring_bwd_workspace_bytes(r) == (align(1024 * 4) + align(256 * 8 * 4)
+    assert ra.ra_ring_bwd_workspace_bytes(r) == (align(1024 * 4) + align(2 * 256 * 8 * 4)
                                                  + align(256 * 4) + 2 * half)
     r1 = _ring(N=1, S=256, rank=0)
-    assert ra.ra_ring_bwd_workspace_bytes(r1) == (align(256 * 4) + align(256 * 8 * 4)
+    assert ra.ra_ring_bwd_workspace_bytes(r1) == (align(256 * 4) + align(2 * 256 * 8 * 4)
                                                   + align(256 * 4))
 
 
@@ -301,7 +302,7 @@ def test_allgather_bwd_workspace_and_errors():
     def align(x):
         return (x + 255) // 256 * 256
     elems = 1024 * 2 * 128
-    want = (2 * align(1024 * 4) + align(256 * 4) + align(256 * 8 * 4)
+    want = (2 * align(1024 * 4) + align(256 * 4) + align(2 * 256 * 8 * 4)
             + 2 * align(elems * 2) + align(1024 * 4))
     assert ra.ra_allgather_bwd_workspace_bytes(_ring()) == want
     for kw in (dict(dtype=ra.RA_F32), dict(flags=ra.RA_RING_SERIALIZE), dict(S=1002)):
