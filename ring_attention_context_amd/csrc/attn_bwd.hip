@@ -471,7 +471,7 @@ constexpr int KV_KT = KV_GROUPS * KV_KW;     // keys per workgroup
 constexpr int KV_QB = 64;                    // queries per staged block (two 32-row sub-blocks)
 constexpr int KV_SUB = 32;
 constexpr int KV_TILE_B = KV_QB * ROW_B;     // 16 KiB (q or dout rows)
-constexpr int KV_LOADS = KV_TILE_B / (1024 * KV_WAVES);
+constexpr int KV_LOADS = KV_TILE_B / (1024 * KV_GROUPS);  // per consumer wave
 constexpr int KV_NSTAGE = 3;
 // LDS: KV_NSTAGE stages of one query block -- q rows, dout rows and, per row,
 // the lse (log2 units), delta, position and document start -- then the P / dS
@@ -487,7 +487,7 @@ constexpr int STAGE_B = ST_O + KV_QB * 4;
 constexpr int XG_B = 4 * 1024;
 constexpr int XCH = KV_NSTAGE * STAGE_B;
 constexpr int KV_LDS_B = XCH + KV_GROUPS * 2 * XG_B;
-static_assert(KV_LOADS * 1024 * KV_WAVES == KV_TILE_B, "block split over waves");
+static_assert(KV_LOADS * 1024 * KV_GROUPS == KV_TILE_B, "block split over the consumer waves");
 static_assert(STAGE_B % 256 == 0, "stage bases leave the swizzled address bits alone");
 static_assert(KV_LDS_B <= 160 * 1024, "LDS of one workgroup");
 
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   uint32_t goff[KV_LOADS];
 #pragma unroll
   for (int i = 0; i < KV_LOADS; ++i) {
-    const int r = 4 * (wave + KV_WAVES * i) + (lane >> 4);
+    const int r = 4 * (grp + KV_GROUPS * i) + (lane >> 4);
     goff[i] = static_cast<uint32_t>(r * q_row_bytes + (((lane & 15) ^ swz(r & 15)) << 4));
   }
   auto stage_b = [&](int it) INLINE -> uint32_t {
@@ -599,9 +599,10 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     *h = kvh * g + static_cast<int>(it - j * g);
   };
   auto blk_q0 = [&](int it) INLINE -> int64_t { return (qb_last - it / g) * KV_QB; };
-  // A block's loads: KV_LOADS 16-byte loads each of its q and dout rows per
-  // wave; waves 0-3 also stage one per-row array each (lse, delta, positions
-  // when causal, document starts with a document mask).
+  // A block's loads: each consumer wave issues KV_LOADS 16-byte loads each
+  // of its q and dout rows (the consumers wait at the barrier for the
+  // producers anyway); producer waves 0-3 stage one per-row array each (lse,
+  // delta, positions when causal, document starts with a document mask).
   auto issue_blk = [&](int it) INLINE {
     int64_t q0;
     int h;
@@ -613,13 +614,16 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
         make_rsrc(qbytes + rbase * D * 2, (left - 1) * q_row_bytes + D * 2);
     const __amdgpu_buffer_rsrc_t rd =
         make_rsrc(dbytes + rbase * D * 2, (left - 1) * q_row_bytes + D * 2);
+    if (!producer) {
 #pragma unroll
-    for (int i = 0; i < KV_LOADS; ++i) {
-      const uint32_t row_b = sb + 4 * (wave + KV_WAVES * i) * ROW_B;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (LDS_AS void *)(smem + row_b + ST_Q), 16, goff[i],
-                                               0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LDS_AS void *)(smem + row_b + ST_D), 16, goff[i],
-                                               0, 0, 0);
+      for (int i = 0; i < KV_LOADS; ++i) {
+        const uint32_t row_b = sb + 4 * (grp + KV_GROUPS * i) * ROW_B;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (LDS_AS void *)(smem + row_b + ST_Q), 16,
+                                                 goff[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LDS_AS void *)(smem + row_b + ST_D), 16,
+                                                 goff[i], 0, 0, 0);
+      }
+      return;
     }
     // lse and delta of rows q0 + lane of head h: head-major runs (hm), else
     // rows with stride n_q floats; positions and document starts q0 + lane.
