@@ -663,7 +663,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // barrier that ends each iteration publishes the P and dS the producers
   // wrote for the consumers' next iteration.
   auto begin_iter = [&](int n) INLINE {
-    if ((n & 1) && n >= 3 && (n + 3) / 2 < n_it) issue_blk((n + 3) / 2);
+    if (producer && (n & 1) && n >= 3 && (n + 3) / 2 < n_it) issue_blk((n + 3) / 2);
     if ((n & 1) && (n + 1) / 2 < n_it) prescale_lse((n + 1) / 2);
   };
   auto end_iter = [&](int n) INLINE {
@@ -844,6 +844,34 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
   bf16x8 pc[2], dsc[2];  // P and dS of the sub-block in C, per k-step
+  // The q and dout rows of block j+3, loaded into registers at the start of
+  // iteration 2j+3 and written to its stage at the end of 2j+4.
+  u32x4 stg[2 * KV_LOADS];
+  auto stg_load = [&](int it) INLINE {
+    int64_t q0;
+    int h;
+    blk_of(it, &q0, &h);
+    const int64_t left = a.s_q - q0;
+    const int64_t rbase = (static_cast<int64_t>(bi) * a.s_q + q0) * a.n_q + h;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(qbytes + rbase * D * 2, (left - 1) * q_row_bytes + D * 2);
+    const __amdgpu_buffer_rsrc_t rd =
+        make_rsrc(dbytes + rbase * D * 2, (left - 1) * q_row_bytes + D * 2);
+#pragma unroll
+    for (int i = 0; i < KV_LOADS; ++i) {
+      stg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, goff[i], 0, 0));
+      stg[KV_LOADS + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, goff[i], 0, 0));
+    }
+  };
+  auto stg_write = [&](int it) INLINE {
+    const uint32_t sb = stage_b(it);
+#pragma unroll
+    for (int i = 0; i < KV_LOADS; ++i) {
+      const uint32_t row_b = sb + 4 * (grp + KV_GROUPS * i) * ROW_B + lane * 16;
+      *reinterpret_cast<u32x4 *>(smem + row_b + ST_Q) = stg[i];
+      *reinterpret_cast<u32x4 *>(smem + row_b + ST_D) = stg[KV_LOADS + i];
+    }
+  };
   // Operand of C item ci (16-row step ci/8, d block (ci/2)%4; dV from dO^T
   // when ci is even, dK from Q^T when odd), by the transposing read; t0 / t1 =
   // stage base + rows + toff0[0 / 1].
@@ -858,7 +886,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   };
   auto step = [&](auto par_c, int n) INLINE {
     constexpr int PAR = decltype(par_c)::value;   // parity of n; C runs on n-1
-    begin_iter(n);
+    if (PAR == 1 && n >= 3 && (n + 3) / 2 < n_it) stg_load((n + 3) / 2);
     if (n - 1 >= n_lo && n - 1 < n_hi) {
       const unsigned char *x = smem + xch + (1 - PAR) * XG_B;
       pc[0] = *reinterpret_cast<const bf16x8 *>(x);
@@ -879,6 +907,10 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
         else
           dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (DIST + 1)], pc[ks], dv[db], 0, 0, 0);
       }
+    }
+    if (PAR == 0 && n >= 4 && (n + 2) / 2 < n_it) {
+      wait_own_loads();
+      stg_write((n + 2) / 2);
     }
     end_iter(n);
   };
