@@ -656,12 +656,14 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   };
   // Iteration n (from -1 to n_sub): the producer runs A on sub-block n+1 and
   // B on n, the consumer C on n-1. Block j+3 goes into the stage of block j,
-  // whose last C ran in iteration 2j+2: its loads are issued at the start of
-  // iteration 2j+3 and have landed by the barrier that ends iteration 2j+4
-  // (every even iteration waits for the loads in flight); wave 0 converts its
-  // lse in iteration 2j+5, before B of its first sub-block in 2j+6. The
-  // barrier that ends each iteration publishes the P and dS the producers
-  // wrote for the consumers' next iteration.
+  // whose last C ran in iteration 2j+2: the producers' per-row loads are
+  // issued at the start of iteration 2j+3, the consumers' q / dout rows at its
+  // end (into registers, written to the stage at the end of 2j+4), and all
+  // have landed by the barrier that ends iteration 2j+4 (every even iteration
+  // waits for the loads in flight); wave 0 converts its lse in iteration
+  // 2j+5, before B of its first sub-block in 2j+6. The barrier that ends each
+  // iteration publishes the P and dS the producers wrote for the consumers'
+  // next iteration.
   auto begin_iter = [&](int n) INLINE {
     if (producer && (n & 1) && n >= 3 && (n + 3) / 2 < n_it) issue_blk((n + 3) / 2);
     if ((n & 1) && (n + 1) / 2 < n_it) prescale_lse((n + 1) / 2);
@@ -844,8 +846,9 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
   bf16x8 pc[2], dsc[2];  // P and dS of the sub-block in C, per k-step
-  // The q and dout rows of block j+3, loaded into registers at the start of
-  // iteration 2j+3 and written to its stage at the end of 2j+4.
+  // The q and dout rows of block j+3, loaded into registers at the end of
+  // iteration 2j+3 (after its C, where the consumer would wait at the
+  // barrier) and written to its stage at the end of 2j+4.
   u32x4 stg[2 * KV_LOADS];
   auto stg_load = [&](int it) INLINE {
     int64_t q0;
@@ -886,7 +889,6 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   };
   auto step = [&](auto par_c, int n) INLINE {
     constexpr int PAR = decltype(par_c)::value;   // parity of n; C runs on n-1
-    if (PAR == 1 && n >= 3 && (n + 3) / 2 < n_it) stg_load((n + 3) / 2);
     if (n - 1 >= n_lo && n - 1 < n_hi) {
       const unsigned char *x = smem + xch + (1 - PAR) * XG_B;
       pc[0] = *reinterpret_cast<const bf16x8 *>(x);
@@ -912,6 +914,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
       wait_own_loads();
       stg_write((n + 2) / 2);
     }
+    if (PAR == 1 && n >= 3 && (n + 3) / 2 < n_it) stg_load((n + 3) / 2);
     end_iter(n);
   };
   for (int n = -1; n <= n_sub; n += 2) {
