@@ -159,6 +159,13 @@ ra_status ra_lse_merge(int64_t rows, int32_t d, float *o, float *lse, const floa
 #define RA_RING_UNFUSED_MERGE 2  /* write (o_b, lse_b) to the workspace and
                                     merge with ra_lse_merge's kernel, instead
                                     of merging in the attention epilogue     */
+#define RA_RING_OVERLAP 4        /* ra_ring_fwd: run the copies on `copy` also
+                                    for chunks of at most
+                                    RA_RING_SERIAL_CHUNK_BYTES                */
+/* ra_ring_fwd runs the copies of K chunks up to this size on `compute` unless
+ * RA_RING_OVERLAP is set: between two short steps the wait for the other
+ * stream costs more than the copy itself. */
+#define RA_RING_SERIAL_CHUNK_BYTES ((size_t)16 << 20)
 
 typedef struct ra_ring_desc {
   int32_t b, n_q, n_kv, d;  /* as in ra_attn_desc                            */
@@ -202,7 +209,10 @@ ra_status ra_ring_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
  *           copy stream), including the rank's own chunk before step 0.
  * Step r computes the block of chunk (rank - r) mod N; the copy of the next
  * step's chunk into the idle half of the double buffer runs on `copy` while
- * step r computes on `compute` (or on `compute` with RA_RING_SERIALIZE).
+ * step r computes on `compute` (on `compute` with RA_RING_SERIALIZE, when
+ * copy == compute, or when a K chunk is at most RA_RING_SERIAL_CHUNK_BYTES
+ * and RA_RING_OVERLAP is not set; RA_RING_SERIALIZE with RA_RING_OVERLAP is
+ * RA_ERR_INVALID_ARG).
  * A causal step whose block no query of the rank can see (with the
  * contiguous map, every later rank's chunk) launches no kernel: merging its
  * statistics would be the identity. Its chunk still arrives on `copy`, as the

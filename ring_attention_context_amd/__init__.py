@@ -19,6 +19,8 @@ from ._lib import (  # noqa: F401
     RA_PART_CONTIGUOUS,
     RA_PART_STRIPED,
     RA_PART_ZIGZAG,
+    RA_RING_OVERLAP,
+    RA_RING_SERIAL_CHUNK_BYTES,
     RA_RING_SERIALIZE,
     RA_RING_UNFUSED_MERGE,
     RA_V_ROWS,

@@ -98,13 +98,16 @@ namespace {
 ra_status make_plan(const ra_ring_desc *r, Plan *p) {
   ra_status st = check_ring_desc(r);
   if (st != RA_OK) return st;
-  if (r->flags & ~(RA_RING_SERIALIZE | RA_RING_UNFUSED_MERGE))
+  if (r->flags & ~(RA_RING_SERIALIZE | RA_RING_UNFUSED_MERGE | RA_RING_OVERLAP))
     return fail(RA_ERR_INVALID_ARG, "ring: unknown flag bits 0x%x", r->flags);
+  if ((r->flags & RA_RING_SERIALIZE) && (r->flags & RA_RING_OVERLAP))
+    return fail(RA_ERR_INVALID_ARG, "ring: RA_RING_SERIALIZE and RA_RING_OVERLAP both set");
   p->c = r->S / r->N;
   p->esize = r->dtype == RA_BF16 ? 2 : 4;
   p->chunk_bytes = static_cast<size_t>(r->b) * p->c * r->n_kv * r->d * p->esize;
   p->fused = !(r->flags & RA_RING_UNFUSED_MERGE);
-  p->serialize = (r->flags & RA_RING_SERIALIZE) != 0;
+  p->serialize = (r->flags & RA_RING_SERIALIZE) != 0 ||
+                 (!(r->flags & RA_RING_OVERLAP) && p->chunk_bytes <= RA_RING_SERIAL_CHUNK_BYTES);
   p->vt = r->dtype == RA_BF16 && p->c % 8 == 0 && p->c > 0 &&
           static_cast<int64_t>(r->b) * r->n_kv <= 65535;
   size_t off = 0;

@@ -112,11 +112,14 @@ def _flag_case(dtype="bf16"):
 
 
 def test_overlap_equals_serialized_bitwise():
-    """Same kernels in the same order: any difference would be a copy/compute race."""
+    """Same kernels in the same order: any difference would be a copy/compute race.
+    The chunks here are small, so the default runs the copies on `compute` too."""
     w, inp, dev = _flag_case()
-    _, o1, l1 = run_ring(w, *dev)
+    _, o1, l1 = run_ring(w, *dev, flags=ra.RA_RING_OVERLAP)
     _, o2, l2 = run_ring(w, *dev, flags=ra.RA_RING_SERIALIZE)
+    _, o3, l3 = run_ring(w, *dev)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
 
 
 def test_poisoned_workspace_and_outputs():
