@@ -122,6 +122,33 @@ def test_overlap_equals_serialized_bitwise():
     assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
 
 
+@pytest.mark.parametrize("flags", [ra.RA_RING_OVERLAP, 0])
+def test_graph_replay_matches_eager(flags):
+    """One ra_ring_fwd call captured as a HIP graph (the copy stream joining
+    the capture when the copies overlap) and replayed three times, with eager
+    work and synchronisations between the replays and the outputs poisoned
+    before each: every replay equals the eager call bit for bit."""
+    w, inp, dev = _flag_case()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        call = runner.RingCall(*dev, kind=w.kind, S=w.S, N=w.N, rank=w.rank, causal=w.causal,
+                               scale=w.scale, flags=flags, compute=side)
+        o_ref, l_ref = (t.clone() for t in call())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call()
+    torch.cuda.synchronize()
+    for i in range(3):
+        call.o.fill_(float("nan"))
+        call.lse.fill_(float("nan"))
+        eager = run_ring(w, *dev)            # other eager work between the replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.o, o_ref) and torch.equal(call.lse, l_ref), i
+        assert np.array_equal(eager[1], o_ref.cpu().numpy())
+
+
 def test_poisoned_workspace_and_outputs():
     """NaN-filled workspace and outputs: a read before its write would surface as NaN."""
     w, inp, dev = _flag_case()
