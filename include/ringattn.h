@@ -162,6 +162,9 @@ ra_status ra_lse_merge(int64_t rows, int32_t d, float *o, float *lse, const floa
 #define RA_RING_OVERLAP 4        /* ra_ring_fwd: run the copies on `copy` also
                                     for chunks of at most
                                     RA_RING_SERIAL_CHUNK_BYTES                */
+#define RA_RING_STEPWISE 8       /* ra_ring_fwd: one attention launch per step
+                                    also when the copies run on `compute`
+                                    (see ra_ring_fwd)                        */
 /* ra_ring_fwd runs the copies of K chunks up to this size on `compute` unless
  * RA_RING_OVERLAP is set: between two short steps the wait for the other
  * stream costs more than the copy itself. */
@@ -213,6 +216,13 @@ ra_status ra_ring_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
  * copy == compute, or when a K chunk is at most RA_RING_SERIAL_CHUNK_BYTES
  * and RA_RING_OVERLAP is not set; RA_RING_SERIALIZE with RA_RING_OVERLAP is
  * RA_ERR_INVALID_ARG).
+ * When the copies run on `compute` (bf16 with V staged transposed, merge
+ * fused, no document mask, RA_RING_STEPWISE not set), two consecutive steps
+ * whose blocks the rank can see share one attention launch: the kernel scans
+ * the keys of both blocks in one online softmax (§3: the same identity
+ * applied within one GPU) and merges into (o, lse) once. The result equals
+ * the stepwise one up to rounding (the order in which the two blocks'
+ * statistics combine); both steps' events are recorded after that launch.
  * A causal step whose block no query of the rank can see (with the
  * contiguous map, every later rank's chunk) launches no kernel: merging its
  * statistics would be the identity. Its chunk still arrives on `copy`, as the

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     RA_RING_OVERLAP,
     RA_RING_SERIAL_CHUNK_BYTES,
     RA_RING_SERIALIZE,
+    RA_RING_STEPWISE,
     RA_RING_UNFUSED_MERGE,
     RA_V_ROWS,
     RA_V_TRANSPOSED,

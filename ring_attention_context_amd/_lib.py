@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("RINGATTN_LIB", os.path.join(_PKG, "libringattn.so"))
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, 1, 2, 3
 RA_PART_CONTIGUOUS, RA_PART_ZIGZAG, RA_PART_STRIPED = 0, 1, 2
 RA_F32, RA_BF16 = 0, 1
-RA_RING_SERIALIZE, RA_RING_UNFUSED_MERGE, RA_RING_OVERLAP = 1, 2, 4
+RA_RING_SERIALIZE, RA_RING_UNFUSED_MERGE, RA_RING_OVERLAP, RA_RING_STEPWISE = 1, 2, 4, 8
 RA_RING_SERIAL_CHUNK_BYTES = 16 << 20
 RA_V_ROWS, RA_V_TRANSPOSED = 0, 1
 

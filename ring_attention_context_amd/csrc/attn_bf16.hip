@@ -187,7 +187,10 @@ __device__ __forceinline__ void barrier_keep_loads() {
 
 // DOC: a document mask is given (a.q_lo); without it the mask code compiles away.
 // NEAR: the launcher has checked that every offset of the key range fits in 31 bits.
-template <int HW, bool VT, bool DOC, bool NEAR>
+// PAIR: a second key block (a.k2, a.v2, a.kv_pos2, same length) follows the
+// first: its tiles come after the first block's in the same scan, so the
+// statistics of both blocks form in one pass and are merged (or written) once.
+template <int HW, bool VT, bool DOC, bool NEAR, bool PAIR>
 __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // One LDS object per stage and operand (the key positions of a tile sit
   // after its K rows): the compiler then sees that the asynchronous loads into
@@ -245,12 +248,13 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // and the tile tests below never skip.
   // With a document mask the range starts at the tile holding the first key
   // of the first query's document (document starts are non-decreasing).
-  int64_t nkeys = a.s_kv;
+  int64_t nkeys = a.s_kv, nkeys2 = PAIR ? a.s_kv : 0;
   int64_t kbeg = 0;
   int32_t w_qmin = INT_MAX - 1, w_qmax = INT_MAX - 1;
   int32_t w_lomax = INT_MIN;  // latest document start among the wave's queries
   if (a.causal) {
     nkeys = wave_count<true>(a.kv_pos, a.s_kv, a.q_pos[wg_tok_last], lane);
+    if (PAIR) nkeys2 = wave_count<true>(a.kv_pos2, a.s_kv, a.q_pos[wg_tok_last], lane);
     if (DOC) kbeg = wave_count<false>(a.kv_pos, a.s_kv, a.q_lo[wg_tok0], lane) / BK * BK;
     if (wave_has_rows) {
       w_qmin = a.q_pos[w_tok0];
@@ -258,7 +262,10 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
       if (DOC) w_lomax = a.q_lo[w_tok_last];
     }
   }
-  const int nt = nkeys > kbeg ? static_cast<int>((nkeys - kbeg + BK - 1) / BK) : 0;
+  // nt1 tiles of the first block, then (PAIR) nt2 of the second.
+  const int nt1 = nkeys > kbeg ? static_cast<int>((nkeys - kbeg + BK - 1) / BK) : 0;
+  const int nt2 = PAIR ? static_cast<int>((nkeys2 + BK - 1) / BK) : 0;
+  const int nt = nt1 + nt2;
   // Merging a block that no query of the workgroup can see leaves (o, lse) as
   // they are (its statistics are the merge identity): nothing to load or write.
   // nt is the same for every wave, so the whole workgroup leaves together.
@@ -268,15 +275,26 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // a key after its first query, and tiles before j_doc a key before its
   // latest document start. Those (and a ragged last tile) take the element
   // mask.
+  // PAIR: the wave's own range ends w_nt1 tiles into the first block (tiles
+  // w_nt1 .. nt1-1 of the first block are masked whole for it) and w_nt2
+  // tiles into the second, whose diagonal starts at tile j_diag2.
   int w_nt = nt, j_diag = INT_MAX, j_doc = 0;
+  int w_nt1 = nt1, j_diag2 = INT_MAX;
   if (a.causal && wave_has_rows) {
     const int64_t c_hi = wave_count<true>(a.kv_pos, a.s_kv, w_qmax, lane);
-    w_nt = c_hi > kbeg ? min(nt, static_cast<int>((c_hi - kbeg + BK - 1) / BK)) : 0;
+    w_nt1 = c_hi > kbeg ? min(nt1, static_cast<int>((c_hi - kbeg + BK - 1) / BK)) : 0;
+    w_nt = w_nt1;
     const int64_t c_lo = wave_count<true>(a.kv_pos, a.s_kv, w_qmin, lane);
     j_diag = c_lo > kbeg ? static_cast<int>((c_lo - kbeg) / BK) : 0;
     if (DOC) {
       const int64_t c_d = wave_count<false>(a.kv_pos, a.s_kv, w_lomax, lane);
       j_doc = c_d > kbeg ? static_cast<int>((c_d - kbeg + BK - 1) / BK) : 0;
+    }
+    if (PAIR) {
+      const int64_t c_hi2 = wave_count<true>(a.kv_pos2, a.s_kv, w_qmax, lane);
+      const int w_nt2 = min(nt2, static_cast<int>((c_hi2 + BK - 1) / BK));
+      if (w_nt2 > 0) w_nt = nt1 + w_nt2;
+      j_diag2 = static_cast<int>(wave_count<true>(a.kv_pos2, a.s_kv, w_qmin, lane) / BK);
     }
   }
 
@@ -365,30 +383,47 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
          : make_rsrc(vg + kv_base + kbeg * kv_row_bytes,
                      rows_left > 0 ? (rows_left - 1) * kv_row_bytes + D * 2 : 0);
   const __amdgpu_buffer_rsrc_t rp_all = make_rsrc(a.kv_pos + kbeg, rows_left * 4);
+  // PAIR: the second block's descriptors (the key range starts at 0 there).
+  const unsigned char *kg2 = static_cast<const unsigned char *>(a.k2);
+  const unsigned char *vg2 = static_cast<const unsigned char *>(a.v2);
+  const int64_t all2 = PAIR ? a.s_kv : 0;
+  const __amdgpu_buffer_rsrc_t rk_all2 =
+      make_rsrc(PAIR ? kg2 + kv_base : kg, all2 > 0 ? (all2 - 1) * kv_row_bytes + D * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rv_all2 =
+      make_rsrc(PAIR ? vg2 + vt_base : vg, all2 > 0 ? (D - 1) * vt_stride + all2 * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rp_all2 = make_rsrc(PAIR ? a.kv_pos2 : a.kv_pos, all2 * 4);
+  // Tile t of the scan: the block it lies in (second when t >= nt1) and its
+  // index there. Tiles past the scan fall past the second block's end.
+  auto second = [&](int t) INLINE -> bool { return PAIR && t >= nt1; };
+  auto local = [&](int t) INLINE -> int { return second(t) ? t - nt1 : t; };
   const uint32_t k_tile_b = static_cast<uint32_t>(BK * kv_row_bytes);
   auto issue_k = [&](int t, auto stage) INLINE {
     if constexpr (NEAR) {
-      const uint32_t toff = static_cast<uint32_t>(t) * k_tile_b;
+      const bool sb = second(t);
+      const uint32_t lt = static_cast<uint32_t>(local(t));
+      const uint32_t toff = lt * k_tile_b;
+      const __amdgpu_buffer_rsrc_t rk = sb ? rk_all2 : rk_all;
 #pragma unroll
       for (int i = 0; i < LOADS_PER_WAVE; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk_all, (LDS_AS void *)(k_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16,
+            rk, (LDS_AS void *)(k_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16,
             goff[i] + toff, 0, 0, 0);
       if (a.causal && wave == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_all, (LDS_AS void *)p_stage(stage), 4,
-                                                 lane * 4 + static_cast<uint32_t>(t) * (BK * 4), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sb ? rp_all2 : rp_all, (LDS_AS void *)p_stage(stage), 4,
+                                                 lane * 4 + lt * (BK * 4), 0, 0, 0);
       return;
     }
-    const int64_t key0 = kbeg + static_cast<int64_t>(t) * BK;
+    const bool sb = second(t);
+    const int64_t key0 = (sb ? 0 : kbeg) + static_cast<int64_t>(local(t)) * BK;
     const int64_t left = a.s_kv - key0;  // rows before the end of the block
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + kv_base + key0 * kv_row_bytes,
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((sb ? kg2 : kg) + kv_base + key0 * kv_row_bytes,
                                                 (left - 1) * kv_row_bytes + D * 2);
 #pragma unroll
     for (int i = 0; i < LOADS_PER_WAVE; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rk, (LDS_AS void *)(k_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16, goff[i], 0, 0, 0);
     if (a.causal && wave == 0) {
-      const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.kv_pos + key0, left * 4);
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc((sb ? a.kv_pos2 : a.kv_pos) + key0, left * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (LDS_AS void *)p_stage(stage), 4, lane * 4,
                                                0, 0, 0);
     }
@@ -396,27 +431,31 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // V (or V^T) of tile t into V stage `stage`: LOADS_PER_WAVE loads per wave.
   auto issue_v = [&](int t, auto stage) INLINE {
     if constexpr (NEAR) {
+      const uint32_t lt = static_cast<uint32_t>(local(t));
+      const __amdgpu_buffer_rsrc_t rv = second(t) ? rv_all2 : rv_all;
 #pragma unroll
       for (int i = 0; i < LOADS_PER_WAVE; ++i) {
         if constexpr (VT)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rv_all, (LDS_AS void *)(v_stage(stage) + (wave + WAVES * i) * 1024), 16,
-              vgoff[i] + static_cast<uint32_t>(t) * (BK * 2), 0, 0, 0);
+              rv, (LDS_AS void *)(v_stage(stage) + (wave + WAVES * i) * 1024), 16,
+              vgoff[i] + lt * (BK * 2), 0, 0, 0);
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rv_all, (LDS_AS void *)(v_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16,
-              goff[i] + static_cast<uint32_t>(t) * k_tile_b, 0, 0, 0);
+              rv, (LDS_AS void *)(v_stage(stage) + 4 * (wave + WAVES * i) * ROW_B), 16,
+              goff[i] + lt * k_tile_b, 0, 0, 0);
       }
       return;
     }
-    const int64_t key0 = kbeg + static_cast<int64_t>(t) * BK;
+    const bool sb = second(t);
+    const int64_t key0 = (sb ? 0 : kbeg) + static_cast<int64_t>(local(t)) * BK;
     const int64_t left = a.s_kv - key0;
+    const unsigned char *vgb = sb ? vg2 : vg;
     // V^T: keys past the block in a d-row read the next d-row's first keys
     // (finite values that meet a zero probability) or, for the last row,
     // zeros from the bounds check.
     const __amdgpu_buffer_rsrc_t rv =
-        VT ? make_rsrc(vg + vt_base + key0 * 2, (D - 1) * vt_stride + left * 2)
-           : make_rsrc(vg + kv_base + key0 * kv_row_bytes, (left - 1) * kv_row_bytes + D * 2);
+        VT ? make_rsrc(vgb + vt_base + key0 * 2, (D - 1) * vt_stride + left * 2)
+           : make_rsrc(vgb + kv_base + key0 * kv_row_bytes, (left - 1) * kv_row_bytes + D * 2);
 #pragma unroll
     for (int i = 0; i < LOADS_PER_WAVE; ++i) {
       if constexpr (VT)
@@ -464,12 +503,16 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // wave's diagonal, starts before a query's document, or is the ragged last
   // tile. Accumulator element e4*4 + j of key block kb holds key kk + j.
   auto mask = [&](int t, auto stage) INLINE {
-    const int64_t key0 = kbeg + static_cast<int64_t>(t) * BK;
+    const bool sb = second(t);
+    const int lt = local(t);
+    const int64_t key0 = (sb ? 0 : kbeg) + static_cast<int64_t>(lt) * BK;
     const bool ragged = key0 + BK > a.s_kv;
-    if (ragged || t >= j_diag || (DOC && t < j_doc)) {
+    // PAIR: a first-block tile past the wave's own range is masked whole.
+    const bool dead = PAIR && !sb && t >= w_nt1;
+    if (ragged || dead || lt >= (sb ? j_diag2 : j_diag) || (DOC && t < j_doc)) {
       // Branch-free selects: key index past the block, position after the
       // query, or before the query's document.
-      const int lim = ragged ? static_cast<int>(a.s_kv - key0) : BK;
+      const int lim = dead ? 0 : ragged ? static_cast<int>(a.s_kv - key0) : BK;
       const int32_t *pp = p_stage(stage);
       const int32_t qp = a.causal ? qpos : INT_MAX;
 #pragma unroll
@@ -757,16 +800,28 @@ hipError_t launch_hw(const AttnArgs &a, hipStream_t stream) {
   const bool near = rows * kv_row_bytes < (int64_t{1} << 31) &&
                     (D - 1) * a.s_kv * 2 + rows * 2 < (int64_t{1} << 31);
   const unsigned grid = static_cast<unsigned>(blocks);
+  if (a.k2) {
+    // Two key blocks in one scan (V^T, no document mask; checked by the caller).
+    if constexpr (VT) {
+      if (near)
+        attn_bf16_kernel<HW, true, false, true, true><<<grid, THREADS, 0, stream>>>(a);
+      else
+        attn_bf16_kernel<HW, true, false, false, true><<<grid, THREADS, 0, stream>>>(a);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (a.q_lo) {
     if (near)
-      attn_bf16_kernel<HW, VT, true, true><<<grid, THREADS, 0, stream>>>(a);
+      attn_bf16_kernel<HW, VT, true, true, false><<<grid, THREADS, 0, stream>>>(a);
     else
-      attn_bf16_kernel<HW, VT, true, false><<<grid, THREADS, 0, stream>>>(a);
+      attn_bf16_kernel<HW, VT, true, false, false><<<grid, THREADS, 0, stream>>>(a);
   } else {
     if (near)
-      attn_bf16_kernel<HW, VT, false, true><<<grid, THREADS, 0, stream>>>(a);
+      attn_bf16_kernel<HW, VT, false, true, false><<<grid, THREADS, 0, stream>>>(a);
     else
-      attn_bf16_kernel<HW, VT, false, false><<<grid, THREADS, 0, stream>>>(a);
+      attn_bf16_kernel<HW, VT, false, false, false><<<grid, THREADS, 0, stream>>>(a);
   }
   return hipGetLastError();
 }

@@ -32,6 +32,11 @@ struct AttnArgs {
   int32_t merge;
   int32_t v_layout;  // ra_v_layout of v (RA_V_TRANSPOSED: [b, n_kv, d, s_kv], bf16 only)
   const int32_t *q_lo;  // optional [s_q]: first visible key position (document start)
+  // optional second key block of s_kv keys (bf16, V^T, no q_lo): scanned after
+  // the first, so one launch covers both blocks (one merge into o / lse)
+  const void *k2;
+  const void *v2;
+  const int32_t *kv_pos2;
 };
 
 // Arguments of one backward launch (one key block against a query shard):
@@ -116,8 +121,13 @@ hipError_t launch_v_transpose(int32_t b, int64_t s, int32_t n_kv, int32_t d, int
                               const void *v, void *vt, hipStream_t stream);
 // bf16 rows -> V^T [b, n_kv, d, s] with 16-byte accesses (s % 8 == 0, d % 8 == 0):
 // position p of batch bi is row (src_row ? src_row[p] : p) + bi * bstride of src.
+// With k_bytes > 0 the same launch also copies k_bytes (16-byte aligned, a
+// multiple of 16, at most b * s * n_kv * d * 2 rounded up to whole tiles)
+// from k_src to k_dst.
 hipError_t launch_rows_to_vt(const void *src, void *vt, const int32_t *src_row, int64_t bstride,
-                             int32_t b, int64_t s, int32_t n_kv, int32_t d, hipStream_t stream);
+                             int32_t b, int64_t s, int32_t n_kv, int32_t d, hipStream_t stream,
+                             const void *k_src = nullptr, void *k_dst = nullptr,
+                             size_t k_bytes = 0);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -59,6 +59,7 @@ struct Plan {
   size_t pos_off = 0, qlo_off = 0, kv_off[2] = {0, 0}, ob_off = 0, lseb_off = 0, total = 0;
   bool fused = true, serialize = false;
   bool vt = false;          // V chunks staged transposed (bf16, c % 8 == 0)
+  bool pairable = false;    // serialized steps may run two blocks per launch
 };
 
 }  // namespace
@@ -98,7 +99,7 @@ namespace {
 ra_status make_plan(const ra_ring_desc *r, Plan *p) {
   ra_status st = check_ring_desc(r);
   if (st != RA_OK) return st;
-  if (r->flags & ~(RA_RING_SERIALIZE | RA_RING_UNFUSED_MERGE | RA_RING_OVERLAP))
+  if (r->flags & ~(RA_RING_SERIALIZE | RA_RING_UNFUSED_MERGE | RA_RING_OVERLAP | RA_RING_STEPWISE))
     return fail(RA_ERR_INVALID_ARG, "ring: unknown flag bits 0x%x", r->flags);
   if ((r->flags & RA_RING_SERIALIZE) && (r->flags & RA_RING_OVERLAP))
     return fail(RA_ERR_INVALID_ARG, "ring: RA_RING_SERIALIZE and RA_RING_OVERLAP both set");
@@ -110,6 +111,7 @@ ra_status make_plan(const ra_ring_desc *r, Plan *p) {
                  (!(r->flags & RA_RING_OVERLAP) && p->chunk_bytes <= RA_RING_SERIAL_CHUNK_BYTES);
   p->vt = r->dtype == RA_BF16 && p->c % 8 == 0 && p->c > 0 &&
           static_cast<int64_t>(r->b) * r->n_kv <= 65535;
+  p->pairable = p->vt && p->fused && !r->doc_start && !(r->flags & RA_RING_STEPWISE);
   size_t off = 0;
   p->pos_off = off;
   off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));
@@ -235,6 +237,10 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
   hipStream_t sc = static_cast<hipStream_t>(compute);
   hipStream_t sp = static_cast<hipStream_t>(copy);
   const bool serialize = P.serialize || sp == sc;
+  // With the copies on `compute`, two consecutive visible steps share one
+  // launch (both blocks in one scan, one merge): at small chunks a launch's
+  // prologue and its o / lse merge cost a fifth of the step.
+  const bool pair = serialize && P.pairable;
   hipEvent_t *step_ev = reinterpret_cast<hipEvent_t *>(r->step_events);
   if (empty) {
     if (step_ev)
@@ -304,16 +310,19 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
     ra_status s2 = RA_OK;
     if (!serialize && step >= 2 && uses_buf(step - 2))
       s2 = hip_check(hipStreamWaitEvent(sp, ev->freed[buf], 0), "ra_ring_fwd: wait freed");
-    if (s2 == RA_OK && step >= 1)
-      s2 = hip_check(hipMemcpyAsync(kbuf[buf], kc + static_cast<size_t>(src) * CB, CB,
-                                    hipMemcpyDeviceToDevice, cs),
-                     "ra_ring_fwd: K copy");
-    if (s2 == RA_OK) {
-      if (P.vt)
-        s2 = hip_check(ra::launch_v_transpose(r->b, P.c, r->n_kv, r->d, 2,
-                                              vc + static_cast<size_t>(src) * CB, vbuf[buf], cs),
-                       "ra_ring_fwd: V transpose");
-      else
+    if (s2 == RA_OK && P.vt) {
+      // V transposed and (from step 1 on) K copied by one launch.
+      s2 = hip_check(ra::launch_rows_to_vt(vc + static_cast<size_t>(src) * CB, vbuf[buf], nullptr,
+                                           P.c, r->b, P.c, r->n_kv, r->d, cs,
+                                           kc + static_cast<size_t>(src) * CB, kbuf[buf],
+                                           step >= 1 ? CB : 0),
+                     "ra_ring_fwd: K copy and V transpose");
+    } else if (s2 == RA_OK) {
+      if (step >= 1)
+        s2 = hip_check(hipMemcpyAsync(kbuf[buf], kc + static_cast<size_t>(src) * CB, CB,
+                                      hipMemcpyDeviceToDevice, cs),
+                       "ra_ring_fwd: K copy");
+      if (s2 == RA_OK)
         s2 = hip_check(hipMemcpyAsync(vbuf[buf], vc + static_cast<size_t>(src) * CB, CB,
                                       hipMemcpyDeviceToDevice, cs),
                        "ra_ring_fwd: V copy");
@@ -328,21 +337,60 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
   }
   a.v_layout = P.vt ? RA_V_TRANSPOSED : RA_V_ROWS;
 
-  for (int step = 0; step < N; ++step) {
-    const int src = ((rank - step) % N + N) % N;
-    if (step + 1 < N) {
-      // Prefetch the next step's chunk into the idle half of the double buffer.
-      st = fill(step + 1);
-      if (st != RA_OK) return st;
+  // Chunks are filled in step order; fill(x) writes half x % 2, which the
+  // launch of step x - 2 (enqueued before it) has finished with.
+  int next_fill = 1;
+  auto fill_upto = [&](int x) -> ra_status {
+    for (; next_fill <= x && next_fill < N; ++next_fill) {
+      ra_status s2 = fill(next_fill);
+      if (s2 != RA_OK) return s2;
     }
+    return RA_OK;
+  };
+  auto visible = [&](int step) {
+    const int src = ((rank - step) % N + N) % N;
+    return step == 0 || !r->causal || !ra::causally_empty(r->kind, r->S, N, rank, src);
+  };
+  auto record_step = [&](int step) -> ra_status {
+    return step_ev ? hip_check(hipEventRecord(step_ev[step + 1], sc), "ra_ring_fwd: step event")
+                   : RA_OK;
+  };
+  for (int step = 0; step < N;) {
+    const int src = ((rank - step) % N + N) % N;
+    if (pair && step + 1 < N && visible(step) && visible(step + 1)) {
+      // Steps step and step + 1 in one launch; both chunks are in place
+      // (serialized copies on `compute`).
+      st = fill_upto(step + 1);
+      if (st != RA_OK) return st;
+      const int src2 = ((rank - step - 1) % N + N) % N;
+      a.k = step == 0 ? kc + static_cast<size_t>(rank) * CB : kbuf[step & 1];
+      a.v = vbuf[step & 1];
+      a.kv_pos = pos + static_cast<int64_t>(src) * P.c;
+      a.k2 = kbuf[(step + 1) & 1];
+      a.v2 = vbuf[(step + 1) & 1];
+      a.kv_pos2 = pos + static_cast<int64_t>(src2) * P.c;
+      a.o = o;
+      a.lse = lse;
+      a.merge = step > 0 ? 1 : 0;
+      st = hip_check(ra::launch_attn_bf16(a, sc), "ra_ring_fwd: attention launch (two blocks)");
+      a.k2 = a.v2 = nullptr;
+      a.kv_pos2 = nullptr;
+      if (st == RA_OK) st = record_step(step);
+      if (st == RA_OK) st = record_step(step + 1);
+      if (st != RA_OK) return st;
+      step += 2;
+      continue;
+    }
+    // Prefetch the next step's chunk into the idle half of the double buffer.
+    st = fill_upto(step + 1);
+    if (st != RA_OK) return st;
     // A block that no query of this rank can see (causal rule; step 0 is the
     // rank's own chunk and never empty) adds nothing: its chunk still arrives
     // (the ring forwards it) but no kernel reads it.
-    if (step > 0 && r->causal && ra::causally_empty(r->kind, r->S, N, rank, src)) {
-      if (step_ev) {
-        st = hip_check(hipEventRecord(step_ev[step + 1], sc), "ra_ring_fwd: step event");
-        if (st != RA_OK) return st;
-      }
+    if (!visible(step)) {
+      st = record_step(step);
+      if (st != RA_OK) return st;
+      ++step;
       continue;
     }
     if (uses_buf(step) && !serialize) {
@@ -369,10 +417,9 @@ extern "C" ra_status ra_ring_fwd(const ra_ring_desc *r, const void *q, const voi
       st = hip_check(hipEventRecord(ev->freed[step & 1], sc), "ra_ring_fwd: record freed");
       if (st != RA_OK) return st;
     }
-    if (step_ev) {
-      st = hip_check(hipEventRecord(step_ev[step + 1], sc), "ra_ring_fwd: step event");
-      if (st != RA_OK) return st;
-    }
+    st = record_step(step);
+    if (st != RA_OK) return st;
+    ++step;
   }
   // Order `compute` after the last chunk's arrival also when its step was
   // skipped (the next call reuses the buffers).

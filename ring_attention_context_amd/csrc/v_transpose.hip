@@ -53,13 +53,30 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const T *__restrict__ 
 // reads of the store phase hit eight different chunks (no bank conflicts)
 // while the row writes stay contiguous. Positions past s read as zero and are
 // not stored (a stored 8-position chunk is whole).
+// Optionally (k_bytes > 0, a multiple of 16) workgroup w also copies bytes
+// [w * 8 KiB, (w + 1) * 8 KiB) of k_src to k_dst: a tile of V^T is 8 KiB, so
+// the grid covers a K chunk of the same shape, and a ring step's K and V
+// arrive in one launch.
 __global__ __launch_bounds__(256) void rows_to_vt_kernel(const uint16_t *__restrict__ src,
                                                          uint16_t *__restrict__ vt,
                                                          const int32_t *__restrict__ src_row,
                                                          int64_t bstride, int64_t s,
-                                                         int32_t n_kv, int32_t d) {
+                                                         int32_t n_kv, int32_t d,
+                                                         const unsigned char *__restrict__ k_src,
+                                                         unsigned char *__restrict__ k_dst,
+                                                         uint64_t k_bytes) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[TS * TS];
   const int tid = threadIdx.x;
+  if (k_bytes) {
+    const uint64_t wg = (static_cast<uint64_t>(blockIdx.z) * gridDim.y + blockIdx.y) * gridDim.x +
+                        blockIdx.x;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint64_t off = wg * (TS * TS * 2) + k * 4096 + tid * 16;
+      if (off < k_bytes)
+        *reinterpret_cast<uint4 *>(k_dst + off) = *reinterpret_cast<const uint4 *>(k_src + off);
+    }
+  }
   const int64_t p0 = static_cast<int64_t>(blockIdx.x) * TS;
   const int e0 = blockIdx.y * TS;
   const int bh = blockIdx.z;  // bi * n_kv + h
@@ -99,15 +116,23 @@ __global__ __launch_bounds__(256) void rows_to_vt_kernel(const uint16_t *__restr
 }  // namespace
 
 hipError_t launch_rows_to_vt(const void *src, void *vt, const int32_t *src_row, int64_t bstride,
-                             int32_t b, int64_t s, int32_t n_kv, int32_t d, hipStream_t stream) {
+                             int32_t b, int64_t s, int32_t n_kv, int32_t d, hipStream_t stream,
+                             const void *k_src, void *k_dst, size_t k_bytes) {
   if (b == 0 || s == 0) return hipSuccess;
   const int64_t gx = (s + TS - 1) / TS, gy = (d + TS - 1) / TS;
   const int64_t gz = static_cast<int64_t>(b) * n_kv;
   if (gx > INT32_MAX || gz > 65535 || s % 8 || d % 8) return hipErrorInvalidValue;
+  // The K copy: 16-byte units, and no more than the grid's 8 KiB per workgroup.
+  if (k_bytes && (k_bytes % 16 || !k_src || !k_dst ||
+                  static_cast<uint64_t>(k_bytes) >
+                      static_cast<uint64_t>(gx) * gy * gz * (TS * TS * 2) ||
+                  ((reinterpret_cast<uintptr_t>(k_src) | reinterpret_cast<uintptr_t>(k_dst)) & 15)))
+    return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy), static_cast<unsigned>(gz));
   rows_to_vt_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(src),
                                               static_cast<uint16_t *>(vt), src_row, bstride, s,
-                                              n_kv, d);
+                                              n_kv, d, static_cast<const unsigned char *>(k_src),
+                                              static_cast<unsigned char *>(k_dst), k_bytes);
   return hipGetLastError();
 }
 

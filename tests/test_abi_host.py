@@ -175,7 +175,7 @@ def test_ring_workspace_bytes():
 
 @pytest.mark.parametrize("kw", [
     dict(S=1002), dict(S=1028, N=4), dict(rank=4), dict(N=0, rank=0), dict(kind=9),
-    dict(flags=8), dict(flags=5), dict(d=64), dict(n_q=5), dict(S=-4),
+    dict(flags=16), dict(flags=5), dict(d=64), dict(n_q=5), dict(S=-4),
 ])
 def test_ring_argument_errors(kw):
     with pytest.raises(ra.RingAttnError):

@@ -113,13 +113,48 @@ def _flag_case(dtype="bf16"):
 
 def test_overlap_equals_serialized_bitwise():
     """Same kernels in the same order: any difference would be a copy/compute race.
-    The chunks here are small, so the default runs the copies on `compute` too."""
+    The chunks here are small, so the default runs the copies on `compute` and
+    pairs visible steps in one launch; RA_RING_STEPWISE keeps one launch per
+    step, the launches RA_RING_OVERLAP makes."""
     w, inp, dev = _flag_case()
     _, o1, l1 = run_ring(w, *dev, flags=ra.RA_RING_OVERLAP)
-    _, o2, l2 = run_ring(w, *dev, flags=ra.RA_RING_SERIALIZE)
-    _, o3, l3 = run_ring(w, *dev)
+    _, o2, l2 = run_ring(w, *dev, flags=ra.RA_RING_SERIALIZE | ra.RA_RING_STEPWISE)
+    _, o3, l3 = run_ring(w, *dev, flags=ra.RA_RING_SERIALIZE)
+    _, o4, l4 = run_ring(w, *dev)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
-    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
+
+
+PAIRED = [("zigzag", 3960, 3, 2, True),       # odd N (a last step alone), ragged tiles
+          ("zigzag", 4096, 4, 1, False),      # non-causal: every step visible
+          ("contiguous", 4096, 4, 2, True),   # step 3 is empty: steps 0-1 paired, 2 alone
+          ("striped", 4096, 4, 3, True),
+          ("zigzag", 8192, 8, 0, True)]
+
+
+@pytest.mark.parametrize("case", PAIRED, ids=lambda c: "-".join(map(str, c)))
+def test_paired_steps_match_stepwise_and_oracle(case):
+    """Two visible steps per launch (the default when the copies run on
+    `compute`) against one launch per step and the fp64 oracle on every row:
+    both within the parity bar, and apart only by rounding."""
+    kind, S, N, rank, causal = case
+    print(f"paired ring {case}", flush=True)
+    w = synth.Workload("paired", 1, S, N, kind, 8, 2, 128, "bf16", 1.0, causal, seed=S + rank,
+                       rank=rank)
+    inp = synth.draw(w)
+    dev = device_inputs(w, inp)
+    _, o1, l1 = run_ring(w, *dev, flags=ra.RA_RING_SERIALIZE)
+    _, o2, l2 = run_ring(w, *dev, flags=ra.RA_RING_SERIALIZE | ra.RA_RING_STEPWISE)
+    ro, rl = oatt.naive_attention(inp.q64, inp.k64, inp.v64,
+                                  opart.partition_map(kind, S, N, rank), np.arange(S), causal,
+                                  w.scale)
+    d1 = compare(o1, l1, ro, rl, "bf16", f"{case} paired")
+    d2 = compare(o2, l2, ro, rl, "bf16", f"{case} stepwise")
+    assert np.array_equal(np.isneginf(l1), np.isneginf(l2))
+    fin = np.isfinite(l1)
+    assert np.max(np.abs(l1[fin] - l2[fin])) <= 1e-4
+    assert np.max(np.abs(o1 - o2)) <= 8e-3
+    print(f"  paired max|dO| {d1[0]:.2e} |dlse| {d1[1]:.2e}; stepwise {d2[0]:.2e} {d2[1]:.2e}")
 
 
 @pytest.mark.parametrize("flags", [ra.RA_RING_OVERLAP, 0])
@@ -142,7 +177,7 @@ def test_graph_replay_matches_eager(flags):
     for i in range(3):
         call.o.fill_(float("nan"))
         call.lse.fill_(float("nan"))
-        eager = run_ring(w, *dev)            # other eager work between the replays
+        eager = run_ring(w, *dev, flags=flags)   # other eager work between the replays
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(call.o, o_ref) and torch.equal(call.lse, l_ref), i
