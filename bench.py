@@ -415,11 +415,7 @@ def run_backward(args, w, q, kc, vc, dev, props):
     dvc = torch.zeros_like(dkc)
     pairs = visible_pairs_per_step(w.kind, w.S, w.N, w.rank, w.causal)
     total_flops = sum(10 * w.b * w.n_q * w.d * p for p in pairs)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(w.N + 1)]
-          for _ in range(args.steps)]
-    for e in ev:
-        for x in e:
-            x.record()
+    ev = [[runner.TimingEvent() for _ in range(w.N + 1)] for _ in range(args.steps)]
     desc_plain, _ = ra.ring_desc(b=w.b, n_q=w.n_q, n_kv=w.n_kv, d=w.d, dtype=ra.RA_BF16,
                                  causal=w.causal, kind=w.kind, S=w.S, N=w.N, rank=w.rank,
                                  scale=w.scale)

@@ -310,7 +310,8 @@ ra_status ra_attn_bwd_delta(int64_t rows, int32_t d, int32_t dtype, const void *
  * anywhere); delta: device float32 [b, s_q, n_q] from ra_attn_bwd_delta;
  * dq: device float32 [b, s_q, n_q, d]; dk, dv: device float32
  * [b, s_kv, n_kv, d] (a key/value head collects every query head of its
- * group). Two kernels run in order on `stream`.
+ * group); dq, dk and dv must not overlap one another. Two kernels run in
+ * order on `stream`.
  */
 ra_status ra_block_attn_bwd(const ra_attn_desc *desc, const void *q, const void *k,
                             const void *v, const void *dout, const float *lse,
@@ -336,7 +337,8 @@ ra_status ra_ring_bwd_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
  * dq: device float32 [b, c, n_q, d], overwritten with the rank's dQ.
  * dk_chunks, dv_chunks: device float32 [N, b, c, n_kv, d], slot j holding
  * block j's dK, dV accumulated so far; this rank's contribution is ADDED:
- * calling every rank on the same slots sums the sequence's dK, dV.
+ * calling every rank on the same slots sums the sequence's dK, dV. dq,
+ * dk_chunks and dv_chunks must not overlap one another.
  * Step r works on block (rank - r) mod N. With N > 1 the block's K, V and
  * slot dK, dV are received into half r % 2 of the workspace's double buffer
  * on `copy`, the step's two kernels run on `compute` against that half, and

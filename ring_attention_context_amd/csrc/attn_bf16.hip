@@ -153,6 +153,47 @@ __device__ __forceinline__ int64_t wave_count(const int32_t *kv_pos, int64_t n, 
   return lo;
 }
 
+// K independent counts of the same kind as wave_count (search k: keys of the
+// non-decreasing arr[k][0, n) with position <= p[k], or < p[k] when lt[k]),
+// advanced together: each round issues every active search's probe load
+// before any is used, so the K searches cost the memory latency of one.
+template <int K>
+__device__ __forceinline__ void wave_counts(const int32_t *const (&arr)[K], int64_t n,
+                                            const int32_t (&p)[K], const bool (&lt)[K],
+                                            int64_t (&cnt)[K], int lane) {
+  int64_t lo[K], hi[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    lo[k] = 0;
+    hi[k] = n;
+  }
+  while (true) {
+    bool active = false;
+#pragma unroll
+    for (int k = 0; k < K; ++k) active |= lo[k] < hi[k];
+    if (!active) break;
+    int64_t step[K], idx[K];
+    int32_t v[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      step[k] = (hi[k] - lo[k] + 63) / 64;
+      idx[k] = lo[k] + lane * step[k];
+      v[k] = lo[k] < hi[k] && idx[k] < hi[k] ? arr[k][idx[k]] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (lo[k] >= hi[k]) continue;
+      const bool in = idx[k] < hi[k] && (lt[k] ? v[k] < p[k] : v[k] <= p[k]);
+      const int c = __popcll(__ballot(in));
+      const int64_t new_hi = min(hi[k], lo[k] + c * step[k]);
+      lo[k] = c == 0 ? lo[k] : lo[k] + (c - 1) * step[k] + 1;
+      hi[k] = new_hi;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) cnt[k] = lo[k];
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
   const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int32_t>(bytes));
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), n,
@@ -248,18 +289,54 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // and the tile tests below never skip.
   // With a document mask the range starts at the tile holding the first key
   // of the first query's document (document starts are non-decreasing).
+  // All the counts below come from one joint search (wave_counts): the
+  // workgroup's range, then the wave's (c_hi: keys not after its last query,
+  // c_lo: not after its first; c_d: before its latest document start), for
+  // the second block too with PAIR. A wave without rows searches with the
+  // workgroup's last query (its results are not used).
   int64_t nkeys = a.s_kv, nkeys2 = PAIR ? a.s_kv : 0;
   int64_t kbeg = 0;
   int32_t w_qmin = INT_MAX - 1, w_qmax = INT_MAX - 1;
   int32_t w_lomax = INT_MIN;  // latest document start among the wave's queries
+  int64_t c_hi = 0, c_lo = 0, c_d = 0, c_hi2 = 0, c_lo2 = 0;
   if (a.causal) {
-    nkeys = wave_count<true>(a.kv_pos, a.s_kv, a.q_pos[wg_tok_last], lane);
-    if (PAIR) nkeys2 = wave_count<true>(a.kv_pos2, a.s_kv, a.q_pos[wg_tok_last], lane);
-    if (DOC) kbeg = wave_count<false>(a.kv_pos, a.s_kv, a.q_lo[wg_tok0], lane) / BK * BK;
-    if (wave_has_rows) {
-      w_qmin = a.q_pos[w_tok0];
-      w_qmax = a.q_pos[w_tok_last];
-      if (DOC) w_lomax = a.q_lo[w_tok_last];
+    const int32_t p_last = a.q_pos[wg_tok_last];
+    w_qmin = wave_has_rows ? a.q_pos[w_tok0] : p_last;
+    w_qmax = wave_has_rows ? a.q_pos[w_tok_last] : p_last;
+    if constexpr (DOC) {
+      w_lomax = a.q_lo[wave_has_rows ? w_tok_last : wg_tok_last];
+      int64_t c[5];
+      wave_counts<5>({a.kv_pos, a.kv_pos, a.kv_pos, a.kv_pos, a.kv_pos}, a.s_kv,
+                     {p_last, a.q_lo[wg_tok0], w_qmax, w_qmin, w_lomax},
+                     {false, true, false, false, true}, c, lane);
+      nkeys = c[0];
+      kbeg = c[1] / BK * BK;
+      c_hi = c[2];
+      c_lo = c[3];
+      c_d = c[4];
+    } else if constexpr (PAIR) {
+      int64_t c[6];
+      wave_counts<6>({a.kv_pos, a.kv_pos, a.kv_pos, a.kv_pos2, a.kv_pos2, a.kv_pos2}, a.s_kv,
+                     {p_last, w_qmax, w_qmin, p_last, w_qmax, w_qmin},
+                     {false, false, false, false, false, false}, c, lane);
+      nkeys = c[0];
+      c_hi = c[1];
+      c_lo = c[2];
+      nkeys2 = c[3];
+      c_hi2 = c[4];
+      c_lo2 = c[5];
+    } else {
+      int64_t c[3];
+      wave_counts<3>({a.kv_pos, a.kv_pos, a.kv_pos}, a.s_kv, {p_last, w_qmax, w_qmin},
+                     {false, false, false}, c, lane);
+      nkeys = c[0];
+      c_hi = c[1];
+      c_lo = c[2];
+    }
+    if (!wave_has_rows) {
+      w_qmin = INT_MAX - 1;
+      w_qmax = INT_MAX - 1;
+      w_lomax = INT_MIN;
     }
   }
   // nt1 tiles of the first block, then (PAIR) nt2 of the second.
@@ -281,20 +358,14 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   int w_nt = nt, j_diag = INT_MAX, j_doc = 0;
   int w_nt1 = nt1, j_diag2 = INT_MAX;
   if (a.causal && wave_has_rows) {
-    const int64_t c_hi = wave_count<true>(a.kv_pos, a.s_kv, w_qmax, lane);
     w_nt1 = c_hi > kbeg ? min(nt1, static_cast<int>((c_hi - kbeg + BK - 1) / BK)) : 0;
     w_nt = w_nt1;
-    const int64_t c_lo = wave_count<true>(a.kv_pos, a.s_kv, w_qmin, lane);
     j_diag = c_lo > kbeg ? static_cast<int>((c_lo - kbeg) / BK) : 0;
-    if (DOC) {
-      const int64_t c_d = wave_count<false>(a.kv_pos, a.s_kv, w_lomax, lane);
-      j_doc = c_d > kbeg ? static_cast<int>((c_d - kbeg + BK - 1) / BK) : 0;
-    }
+    if (DOC) j_doc = c_d > kbeg ? static_cast<int>((c_d - kbeg + BK - 1) / BK) : 0;
     if (PAIR) {
-      const int64_t c_hi2 = wave_count<true>(a.kv_pos2, a.s_kv, w_qmax, lane);
       const int w_nt2 = min(nt2, static_cast<int>((c_hi2 + BK - 1) / BK));
       if (w_nt2 > 0) w_nt = nt1 + w_nt2;
-      j_diag2 = static_cast<int>(wave_count<true>(a.kv_pos2, a.s_kv, w_qmin, lane) / BK);
+      j_diag2 = static_cast<int>(c_lo2 / BK);
     }
   }
 
@@ -749,9 +820,22 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   const float lse_new = l_tot > 0.f ? (m_run + __log2f(l_tot)) * LN2 : -INFINITY;
   const float inv = l_tot > 0.f && lh_tot > 0.f ? 1.f / lh_tot : 0.f;
   const int64_t row = (bi * a.s_q + tok) * a.n_q + h;
+  // Accumulator element e4*4 + j of block db holds d = db*32 + e4*8 + hi*4 + j.
+  float *orow = a.o + row * D + hi * 4;
+  // Merging: the old lse and all sixteen 16-byte pieces of the old o row go
+  // out together, so the epilogue waits for memory once, not once per piece.
+  float4 o_old[D / 32][4];
+  float lse_old = -INFINITY;
+  if (a.merge) {
+    lse_old = a.lse[row];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        o_old[db][e4] = *reinterpret_cast<const float4 *>(orow + db * 32 + e4 * 8);
+  }
   float w_old = 0.f, w_new = inv, lse_out = lse_new;
   if (a.merge) {
-    const float lse_old = a.lse[row];
     const float m = fmaxf(lse_old, lse_new);
     if (m == -INFINITY) {
       w_new = 0.f;
@@ -762,26 +846,23 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
       w_new = __expf(lse_new - lse_out) * inv;
     }
   }
-  // Accumulator element e4*4 + j of block db holds d = db*32 + e4*8 + hi*4 + j.
-  float *orow = a.o + row * D + hi * 4;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
-      float4 *dst = reinterpret_cast<float4 *>(orow + db * 32 + e4 * 8);
       float4 r;
       r.x = w_new * acc[db][e4 * 4 + 0];
       r.y = w_new * acc[db][e4 * 4 + 1];
       r.z = w_new * acc[db][e4 * 4 + 2];
       r.w = w_new * acc[db][e4 * 4 + 3];
       if (a.merge) {
-        const float4 old = *dst;
+        const float4 old = o_old[db][e4];
         r.x += w_old * old.x;
         r.y += w_old * old.y;
         r.z += w_old * old.z;
         r.w += w_old * old.w;
       }
-      *dst = r;
+      *reinterpret_cast<float4 *>(orow + db * 32 + e4 * 8) = r;
     }
   if (hi == 0) a.lse[row] = lse_out;
 }

@@ -928,24 +928,30 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int64_t orow = a.kv_row ? (a.kv_row[key] + bi * a.kv_row_bstride) * a.n_kv + kvh : krow;
   float *krow_out = a.dk + orow * D + hi * 4;
   float *vrow_out = a.dv + orow * D + hi * 4;
+  // Per 32-column block, the eight 16-byte loads go out together before its
+  // stores (dk and dv are separate arrays), so the block waits for memory once.
 #pragma unroll
-  for (int dblk = 0; dblk < D / 32; ++dblk)
+  for (int dblk = 0; dblk < D / 32; ++dblk) {
+    float4 rk[4], rv[4];
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
-      float4 *pk = reinterpret_cast<float4 *>(krow_out + dblk * 32 + e4 * 8);
-      float4 *pv = reinterpret_cast<float4 *>(vrow_out + dblk * 32 + e4 * 8);
-      float4 rk = *pk, rv = *pv;
-      rk.x += a.scale * dk[dblk][e4 * 4 + 0];
-      rk.y += a.scale * dk[dblk][e4 * 4 + 1];
-      rk.z += a.scale * dk[dblk][e4 * 4 + 2];
-      rk.w += a.scale * dk[dblk][e4 * 4 + 3];
-      rv.x += dv[dblk][e4 * 4 + 0];
-      rv.y += dv[dblk][e4 * 4 + 1];
-      rv.z += dv[dblk][e4 * 4 + 2];
-      rv.w += dv[dblk][e4 * 4 + 3];
-      *pk = rk;
-      *pv = rv;
+      rk[e4] = *reinterpret_cast<const float4 *>(krow_out + dblk * 32 + e4 * 8);
+      rv[e4] = *reinterpret_cast<const float4 *>(vrow_out + dblk * 32 + e4 * 8);
     }
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      rk[e4].x += a.scale * dk[dblk][e4 * 4 + 0];
+      rk[e4].y += a.scale * dk[dblk][e4 * 4 + 1];
+      rk[e4].z += a.scale * dk[dblk][e4 * 4 + 2];
+      rk[e4].w += a.scale * dk[dblk][e4 * 4 + 3];
+      rv[e4].x += dv[dblk][e4 * 4 + 0];
+      rv[e4].y += dv[dblk][e4 * 4 + 1];
+      rv[e4].z += dv[dblk][e4 * 4 + 2];
+      rv[e4].w += dv[dblk][e4 * 4 + 3];
+      *reinterpret_cast<float4 *>(krow_out + dblk * 32 + e4 * 8) = rk[e4];
+      *reinterpret_cast<float4 *>(vrow_out + dblk * 32 + e4 * 8) = rv[e4];
+    }
+  }
 }
 
 template <int HW>
