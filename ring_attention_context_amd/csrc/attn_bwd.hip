@@ -199,26 +199,60 @@ constexpr int Q_QW = 32;
 constexpr int Q_BK = 64;
 constexpr int Q_TILE_B = Q_BK * ROW_B;
 constexpr int Q_LOADS = Q_TILE_B / (1024 * Q_WAVES);
+constexpr int Q_NSTAGE = 4;
+
+// Waits until at most n (0..15) of this wave's vector-memory loads are in
+// flight: the n most recent ones (loads complete in order).
+__device__ __forceinline__ void wait_loads_upto(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+  }
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for every load still in flight); the empty asm statements keep
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // DOC: a document mask is given (a.q_lo); without it the mask code compiles away.
 template <int HW, bool DOC>
 __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[Q_TILE_B], k_lds1[Q_TILE_B],
-      k_lds2[Q_TILE_B];
+  // One LDS object per stage and operand (a tile's key positions after its K
+  // rows): the compiler then sees that the asynchronous loads into one stage
+  // never alias the reads of the others. It tells at most eight apart.
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[Q_TILE_B + Q_BK * 4],
+      k_lds1[Q_TILE_B + Q_BK * 4], k_lds2[Q_TILE_B + Q_BK * 4], k_lds3[Q_TILE_B + Q_BK * 4];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds0[Q_TILE_B], v_lds1[Q_TILE_B],
-      v_lds2[Q_TILE_B];
-  __shared__ __attribute__((aligned(16))) int32_t p_lds0[Q_BK], p_lds1[Q_BK], p_lds2[Q_BK];
+      v_lds2[Q_TILE_B], v_lds3[Q_TILE_B];
   auto k_stage = [&](auto s) INLINE -> unsigned char * {
     constexpr int v = decltype(s)::value;
-    return v == 0 ? k_lds0 : v == 1 ? k_lds1 : k_lds2;
+    return v == 0 ? k_lds0 : v == 1 ? k_lds1 : v == 2 ? k_lds2 : k_lds3;
   };
   auto v_stage = [&](auto s) INLINE -> unsigned char * {
     constexpr int v = decltype(s)::value;
-    return v == 0 ? v_lds0 : v == 1 ? v_lds1 : v_lds2;
+    return v == 0 ? v_lds0 : v == 1 ? v_lds1 : v == 2 ? v_lds2 : v_lds3;
   };
   auto p_stage = [&](auto s) INLINE -> int32_t * {
-    constexpr int v = decltype(s)::value;
-    return v == 0 ? p_lds0 : v == 1 ? p_lds1 : p_lds2;
+    return reinterpret_cast<int32_t *>(k_stage(s) + Q_TILE_B);
   };
 
   constexpr int TB = Q_WAVES / HW;
@@ -298,10 +332,14 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
   const float dlt = !tok_ok ? 0.f : a.hm ? a.delta[hrow] : a.delta[row];
   const float sl2 = a.scale * LOG2E;
 
-  uint32_t koff[D / 16];
-#pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds)
-    koff[ds] = col * ROW_B + ((((2 * ds + hi) ^ swz(col & 15))) << 4);
+  // Waves w and w + 4 share a SIMD and run the tile phases in opposite orders.
+  const bool grp_b = wave >= Q_WAVES / 2;
+
+  // K / V row operand of k-step ds: the swizzle is an XOR of the chunk index,
+  // so one offset register serves every k-step (kept live by the pin in the
+  // loop, which stops the compiler from hoisting eight offsets).
+  uint32_t koff0 = col * ROW_B + ((hi ^ swz(col & 15)) << 4);
+  auto koff = [&](int ds) INLINE -> uint32_t { return koff0 ^ (static_cast<uint32_t>(ds) << 5); };
   uint32_t toff[2][D / 32];
   tr_offsets(lane, toff);
 
@@ -315,6 +353,10 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     const int r = 4 * (wave + Q_WAVES * i) + (lane >> 4);
     goff[i] = static_cast<uint32_t>(r * kv_row_bytes + (((lane & 15) ^ swz(r & 15)) << 4));
   }
+  // K, V rows (and key positions, by wave 0 when causal) of tile t into
+  // stage `stage`. Issued for every step, past the range too (the buffer
+  // descriptors' bounds return zeros there), so every wave issues the same
+  // loads per step and the waits below count them exactly.
   auto issue_tile = [&](int t, auto stage) INLINE {
     const int64_t key0 = kbeg + static_cast<int64_t>(t) * Q_BK;
     const int64_t left = a.s_kv - key0;
@@ -335,50 +377,84 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
                                                0, 0, 0);
     }
   };
+  const int n_step = 2 * Q_LOADS + (a.causal && wave == 0 ? 1 : 0);  // loads per issue_tile
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  // S^T and dP^T of the tile whose dS comes next; dS^T (bf16 B operand per
+  // k-step) of the tile whose dQ products come next.
+  f32x16 s[2], dp[2];
+  bf16x8 dsb[4];
+  bool done = !wave_has_rows || w_nt == 0;
 
-  // Per tile: S^T and dP^T (32 MFMAs, K and V rows read a few MFMAs ahead),
-  // the element mask where needed, then dQ^T += K^T dS^T (16 MFMAs, K^T by the
-  // transposing read) with dS^T of the next k-step formed on the VALU between
-  // them. Scheduling fences keep the reads ahead of their MFMAs: left to
-  // itself the compiler waits for each read right before its MFMA.
+  // Item m of S^T, dP^T (32 MFMAs): k-step m/4, key block (m/2)%2; S^T from
+  // the K rows when m is even, dP^T from the V rows when odd.
+  auto rd_m1 = [&](const unsigned char *kb, const unsigned char *vb, int m) INLINE -> bf16x8 {
+    return *reinterpret_cast<const bf16x8 *>(((m & 1) ? vb : kb) + koff(m >> 2) +
+                                             ((m >> 1) & 1) * 32 * ROW_B);
+  };
+  auto mfma_m1 = [&](int m, const bf16x8 &o) INLINE {
+    const int ds = m >> 2, j = (m >> 1) & 1;
+    if (m & 1)
+      dp[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, dreg[ds], ds == 0 ? f32x16{} : dp[j], 0, 0, 0);
+    else
+      s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, qreg[ds], ds == 0 ? f32x16{} : s[j], 0, 0, 0);
+  };
   constexpr int DIST = 4;
-  auto process = [&](int t, auto stage) INLINE {
-    const unsigned char *kb = k_stage(stage);
-    const unsigned char *vb = v_stage(stage);
-    f32x16 s[2], dp[2];
-    // Item i: k-step i/4, key block (i/2)%2; S^T from K when i is even, dP^T
-    // from V when odd.
-    auto rd_a = [&](int i) INLINE -> bf16x8 {
-      const unsigned char *base = (i & 1) ? vb : kb;
-      return *reinterpret_cast<const bf16x8 *>(base + koff[i >> 2] + ((i >> 1) & 1) * 32 * ROW_B);
-    };
-    {
-      bf16x8 op[DIST + 1];
+  // S^T and dP^T of the tile in stage `st` alone (before the loop).
+  auto m1_only = [&](auto st) INLINE {
+    const unsigned char *kb = k_stage(st);
+    const unsigned char *vb = v_stage(st);
+    bf16x8 op[DIST + 1];
 #pragma unroll
-      for (int i = 0; i < DIST; ++i) op[i] = rd_a(i);
+    for (int i = 0; i < DIST; ++i) op[i] = rd_m1(kb, vb, i);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i + DIST < 32) op[(i + DIST) % (DIST + 1)] = rd_a(i + DIST);
-        const int ds = i >> 2, j = (i >> 1) & 1;
-        const bf16x8 o = op[i % (DIST + 1)];
-        if (i & 1)
-          dp[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, dreg[ds], ds == 0 ? f32x16{} : dp[j], 0, 0, 0);
-        else
-          s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, qreg[ds], ds == 0 ? f32x16{} : s[j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int i = 0; i < 32; ++i) {
+      if (i + DIST < 32) op[(i + DIST) % (DIST + 1)] = rd_m1(kb, vb, i + DIST);
+      mfma_m1(i, op[i % (DIST + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // Matrix phase: S^T, dP^T of the next tile (stage `sn`) interleaved with
+  // dQ^T += K^T dS^T of the current one (stage `sc`, K^T by the transposing
+  // read): two of the former, then one of the latter. Operands are read DIST
+  // items ahead behind scheduling fences.
+  auto xphase = [&](auto sn, auto sc) INLINE {
+    const unsigned char *kn = k_stage(sn);
+    const unsigned char *vn = v_stage(sn);
+    const unsigned char *kc = k_stage(sc);
+    auto rd = [&](int i) INLINE -> bf16x8 {
+      if (i % 3 < 2) return rd_m1(kn, vn, 2 * (i / 3) + i % 3);
+      const int c = i / 3;
+      return tr_read(kc, toff, c & 3, (c >> 2) * 16);
+    };
+    bf16x8 op[DIST + 1];
+#pragma unroll
+    for (int i = 0; i < DIST; ++i) op[i] = rd(i);
+#pragma unroll
+    for (int i = 0; i < 48; ++i) {
+      if (i + DIST < 48) op[(i + DIST) % (DIST + 1)] = rd(i + DIST);
+      const bf16x8 o = op[i % (DIST + 1)];
+      if (i % 3 < 2) {
+        mfma_m1(2 * (i / 3) + i % 3, o);
+      } else {
+        const int c = i / 3, ks = c >> 2, db = c & 3;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, dsb[ks], acc[db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Vector phase for tile t (scores in s, dp; positions in stage `st`): the
+  // element mask where needed, then dS^T = P^T (dP^T - D) into dsb: k-step ks
+  // holds accumulator elements (ks%2)*8 .. +7 of key block ks/2.
+  auto yphase = [&](int t, auto st) INLINE {
     // Element e4*4 + j of key block kb holds key kb*32 + e4*8 + hi*4 + j.
     const int64_t key0 = kbeg + static_cast<int64_t>(t) * Q_BK;
     const bool ragged = key0 + Q_BK > a.s_kv;
-    if (ragged || (a.causal && p_stage(stage)[Q_BK - 1] > w_qmin) ||
-        (DOC && p_stage(stage)[0] < w_lomax)) {
+    const int32_t *pp = p_stage(st);
+    if (ragged || (a.causal && pp[Q_BK - 1] > w_qmin) || (DOC && pp[0] < w_lomax)) {
       const int lim = ragged ? static_cast<int>(a.s_kv - key0) : Q_BK;
-      const int32_t *pp = p_stage(stage);
       const int32_t qp = a.causal ? qpos : INT_MAX;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -392,55 +468,72 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
           }
         }
     }
-    // dS^T = P^T (dP^T - D) as the bf16 B operand of dQ^T += K^T dS^T:
-    // k-step ks holds accumulator elements (ks%2)*8 .. +7 of key block ks/2.
-    bf16x8 dsb[4];
-    auto ds_pair = [&](int ks, int e) INLINE {
 #pragma unroll
-      for (int u = e; u < e + 2; ++u) {
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
         const int j = ks >> 1, el = (ks & 1) * 8 + u;
         const float p = exp2_fast(fmaf(s[j][el], sl2, -lse2));
         dsb[ks][u] = static_cast<__bf16>(p * (dp[j][el] - dlt));
       }
-      asm volatile("" : "+v"(dsb[ks]));  // keep it between the MFMAs
-    };
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) ds_pair(0, e);
-    auto rd_c = [&](int i) INLINE -> bf16x8 { return tr_read(kb, toff, i & 3, (i >> 2) * 16); };
-    {
-      bf16x8 op[DIST + 1];
-#pragma unroll
-      for (int i = 0; i < DIST; ++i) op[i] = rd_c(i);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i + DIST < 16) op[(i + DIST) % (DIST + 1)] = rd_c(i + DIST);
-        const int ks = i >> 2, db = i & 3;
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (DIST + 1)], dsb[ks], acc[db], 0, 0, 0);
-        if (ks + 1 < 4) ds_pair(ks + 1, 2 * (i & 3));
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      asm volatile("" : "+v"(dsb[ks]));  // one k-step of fp32 values live at a time
     }
   };
 
   using St0 = std::integral_constant<int, 0>;
   using St1 = std::integral_constant<int, 1>;
   using St2 = std::integral_constant<int, 2>;
-  if (nt > 0) issue_tile(0, St0{});
-  if (nt > 1) issue_tile(1, St1{});
+  using St3 = std::integral_constant<int, 3>;
+  // ---- prologue: tiles 0..2 in flight, tile 0's scores (and, for the first
+  // group, its dS) ----
+  issue_tile(0, St0{});
+  issue_tile(1, St1{});
+  issue_tile(2, St2{});
+  wait_loads_upto(2 * n_step);  // tile 0 has landed (this wave's share)
+  barrier_keep_loads();         // ... and everyone's
+  if (!done) {
+    m1_only(St0{});
+    if (!grp_b) yphase(0, St0{});
+  }
+  // ---- main loop: step t = 0 .. nt-1, tile t in stage t % 4 ----
+  // Step t issues tile t + 3 into the stage tile t - 1 left and needs tiles t
+  // (dQ products) and t + 1 (scores): its loads have had two steps to land.
+  // The matrix phase runs the dQ products of tile t with the scores of tile
+  // t + 1; the vector phase forms dS of the tile whose scores are at hand. The
+  // first group runs matrix then vector (tile t + 1), the second vector (tile
+  // t) then matrix, so one wave's exponentials overlap the other's MFMAs.
   auto step = [&](auto stage_c, int t) INLINE {
     constexpr int S = decltype(stage_c)::value;
     using SC = std::integral_constant<int, S>;
-    using SL = std::integral_constant<int, (S + 2) % 3>;
-    wait_own_loads();  // tiles t (and t+1) have landed in this wave's share ...
-    __syncthreads();   // ... and in everyone's; every wave is done with tile t-1
-    if (t + 2 < nt) issue_tile(t + 2, SL{});
-    if (t < w_nt) process(t, SC{});
+    using SN = std::integral_constant<int, (S + 1) % Q_NSTAGE>;
+    using SP = std::integral_constant<int, (S + Q_NSTAGE - 1) % Q_NSTAGE>;
+    wait_loads_upto(n_step);  // tile t + 1 has landed (tile t + 2 may be in flight)
+    barrier_keep_loads();     // everyone's too; every wave is done with tile t - 1
+    asm volatile("" : "+v"(koff0));  // pin: see koff
+    issue_tile(t + 3, SP{});
+    if (!done) {
+      if (grp_b) yphase(t, SC{});
+      // After the wave's last tile the scores computed here are of a tile past
+      // its range and are dropped.
+      __builtin_amdgcn_s_setprio(1);
+      xphase(SN{}, SC{});
+      __builtin_amdgcn_s_setprio(0);
+      if (t + 1 < w_nt) {
+        if (!grp_b) yphase(t + 1, SN{});
+      } else {
+        done = true;
+      }
+    }
   };
-  for (int t = 0; t < nt; t += 3) {
+  // The body always runs all four steps (steps past nt only wait, synchronise
+  // and issue loads past the range).
+  for (int t = 0; t < nt; t += Q_NSTAGE) {
     step(St0{}, t);
-    if (t + 1 < nt) step(St1{}, t + 1);
-    if (t + 2 < nt) step(St2{}, t + 2);
+    step(St1{}, t + 1);
+    step(St2{}, t + 2);
+    step(St3{}, t + 3);
   }
+  wait_loads_upto(0);  // the loads past the range have landed before the wave ends
 
   // With a document mask many waves see no key at all: they skip the dq
   // update (adding zeros).
