@@ -15,7 +15,10 @@
 //     S^T = K Q^T and dP^T = V dO^T (K and V rows by ds_read_b128),
 //     P^T = 2^(S^T scale log2 e - lse log2 e), dS^T = P^T (dP^T - D), and
 //     dQ^T += K^T dS^T (K^T operands by the transposing ds_read_b64_tr_b16).
-//     Every lane holds one query, so lse and D are per-lane constants;
+//     Every lane holds one query, so lse and D are per-lane constants. As in
+//     the forward, the MFMAs of two tiles form one matrix phase and the
+//     element-wise work a vector phase, which the two waves of a SIMD run in
+//     opposite orders;
 //   * bwd_dkdv_kernel (bf16, d = 128): a workgroup owns 128 keys of one
 //     key/value head in four groups of 32, one group per SIMD, and walks the
 //     blocks of 64 queries (q, do, lse, D, positions, staged in LDS) of every
