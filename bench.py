@@ -539,8 +539,18 @@ def time_ring(w, q, kc, vc, warmup, steps, flags=0):
     compute, copy = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
     call = runner.RingCall(q, kc, vc, kind=w.kind, S=w.S, N=w.N, rank=w.rank, causal=w.causal,
                            scale=w.scale, flags=flags, compute=compute, copy=copy)
-    for _ in range(warmup):
+    # Short calls: warm up for at least 0.3 s (the shader clock ramps over the
+    # first launches after idle) and time at least 0.2 s of calls.
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < 0.3:
         call()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    per_call = (time.perf_counter() - t0) / max(n, 1)
+    steps = max(steps, int(0.2 / max(per_call, 1e-6)))
     evs = [call.make_events() for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
