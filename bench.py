@@ -531,7 +531,13 @@ class ClockSampler:
 
 
 def time_ring(w, q, kc, vc, warmup, steps, flags=0):
-    """Mean ms per ra_ring_fwd call and the median per-step ms (step events)."""
+    """Mean ms per ra_ring_fwd call, the median per-step ms, and the mean ms
+    per call of the calls that recorded the step events.
+
+    Recording an event between two launches on a stream holds the next launch
+    until the event's timestamp is written (~8 us here), so the calls are
+    timed without step events and the per-step times come from as many
+    further calls that record them."""
     import numpy as np
     import torch
     from ring_attention_context_amd import runner
@@ -551,15 +557,20 @@ def time_ring(w, q, kc, vc, warmup, steps, flags=0):
     torch.cuda.synchronize()
     per_call = (time.perf_counter() - t0) / max(n, 1)
     steps = max(steps, int(0.2 / max(per_call, 1e-6)))
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
     evs = [call.make_events() for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         call(events=evs[i])
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms_ev = (time.perf_counter() - t0) * 1e3 / steps
     step_ms = np.median([[e[i].elapsed_time(e[i + 1]) for i in range(w.N)] for e in evs], axis=0)
-    return ms, step_ms.tolist()
+    return ms, step_ms.tolist(), ms_ev
 
 
 def run_sweep(path, warmup, steps):
@@ -576,14 +587,15 @@ def run_sweep(path, warmup, steps):
         inp = synth.draw(w)
         q, kc, vc = runner.ring_inputs(inp.q, inp.k, inp.v, w.dtype, w.kind, w.N, dev)
         del inp
-        ms, step_ms = time_ring(w, q, kc, vc, warmup, steps)
+        ms, step_ms, ms_ev = time_ring(w, q, kc, vc, warmup, steps)
         pairs = sum(visible_pairs_per_step(w.kind, w.S, w.N, w.rank, w.causal))
         tf = 4 * w.b * w.n_q * w.d * pairs / (ms * 1e-3) / 1e12
         rec = {"workload": name, "kind": w.kind, "rank": w.rank, "ms": ms, "tflops": tf,
                "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS, "step_ms": step_ms,
-               "visible_pairs": pairs, "dtype": w.dtype}
+               "ms_with_step_events": ms_ev, "visible_pairs": pairs, "dtype": w.dtype}
         out["workloads"].append(rec)
-        log(f"[sweep] {name}: {ms:.3f} ms/call, {tf:.1f} TFLOP/s")
+        log(f"[sweep] {name}: {ms:.3f} ms/call, {tf:.1f} TFLOP/s "
+            f"({ms_ev:.3f} ms/call recording the step events)")
         del q, kc, vc
         torch.cuda.empty_cache()
     base = synth.WORKLOADS["llama3_70b_128k_zigzag"]
@@ -598,7 +610,7 @@ def run_sweep(path, warmup, steps):
         tiles = np.zeros((w0.N, w0.N), dtype=np.int64)
         for rank in range(w0.N):
             w = w0.with_(rank=rank)
-            ms, step_ms = time_ring(w, q, kc, vc, warmup, steps)
+            ms, step_ms, _ = time_ring(w, q, kc, vc, warmup, steps)
             t[rank] = step_ms
             work[rank] = visible_pairs_per_step(kind, w.S, w.N, rank, True)
             tiles[rank] = tile_pairs_per_step(kind, w.S, w.N, rank)
