@@ -289,6 +289,56 @@ def test_full_workload_bwd_sampled_rows_and_invariant(name):
           f"max |sum dv - sum dout| {err_dv:.2e} (max {np.max(np.abs(want_dv)):.2e})", flush=True)
 
 
+def test_ring_bwd_128k_sampled_keys_against_oracle():
+    """The 128K ring backward at full size, element by element on this rank's
+    dK, dV contribution to 64+ sampled keys (chunk and half boundaries among
+    them) x all KV heads (dq rows at this size are checked above, against the
+    oracle's own forward).
+
+    The backward is a function of (q, k, v, dout, o, lse); the oracle cannot
+    afford the 128K forward of every row, so both sides get the same seeded
+    o ~ N(0, 0.05^2) and lse = ln(pos + 1) + 1/2 (the expected log-sum-exp of
+    pos + 1 unit-variance scores; any finite lse is a valid input) instead of
+    the forward's. A key's gradient then needs only that lse and D = dout . o
+    of every query that sees it."""
+    w = synth.WORKLOADS["llama3_70b_128k_zigzag"]
+    print(f"workload {w.name} backward, seeded o / lse, sampled keys", flush=True)
+    inp = synth.draw(w)
+    q_pos = opart.partition_map(w.kind, w.S, w.N, w.rank)
+    rng = np.random.default_rng(w.seed + 2000)
+    o32 = (0.05 * rng.standard_normal((w.b, w.c, w.n_q, w.d))).astype(np.float32)
+    lse32 = np.broadcast_to((np.log(q_pos + 1.0) + 0.5)[None, :, None],
+                            (w.b, w.c, w.n_q)).astype(np.float32)
+    rng = np.random.default_rng(w.seed + 1000)
+    do_bits = synth.bf16_bits(rng.standard_normal((w.b, w.c, w.n_q, w.d), dtype=np.float32))
+    q, kc, vc = runner.ring_inputs(inp.q, inp.k, inp.v, w.dtype, w.kind, w.N, "cuda")
+    desc, _ = ra.ring_desc(b=w.b, n_q=w.n_q, n_kv=w.n_kv, d=w.d, dtype=ra.RA_BF16,
+                           causal=w.causal, kind=w.kind, S=w.S, N=w.N, rank=w.rank,
+                           scale=w.scale)
+    ws = torch.empty(ra.ra_ring_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    dq = torch.empty(tuple(q.shape), device="cuda")
+    dkc = torch.zeros(tuple(kc.shape), device="cuda")
+    dvc = torch.zeros_like(dkc)
+    ra.ra_ring_bwd(desc, q, kc, vc, torch.from_numpy(o32).cuda(),
+                   torch.from_numpy(np.ascontiguousarray(lse32)).cuda(),
+                   runner.host_to_device(do_bits, "bf16", "cuda"), dq, dkc, dvc, ws)
+    torch.cuda.synchronize()
+    keys = sample_keys(w.kind, w.S, w.N, 64, w.seed)
+    slots = key_slots(w.kind, w.S, w.N, keys)
+    got_k = torch.stack([dkc[j][:, a] for j, a in slots], dim=1).cpu().numpy()
+    got_v = torch.stack([dvc[j][:, a] for j, a in slots], dim=1).cpu().numpy()
+    del q, kc, vc, dkc, dvc, ws
+    torch.cuda.empty_cache()
+    q64, k64, v64 = inp.q64, inp.k64, inp.v64
+    do64 = synth.bf16_to_f32(do_bits).astype(np.float64)
+    D = obwd.delta(o32, do64)
+    _, rk, rv = obwd.block_attention_bwd(q64, k64[:, keys], v64[:, keys], do64, lse32, D, q_pos,
+                                         keys, w.causal, w.scale)
+    for got, want, what in ((got_k, rk, "dk"), (got_v, rv, "dv")):
+        err, m = grad_close(got, want, f"128K {what} keys")
+        print(f"  {what} keys {len(keys)}: max err {err:.2e} (max |ref| {m:.2e})", flush=True)
+
+
 def test_ring_batched_forward_and_backward():
     """b = 2 through ra_ring_fwd and every rank's ra_ring_bwd (the [N, b, c, ...]
     chunk layout and the per-batch rows of every step), against naive attention
