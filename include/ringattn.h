@@ -71,9 +71,13 @@ typedef enum {
   RA_V_ROWS = 0,        /* [b, s_kv, n_kv, d], the layout of k                */
   RA_V_TRANSPOSED = 1   /* [b, n_kv, d, s_kv]: element (i, s, h, e) at
                            ((i*n_kv + h)*d + e)*s_kv + s; bf16 only, and
-                           s_kv % 8 == 0 (16-byte aligned rows). Produced by
-                           ra_v_transpose. The kernel then reads V^T tiles
-                           with plain 16-byte LDS reads.                     */
+                           s_kv % 8 == 0 (16-byte aligned rows), else
+                           RA_ERR_INVALID_ARG; d * s_kv * 2 < 2^31 bytes (the
+                           d rows of one head within 31-bit buffer offsets,
+                           s_kv < 8,388,608 at d = 128), else
+                           RA_ERR_UNSUPPORTED. Produced by ra_v_transpose.
+                           The kernel then reads V^T tiles with plain
+                           16-byte LDS reads.                                */
 } ra_v_layout;
 
 /*
@@ -207,9 +211,11 @@ ra_status ra_ring_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
  *           the merged result over all N blocks.
  * workspace: device, >= ra_ring_workspace_bytes(); holds the double buffer
  *           for the incoming K/V chunk and the position maps. Its contents on
- *           entry do not matter. For bf16 with c % 8 == 0 the V half of each
- *           buffer holds the chunk transposed (RA_V_TRANSPOSED, written by the
- *           copy stream), including the rank's own chunk before step 0.
+ *           entry do not matter. For bf16 with c % 8 == 0 (and c < 8,388,608
+ *           at d = 128, the RA_V_TRANSPOSED limit) the V half of each buffer
+ *           holds the chunk transposed (RA_V_TRANSPOSED, written by the copy
+ *           stream), including the rank's own chunk before step 0; otherwise
+ *           V stays row-major.
  * Step r computes the block of chunk (rank - r) mod N; the copy of the next
  * step's chunk into the idle half of the double buffer runs on `copy` while
  * step r computes on `compute` (on `compute` with RA_RING_SERIALIZE, when
@@ -274,7 +280,7 @@ ra_status ra_allgather_workspace_bytes(const ra_ring_desc *desc, size_t *bytes);
  * overwritten. step_events, if set, holds 2 hipEvent_t recorded on `stream`
  * just before and just after the attention launch. workspace: device, >= ra_allgather_workspace_bytes();
  * holds the positions, the gathered K and V of the sequence (for bf16 with
- * S % 8 == 0, V gathered straight into the transposed layout RA_V_TRANSPOSED,
+ * S % 8 == 0 and S < 8,388,608, V gathered straight into the transposed layout RA_V_TRANSPOSED,
  * with the chunk row of every position) and the queries' document starts.
  * Runs on `stream`.
  */

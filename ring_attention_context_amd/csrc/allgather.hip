@@ -109,8 +109,7 @@ ra_status make_ag_plan(const ra_ring_desc *r, AgPlan *p) {
   // V^T rows of S keys: 16-byte aligned rows, and a head's d-rows addressable
   // with 32-bit buffer offsets.
   p->vt = r->dtype == RA_BF16 && r->S % 8 == 0 && r->S > 0 &&
-          static_cast<int64_t>(r->b) * r->n_kv <= 65535 &&
-          static_cast<int64_t>(r->d) * r->S * 2 < (int64_t{1} << 31);
+          static_cast<int64_t>(r->b) * r->n_kv <= 65535 && vt_addressable(r->d, r->S);
   size_t off = 0;
   p->pos_off = off;
   off += align_up(static_cast<size_t>(r->S) * sizeof(int32_t));

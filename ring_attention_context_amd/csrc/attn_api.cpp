@@ -26,6 +26,10 @@ ra_status validate_attn(const ra_attn_desc *d, const void *q, const void *k, con
       return fail(RA_ERR_UNSUPPORTED, "attention: RA_V_TRANSPOSED needs bf16");
     if (d->s_kv % 8)
       return fail(RA_ERR_INVALID_ARG, "attention: RA_V_TRANSPOSED needs s_kv %% 8 == 0");
+    if (!vt_addressable(d->d, d->s_kv))
+      return fail(RA_ERR_UNSUPPORTED,
+                  "attention: RA_V_TRANSPOSED needs d * s_kv * 2 < 2^31 bytes (s_kv = %lld)",
+                  static_cast<long long>(d->s_kv));
   }
   if (d->causal != 0 && d->causal != 1)
     return fail(RA_ERR_INVALID_ARG, "attention: causal must be 0 or 1");

@@ -131,4 +131,9 @@ hipError_t launch_rows_to_vt(const void *src, void *vt, const int32_t *src_row, 
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// V^T [.., d, s_kv] of one (batch, kv head) must be addressable with 31-bit
+// buffer offsets: the attention kernel reads a V^T tile through one buffer
+// descriptor whose records span all d rows of s_kv keys.
+inline bool vt_addressable(int64_t d, int64_t s_kv) { return d * s_kv * 2 < (int64_t{1} << 31); }
+
 }  // namespace ra

@@ -10,7 +10,8 @@
 // events against the compute stream:
 //   copy(r+1 -> buf[(r+1)&1]) waits for step r-1 (the last reader of that half)
 //   step r waits for copy(r -> buf[r&1]).
-// For bf16 (with c % 8 == 0) the copy of V is a transpose into the V^T
+// For bf16 (with c % 8 == 0 and d * c * 2 < 2^31 bytes, the reach of one
+// buffer descriptor) the copy of V is a transpose into the V^T
 // layout the attention kernel reads fastest, and the rank's own V chunk is
 // transposed into buffer half 0 before step 0 as well; K of step 0 is read in
 // place. Step 0 writes (o, lse) directly (merging into the identity
@@ -110,7 +111,7 @@ ra_status make_plan(const ra_ring_desc *r, Plan *p) {
   p->serialize = (r->flags & RA_RING_SERIALIZE) != 0 ||
                  (!(r->flags & RA_RING_OVERLAP) && p->chunk_bytes <= RA_RING_SERIAL_CHUNK_BYTES);
   p->vt = r->dtype == RA_BF16 && p->c % 8 == 0 && p->c > 0 &&
-          static_cast<int64_t>(r->b) * r->n_kv <= 65535;
+          static_cast<int64_t>(r->b) * r->n_kv <= 65535 && vt_addressable(r->d, p->c);
   p->pairable = p->vt && p->fused && !r->doc_start && !(r->flags & RA_RING_STEPWISE);
   size_t off = 0;
   p->pos_off = off;

@@ -117,6 +117,7 @@ UNALIGNED = ctypes.c_void_p(0x1004)
     (dict(v_layout=2), ra.RA_ERR_INVALID_ARG),      # unknown V layout
     (dict(v_layout=1, dtype=ra.RA_F32), ra.RA_ERR_UNSUPPORTED),  # V^T is bf16 only
     (dict(v_layout=1, s_kv=60), ra.RA_ERR_INVALID_ARG),          # V^T rows 16-byte aligned
+    (dict(v_layout=1, s_kv=2**23), ra.RA_ERR_UNSUPPORTED),       # V^T past 31-bit offsets
 ])
 def test_block_attn_argument_errors(kw, code):
     lib = ra.load_library()

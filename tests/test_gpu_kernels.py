@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import ring_attention_context_amd as ra
+import synth
 from gpu_util import TOL_O, compare, rand_inputs, require_gpu, to_device
 from oracle import attention as oatt
 from oracle import partition as opart
@@ -168,3 +169,58 @@ def test_block_attn_large_scores_stay_finite():
     o, lse = _run_block("bf16", host, q_pos, kv_pos, True, scale)
     ro, rl = oatt.naive_attention(*wide, q_pos, kv_pos, True, np.float32(scale))
     compare(o, lse, ro, rl, "bf16", "x4 scores")
+
+
+def test_block_attn_offsets_past_2gib():
+    """Key blocks whose K and V span more than 2^31 bytes: every tile is then
+    read through a descriptor of its own (the far path), with one (batch, kv
+    head) of 8,388,672 keys (2.1 GB per tensor): row-major V at that length
+    with causal queries near the end of the block (positions and diagonal
+    tiles at the far end), and V^T at the longest length the transposed
+    layout accepts (8,388,544 keys: its d rows of one head still fit 31-bit
+    offsets) with non-causal ones. K and V hold seeded bf16 values of random sign,
+    exponent and mantissa in +-[0.5, 2) (drawn as bit patterns: 2^31 normal
+    draws would take a minute on the host), every key different, so a read
+    from the wrong place or a zero-filled one moves the result."""
+    n = 2**23 + 64
+    n_vt = 2**23 - 64
+    print(f"block attention, {n} keys (2.1 GB K, V)", flush=True)
+    rng = np.random.default_rng(2**23)
+    q, q64 = rand_inputs((1, 40, 1, 128), "bf16", rng)
+
+    def bits():
+        r = rng.integers(0, 1 << 16, size=(1, n, 1, 128), dtype=np.uint16)
+        return (r & np.uint16(0x80FF)) | np.uint16(0x3F00)   # sign, exponent 126 or 127
+
+    k, v = bits(), bits()
+    tq = to_device(q, "bf16")
+    tk = to_device(k, "bf16")
+    tv = to_device(v, "bf16")
+    cases = []
+    for s_kv, vt, causal in ((n, False, True), (n_vt, True, False)):
+        kv_pos = np.arange(s_kv, dtype=np.int32)
+        q_pos = np.arange(s_kv - 100, s_kv - 60, dtype=np.int32)
+        ks, vs = tk[:, :s_kv], tv[:, :s_kv]
+        if vt:
+            vs = torch.empty((1, 1, 128, s_kv), dtype=torch.bfloat16, device="cuda")
+            ra.ra_v_transpose(tv[:, :s_kv].contiguous(), vs)
+        o = torch.full((1, 40, 1, 128), float("nan"), device="cuda")
+        lse = torch.full((1, 40, 1), float("nan"), device="cuda")
+        ra.ra_block_attn_fwd(tq, ks, vs, o, lse, causal=causal,
+                             q_pos=torch.from_numpy(q_pos).cuda(),
+                             kv_pos=torch.from_numpy(kv_pos).cuda(), v_transposed=vt)
+        torch.cuda.synchronize()
+        cases.append((s_kv, vt, causal, q_pos, o.cpu().numpy(), lse.cpu().numpy()))
+        del vs
+    del tk, tv
+    torch.cuda.empty_cache()
+    k64 = synth.bf16_to_f32(k).astype(np.float64)
+    del k
+    v64 = synth.bf16_to_f32(v).astype(np.float64)
+    del v
+    for s_kv, vt, causal, q_pos, o, lse in cases:
+        ro, rl = oatt.naive_attention(q64, k64[:, :s_kv], v64[:, :s_kv], q_pos,
+                                      np.arange(s_kv), causal, 1 / math.sqrt(128))
+        do, dl = compare(o, lse, ro, rl, "bf16", f"{s_kv} keys vt={vt} causal={causal}")
+        print(f"  {s_kv} keys vt={vt} causal={causal}: max|dO| {do:.2e} max|dlse| {dl:.2e}",
+              flush=True)
