@@ -339,6 +339,68 @@ def test_ring_bwd_128k_sampled_keys_against_oracle():
         print(f"  {what} keys {len(keys)}: max err {err:.2e} (max |ref| {m:.2e})", flush=True)
 
 
+def test_block_bwd_offsets_past_2gib():
+    """ra_block_attn_bwd over one (batch, kv head) of 8,388,672 keys, K and V
+    past 2 GiB each (every K / V tile of the dq kernel through a descriptor of
+    its own), with 40 causal queries near the end of the block: dq of every
+    row and dK, dV of 64+ sampled keys (the last ones among them) against the
+    oracle, fed the oracle's o and lse (rounded to float32). K and V hold
+    seeded bf16 bit patterns of random sign, exponent and mantissa in
+    +-[0.5, 2) (2^31 normal draws would take the host a minute)."""
+    n = 2**23 + 64
+    print(f"block backward, {n} keys (2.1 GB K, V)", flush=True)
+    rng = np.random.default_rng(2**23 + 1)
+    q, q64 = rand_inputs((1, 40, 1, 128), "bf16", rng)
+    do, do64 = rand_inputs((1, 40, 1, 128), "bf16", rng)
+
+    def bits():
+        r = rng.integers(0, 1 << 16, size=(1, n, 1, 128), dtype=np.uint16)
+        return (r & np.uint16(0x80FF)) | np.uint16(0x3F00)   # sign, exponent 126 or 127
+
+    k, v = bits(), bits()
+    k64 = synth.bf16_to_f32(k).astype(np.float64)
+    v64 = synth.bf16_to_f32(v).astype(np.float64)
+    q_pos = np.arange(n - 100, n - 60, dtype=np.int32)
+    kv_pos = np.arange(n, dtype=np.int32)
+    scale = 1 / math.sqrt(128)
+    o, lse = oatt.naive_attention(q64, k64, v64, q_pos, kv_pos, True, scale)
+    o32, lse32 = o.astype(np.float32), lse.astype(np.float32)
+    tk, tv = to_device(k, "bf16"), to_device(v, "bf16")
+    del k, v
+    tdo = to_device(do, "bf16")
+    delta = torch.empty((1, 40, 1), device="cuda")
+    ra.ra_attn_bwd_delta(tdo, torch.from_numpy(o32).cuda(), delta)
+    dq = torch.zeros((1, 40, 1, 128), device="cuda")
+    dk = torch.zeros((1, n, 1, 128), device="cuda")
+    dv = torch.zeros_like(dk)
+    ra.ra_block_attn_bwd(to_device(q, "bf16"), tk, tv, tdo, torch.from_numpy(lse32).cuda(), delta,
+                         dq, dk, dv, causal=True, q_pos=torch.from_numpy(q_pos).cuda(),
+                         kv_pos=torch.from_numpy(kv_pos).cuda())
+    torch.cuda.synchronize()
+    keys = np.unique(np.concatenate([np.arange(n - 130, n, 8), np.arange(n - 100, n - 58),
+                                     rng.integers(0, n, 16)]))
+    idx = torch.from_numpy(keys).cuda()
+    got_k = dk[:, idx].cpu().numpy()
+    got_v = dv[:, idx].cpu().numpy()
+    got_q = dq.cpu().numpy()
+    del tk, tv, dk, dv, idx
+    torch.cuda.empty_cache()
+    rq = obwd.rows_dq(q64, k64, v64, do64, q_pos, kv_pos, True, scale)
+    D = obwd.delta(o32, do64)
+    _, rk, rv = obwd.block_attention_bwd(q64, k64[:, keys], v64[:, keys], do64, lse32, D, q_pos,
+                                         keys, True, scale)
+    # Each query spreads its weight over ~2^23 keys, so the gradients are tiny
+    # (|dk| ~ 1e-5): compared relative to their largest magnitude, without the
+    # absolute floor of grad_close.
+    for got, want, what in ((got_q, rq, "dq"), (got_k, rk, "dk"), (got_v, rv, "dv")):
+        err = float(np.max(np.abs(got - want)))
+        m = float(np.max(np.abs(want)))
+        assert m > 0 and err <= TOL_REL * m, f"{what}: max err {err:.3g} vs max |ref| {m:.3g}"
+        print(f"  {what}: max err {err:.2e} (max |ref| {m:.2e})", flush=True)
+    late = keys > q_pos[-1]            # keys after every query: no gradient at all
+    assert late.any() and not got_k[:, late].any() and not got_v[:, late].any()
+
+
 def test_ring_batched_forward_and_backward():
     """b = 2 through ra_ring_fwd and every rank's ra_ring_bwd (the [N, b, c, ...]
     chunk layout and the per-batch rows of every step), against naive attention
