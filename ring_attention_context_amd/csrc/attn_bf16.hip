@@ -56,7 +56,11 @@
 //     redone with its true row max only when a row has no reference yet or
 //     the sum leaves [0, 2^32] (a score far above the reference). The result
 //     is exact for any reference (o = acc / l, lse = ref + log2 l) as long as
-//     nothing overflows, which those bounds guarantee;
+//     nothing overflows, which those bounds guarantee. Each lane first tests
+//     its own half of the row sum: while every half is at most 2^7 the row
+//     sums are at most 2^8 and the tile needs neither, so the row sums (a
+//     cross-lane exchange) and the logarithm are formed only on the rare
+//     tiles where some half exceeds it;
 //   * two row sums: l over the fp32 probabilities gives lse, and l^ over the
 //     bf16-rounded probabilities that enter P V divides the accumulator, so o
 //     is a convex combination of V rows with exactly the weights the MFMA
@@ -554,6 +558,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   const bf16x4 ones4 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f),
                         static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   float alpha = 1.f;        // rescale factor pending for acc / l_run
+  bool pend = false;        // some lane has alpha != 1 (wave-uniform)
+  float m_use = 0.f;        // m_run, or 0 while it is -inf (the exponentials' offset)
   bool done = !wave_has_rows || w_nt == 0;
   bf16x8 pb[4];             // probabilities of the tile whose P V is next
   f32x16 s[2];              // scores of the tile whose probabilities are next
@@ -612,12 +618,13 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   };
 
   auto apply_rescale = [&]() INLINE {
-    if (__any(alpha != 1.f)) {
+    if (pend) {
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
       l_run *= alpha;
       lh4 *= alpha;
       alpha = 1.f;
+      pend = false;
     }
   };
 
@@ -627,7 +634,6 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // (before bf16 rounding), so lse carries no bf16 error; four partial sums
   // keep the dependency chains short.
   auto softmax = [&]() INLINE {
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float lp[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -709,27 +715,36 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   // moves up by log2 of it, and the rescale of acc and the sums waits until
   // the P V of this tile has been added (the next vector phase). A tile is
   // redone against its true row max when a row has no reference yet or its
-  // sum leaves [0, 2^32].
+  // sum leaves [0, 2^32]. Both tests run only when some lane's half of its
+  // row sum exceeds 2^(TAU-1) (or a reference is missing): otherwise every
+  // row sum is at most 2^TAU and both would come out false.
   auto yphase = [&]() INLINE {
     apply_rescale();
     softmax();
-    float lt_row = pair_sum(lt);
-    if (__any((m_run == -INFINITY) | !(lt_row <= 0x1p32f))) {
-      const float m_new = fmaxf(m_run, rowmax());
-      const float al = (m_run == -INFINITY || m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+    // Every half-row sum at most 2^(TAU-1) and every reference set: the row
+    // sums are at most 2^TAU, so neither a redo nor a reference move is due.
+    if (__any((m_run == -INFINITY) | !(lt <= 0x1p7f))) {
+      float lt_row = pair_sum(lt);
+      if (__any((m_run == -INFINITY) | !(lt_row <= 0x1p32f))) {
+        const float m_new = fmaxf(m_run, rowmax());
+        const float al = (m_run == -INFINITY || m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc[i] *= al;
-      l_run *= al;
-      lh4 *= al;
-      m_run = m_new;
-      softmax();
-      lt_row = pair_sum(lt);
+        for (int i = 0; i < D / 32; ++i) acc[i] *= al;
+        l_run *= al;
+        lh4 *= al;
+        m_run = m_new;
+        m_use = m_run == -INFINITY ? 0.f : m_run;
+        softmax();
+        lt_row = pair_sum(lt);
+      }
+      const bool need = lt_row > 0x1p8f;  // 2^TAU
+      const float lg = __builtin_amdgcn_logf(lt_row);  // log2
+      alpha = need ? exp2_fast(-lg) : 1.f;
+      m_run = need ? m_run + lg : m_run;
+      m_use = m_run == -INFINITY ? 0.f : m_run;
+      pend = __any(need);
     }
     l_run += lt;
-    const bool need = lt_row > 0x1p8f;  // 2^TAU
-    const float lg = __builtin_amdgcn_logf(lt_row);  // log2
-    alpha = need ? exp2_fast(-lg) : 1.f;
-    m_run = need ? m_run + lg : m_run;
   };
   static_assert(TAU == 8.f, "yphase compares against 2^TAU");
 
@@ -758,6 +773,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     qk(St0{});
     mask(0, St0{});
     m_run = rowmax();
+    m_use = m_run == -INFINITY ? 0.f : m_run;
   }
 
   // ---- main loop: step t = 0 .. nt-1 ----
