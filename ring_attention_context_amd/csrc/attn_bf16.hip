@@ -25,7 +25,10 @@
 //     zeros from the buffer descriptor's bounds check. Step t loads tile t+3
 //     into the stages tile t-1 left, so every load has two steps to land:
 //     the barrier waits only for loads older than the previous step's (a
-//     fence-free barrier; __syncthreads would drain all of them);
+//     fence-free barrier; __syncthreads would drain all of them). The K
+//     stage of tile t-1 is free a step before its V stage, so each wave
+//     issues the K rows before the step's barrier, where it would otherwise
+//     wait, and only the V rows after it;
 //   * K rows are row-major in LDS with the 16-byte chunks of each 256-byte row
 //     XOR-swizzled by the row index, so the operand reads (ds_read_b128) are
 //     bank-conflict free. V comes either row-major (read with the gfx950
@@ -216,7 +219,10 @@ __device__ __forceinline__ void wait_loads_upto(int n) {
     case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
     case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
     case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
   }
 }
 
@@ -754,8 +760,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
   using St2 = std::integral_constant<int, 2>;
   using St3 = std::integral_constant<int, 3>;
   // Step t issues K (with positions) and V of tile t+3 into the stages tile
-  // t-1 left, and needs everything issued up to step t-2: K of tile t+1 has
-  // two steps to land, V of tile t three. The loads are issued
+  // t-1 left (K before its barrier, V after it), and needs everything issued
+  // up to step t-2: K of tile t+1 has two steps to land, V of tile t three. The loads are issued
   // unconditionally (a tile past the range reads zeros, or keys that are never
   // used, into a free stage): the compiler's own waits before LDS reads then
   // count the loads that follow exactly instead of assuming none did. The
@@ -790,12 +796,15 @@ __global__ __launch_bounds__(THREADS, 1) void attn_bf16_kernel(AttnArgs a) {
     using SC = std::integral_constant<int, S>;
     using SN = std::integral_constant<int, (S + 1) % NSTAGE>;
     using SP = std::integral_constant<int, (S + NSTAGE - 1) % NSTAGE>;
-    // This wave's loads up to step t-2 have landed, and after the barrier
-    // everyone's; every wave is done with step t-1, so stage t-1 is free.
-    wait_loads_upto(n_step);
+    // K (and positions) of tile t-1 were last read in step t-2, which every
+    // wave finished before the barrier of step t-1: their stage takes tile
+    // t+3 before this step's barrier. Then this wave's loads up to step t-2
+    // have landed, and after the barrier everyone's; every wave is done with
+    // step t-1, so the V stage of tile t-1 is free too.
+    issue_k(t + 3, SP{});
+    wait_loads_upto(n_step + nk);
     barrier_keep_loads();
     asm volatile("" : "+v"(koff0), "+v"(voff0));  // pin: see koff
-    issue_k(t + 3, SP{});
     issue_v(t + 3, SP{});
     if (!done) {
       if (grp_b) yphase();
