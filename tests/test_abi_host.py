@@ -172,6 +172,12 @@ def test_ring_workspace_bytes():
                                                               + 2 * 2 * align(one_chunk))
     # ... float32 reads K and V in place: no double buffer
     assert ra.ra_ring_workspace_bytes(_ring(N=1, rank=0, dtype=ra.RA_F32)) == 2 * align(1024 * 4)
+    # ... and so does bf16 once a chunk's V^T rows leave 31-bit buffer offsets
+    # (d * c * 2 >= 2^31 bytes: c >= 2^23 at d = 128); just below, it stages V^T
+    for S, vt in ((2**23, False), (2**23 - 8, True)):
+        got = ra.ra_ring_workspace_bytes(_ring(N=1, rank=0, S=S, n_kv=1, n_q=1))
+        base = 2 * align(S * 4)
+        assert got == base + (2 * 2 * align(S * 128 * 2) if vt else 0), (S, got)
 
 
 @pytest.mark.parametrize("kw", [
