@@ -8,19 +8,21 @@
 // transcendentals of the weights are paid once per 16 U bytes: with T = d/4/U
 // threads per row, thread j takes units j, j + T, ..., so each load and store
 // instruction of a wave covers contiguous runs of 16 T bytes. d is a power of
-// two, so rows and units come from shifts.
+// two, so rows and units come from shifts. o and o_b are streamed with
+// nontemporal loads and stores: every byte is touched once.
 #include "ra_internal.h"
 
 namespace ra {
 namespace {
+typedef float fv4 __attribute__((ext_vector_type(4)));
 
 template <int U>
 __global__ __launch_bounds__(256) void lse_merge_kernel(int64_t n_units, int32_t shift,
                                                         int32_t d4, float *o, float *lse,
                                                         const float *o_b, const float *lse_b) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  float4 *o4 = reinterpret_cast<float4 *>(o);
-  const float4 *ob4 = reinterpret_cast<const float4 *>(o_b);
+  fv4 *o4 = reinterpret_cast<fv4 *>(o);
+  const fv4 *ob4 = reinterpret_cast<const fv4 *>(o_b);
   constexpr int LU = U == 4 ? 2 : U == 2 ? 1 : 0;
   const int32_t tpr = d4 >> LU;   // threads per row
   for (int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; u < n_units;
@@ -28,11 +30,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(int64_t n_units, int32_t
     const int64_t r = u >> (shift - LU);  // row (d4 = 1 << shift units per row)
     const int32_t c = static_cast<int32_t>(u & (tpr - 1));
     const int64_t i = (r << shift) + c;   // this thread's first unit; then every tpr-th
-    float4 x[U], y[U];
+    fv4 x[U], y[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      x[k] = o4[i + k * tpr];
-      y[k] = ob4[i + k * tpr];
+      x[k] = __builtin_nontemporal_load(o4 + i + k * tpr);
+      y[k] = __builtin_nontemporal_load(ob4 + i + k * tpr);
     }
     const float l1 = lse[r];
     const float l2 = lse_b[r];
@@ -45,12 +47,10 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(int64_t n_units, int32_t
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      float4 z;
-      z.x = w1 * x[k].x + w2 * y[k].x;
-      z.y = w1 * x[k].y + w2 * y[k].y;
-      z.z = w1 * x[k].z + w2 * y[k].z;
-      z.w = w1 * x[k].w + w2 * y[k].w;
-      o4[i + k * tpr] = z;
+      fv4 z;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z[j] = w1 * x[k][j] + w2 * y[k][j];
+      __builtin_nontemporal_store(z, o4 + i + k * tpr);
     }
     // Every thread of a row sits in the same wave (tpr divides 64) and reads
     // lse[r] before this store is issued.
